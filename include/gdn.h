@@ -1,0 +1,240 @@
+/*
+ * gdn.h -- C ABI of libgdn, the Gated DeltaNet layer core for AMD MI355X
+ * (gfx950).
+ *
+ * The library computes, for a batch of sequences, the four parts of a GDN
+ * layer core named by the method statement of this project (Gated DeltaNet):
+ *   (a) a width-W depthwise causal conv with SiLU over the q/k/v channels and
+ *       the rolling conv window;
+ *   (b) the post-conv gating: L2-normalised q and k, decay
+ *       g = -exp(A_log) * softplus(a + dt_bias), update strength beta = sigmoid(b);
+ *   (c) the gated delta rule per value head,
+ *         S_t = e^{g_t} (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *         o_t = scale * S_t^T q_t,
+ *       with S a d_k x d_v matrix, token by token or in the chunked WY/UT form;
+ *   (d) speculative verify that replays the previous step's accepted
+ *       candidate rows from a one-page record ("r9700-stack v0.2.4: one GDN
+ *       state page per request", section "What it does").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer is a DEVICE pointer unless its comment says host.  The
+ *   caller owns every buffer; libgdn never allocates, frees or synchronises,
+ *   and keeps no state between calls.  Kernels run on `stream` (a hipStream_t;
+ *   NULL is the default stream).
+ * - Channel order of a pre-conv row is [q | k | v], head-major then dim:
+ *   C_conv = 2*h_k*d_k + h_v*d_v.  Value head h reads key head h / (h_v/h_k).
+ * - Activations (x, conv window, conv weights, a, b) use dims->act_dtype;
+ *   states use dims->state_dtype; A_log, dt_bias and every output o are fp32.
+ * - A state page holds h_v heads, each a row-major d_k x d_v matrix.
+ * - Page indices < 0 mark padding rows: they are skipped and nothing of
+ *   theirs is read or written.  Page indices used in one call must be
+ *   distinct.  Sequences of length 0 are no-ops.
+ * - Host-side argument errors return GDN_ERR_ARG before anything is
+ *   launched.  Errors only the device can see (page index >= n_pages, a
+ *   malformed cu_seqlens, an acceptance beyond the record, a replayed
+ *   step) skip the affected sequence or request and OR a GDN_DEVERR_* bit
+ *   into *err when err is not NULL.
+ * - conv-window sync words: sequences whose workgroups share conv channels
+ *   hand the rolled window to the last workgroup to finish reading it, which
+ *   counts arrivals in gdn_conv_pool.sync.  The words must be zero before the
+ *   first call and every call leaves them zero when its kernels complete;
+ *   a call aborted midway must be followed by re-zeroing them.
+ * - Calls that touch the same pages must be ordered (same stream, or events).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+/* status codes returned by every entry point */
+#define GDN_OK 0
+#define GDN_ERR_ARG 1          /* invalid argument (null pointer, bad dims/stride/size) */
+#define GDN_ERR_UNSUPPORTED 2  /* valid but not compiled (head dim, width, dtype combination) */
+#define GDN_ERR_LAUNCH 3       /* the HIP launch failed */
+
+/* dtypes */
+#define GDN_F32 0
+#define GDN_BF16 1
+
+/* speculative page layouts */
+#define GDN_SPEC_ONEPAGE 0     /* one state checkpoint + a two-slot record per request */
+#define GDN_SPEC_SLOTS 1       /* one state page per candidate (the comparison design) */
+
+/* sticky device error bits OR-ed into *err */
+#define GDN_DEVERR_PAGE 1u      /* page index >= n_pages */
+#define GDN_DEVERR_BATCH 2u     /* cu_seqlens decreasing or beyond n_rows */
+#define GDN_DEVERR_ACCEPTED 4u  /* num_accepted >= rows held by the live record */
+#define GDN_DEVERR_PARITY 8u    /* step parity equals the live record's: step already applied */
+
+typedef struct gdn_dims {
+    int32_t h_k, h_v;      /* key heads, value heads; h_v % h_k == 0 */
+    int32_t d_k, d_v;      /* head dims; d_k in {32, 64, 128}, d_v % 32 == 0 */
+    int32_t conv_w;        /* conv width; 4 is compiled */
+    int32_t n_spec;        /* drafts per verify step (candidates per step <= n_spec + 1) */
+    int32_t act_dtype;     /* GDN_BF16 or GDN_F32 */
+    int32_t state_dtype;   /* GDN_F32 or GDN_BF16 */
+    float scale;           /* s in o = s * S^T q */
+    float l2_eps;          /* eps in q / sqrt(sum q^2 + eps) */
+} gdn_dims;
+
+typedef struct gdn_params {
+    const void* conv_w;    /* [C_conv][conv_w], act dtype; tap conv_w-1 meets the newest row */
+    const float* a_log;    /* [h_v] */
+    const float* dt_bias;  /* [h_v] */
+} gdn_params;
+
+/* Ragged batch of sequences packed row by row. */
+typedef struct gdn_batch {
+    const int32_t* cu_seqlens;  /* [n_seqs+1], cu[0] = 0, non-decreasing, cu[n_seqs] <= n_rows */
+    const int32_t* page_idx;    /* [n_seqs], page in both pools; < 0 = padding */
+    const uint8_t* has_init;    /* [n_seqs] or NULL (all 1): 0 = start from a zero window and state */
+    int32_t n_seqs;
+    int32_t max_seqlen;         /* host: upper bound of every length, or 0 if unknown */
+    int64_t n_rows;             /* host: rows available in x, a, b and o */
+} gdn_batch;
+
+/* Conv windows: page p, row r (oldest first), channel c lives at
+ * base + p*page_stride + r*C_conv + c (act dtype).  Rows 0..conv_w-2 hold the
+ * window after a sequence call; verify uses rows 0..conv_w-2+n_spec. */
+typedef struct gdn_conv_pool {
+    void* base;
+    int64_t page_stride;   /* elements, >= rows * C_conv */
+    int32_t rows;          /* >= conv_w - 1 (verify: >= conv_w - 1 + n_spec) */
+    int32_t n_pages;
+    uint32_t* sync;        /* [n_pages][h_k] arrival counters, zero between calls */
+} gdn_conv_pool;
+
+/* Recurrent states: page p, head h at base + p*page_stride + h*d_k*d_v
+ * (state dtype), row-major d_k x d_v. */
+typedef struct gdn_state_pool {
+    void* base;
+    int64_t page_stride;   /* elements, >= h_v * d_k * d_v */
+    int32_t n_pages;
+} gdn_state_pool;
+
+/* Byte layout of one speculative page (see gdn_spec_page_layout). */
+typedef struct gdn_spec_layout {
+    size_t page_bytes;     /* minimum page size (a multiple of 256) */
+    size_t header_off;     /* gdn_spec_header */
+    size_t state_off;      /* one-page: checkpoint [h_v][d_k][d_v]; slots: [n_spec+1][h_v][d_k][d_v] */
+    size_t record_off;     /* one-page only: record slot s, row i at record_off + (s*(n_spec+1)+i)*record_row_bytes */
+    size_t record_row_bytes; /* fp32 [C_conv] post-conv q|k|v, then fp32 [h_v] a, then fp32 [h_v] b */
+} gdn_spec_layout;
+
+/* Header at the start of every speculative page.  An all-zero header is a
+ * fresh page (live slot 0 holding no rows, parity 0): zero it after a
+ * prefill or sequence call has written the page's state. */
+typedef struct gdn_spec_header {
+    uint32_t flag;         /* bit 0 live slot, bit 1 parity of the step that wrote it, bits 8..31 done counter */
+    uint32_t n_rows[2];    /* candidate rows held by record slot 0 / 1 (slots layout: slots written) */
+    uint32_t accepted;     /* echo of the acceptance the last step replayed */
+    uint32_t reserved[60];
+} gdn_spec_header;
+
+/* ------------------------------------------------------------ queries */
+
+/* GDN_ABI_VERSION of the loaded library. */
+int32_t gdn_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* gdn_status_str(int32_t status);
+
+/* Fill *out with the byte layout of a speculative page for `dims` and
+ * `layout`.  Host-only.  Returns GDN_ERR_ARG on invalid dims or layout. */
+int32_t gdn_spec_page_layout(const gdn_dims* dims, int32_t layout, gdn_spec_layout* out);
+
+/* Workspace bytes gdn_chunked_prefill needs for this batch shape (host-only). */
+int32_t gdn_chunked_workspace_bytes(const gdn_dims* dims, int32_t n_seqs, int64_t n_rows,
+                                    int32_t chunk, size_t* out_bytes);
+
+/* ---------------------------------------------------- (a) conv update */
+
+/* Causal depthwise conv over a ragged batch (Gated DeltaNet part (a)):
+ *   z_t[c] = sum_{j<W} conv_w[c][j] * X_{t-W+1+j}[c],  y = SiLU(z) if activation
+ * where rows before the first token come from the page's conv window (zeros if
+ * has_init is 0).  Writes y [n_rows][y_stride] (y_dtype, GDN_F32 or GDN_BF16)
+ * and rolls the window to the last W-1 rows of (window ++ x).  fp32
+ * arithmetic: acc = 0, then one fused multiply-add per tap, oldest first.
+ * x: [n_rows][x_stride] act dtype. */
+int32_t gdn_conv_update(const gdn_dims* dims, const void* conv_w,
+                        const void* x, int64_t x_stride,
+                        const gdn_batch* batch, gdn_conv_pool conv,
+                        int32_t activation, void* y, int32_t y_dtype, int64_t y_stride,
+                        int32_t* err, void* stream);
+
+/* ------------------------------------ (a)+(b)+(c) token-by-token core */
+
+/* The layer core token by token, conv + gating + delta rule fused in one
+ * launch (Gated DeltaNet parts (a)-(c); the token-by-token core of
+ * "r9700-stack v0.2.3", section "1. Time to first token").  Each sequence
+ * continues the state and window of its page (or zeros if has_init is 0);
+ * its final state and rolled window are written back.  Decode is T = 1.
+ *   x: [n_rows][x_stride] pre-conv rows; a, b: [n_rows][ab_stride] (first
+ *   h_v entries used); o: [n_rows][h_v][d_v] fp32. */
+int32_t gdn_recurrent_seq(const gdn_dims* dims, const gdn_params* params,
+                          const void* x, int64_t x_stride,
+                          const void* a, const void* b, int64_t ab_stride,
+                          const gdn_batch* batch, gdn_conv_pool conv, gdn_state_pool state,
+                          float* o, int32_t* err, void* stream);
+
+/* ------------------------------------------- (c) chunked WY/UT prefill */
+
+/* The same result as gdn_recurrent_seq computed in the chunked WY/UT form
+ * (Gated DeltaNet part (c)): per chunk of `chunk` rows, the UT transform
+ * T = (I + A)^{-1} of A = tril(diag(beta) K K^T o e^{G_i-G_j}, -1), then
+ * W = T diag(beta e^G) K, U = T diag(beta) V and the chunk-state update,
+ * with bf16 matrix-core products accumulated in fp32.  chunk == 64 is
+ * compiled.  workspace: device bytes >= gdn_chunked_workspace_bytes (may be
+ * NULL when that is 0). */
+int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* params,
+                            const void* x, int64_t x_stride,
+                            const void* a, const void* b, int64_t ab_stride,
+                            const gdn_batch* batch, gdn_conv_pool conv, gdn_state_pool state,
+                            float* o, int32_t chunk, void* workspace, size_t ws_bytes,
+                            int32_t* err, void* stream);
+
+/* --------------------------------------------------- (d) spec verify */
+
+/* One speculative verify step over n_req requests ("r9700-stack v0.2.4",
+ * section "What it does").  Request r uses page req_page[r] of `pages`
+ * (page_bytes apart, laid out per gdn_spec_page_layout) and of the conv pool
+ * (rows >= conv_w - 1 + n_spec).  num_accepted[r] is how many drafts of the
+ * previous step were accepted (1 + num_accepted[r] rows are committed); it is
+ * ignored when the live record holds no rows.  step_parity[r] is 0 or 1 and
+ * must differ from the parity stored in the page.
+ * ONEPAGE: replay rows 0..num_accepted of the live record into the
+ *   checkpoint, store it (rounded to the state dtype) and continue from the
+ *   stored value; run the n_cand candidates, write their post-conv q|k|v
+ *   and a/b into the other record slot; flip the live slot.
+ * SLOTS: start from slot[num_accepted], store the state after candidate i
+ *   into slot i.
+ * Both designs give bit-identical o and committed states.  n_cand == 0 only
+ *   commits (replays) and leaves an empty record.
+ * Conv buffer: the window of the step is rows a'..a'+W-2 (a' = the replayed
+ * acceptance, 0 for an empty record); afterwards rows are
+ * [a'+1 .. a'+W-2, x of the n_cand candidates] (n_cand > 0) or
+ * [a' .. a'+W-2] (n_cand == 0).
+ *   x: [n_req][n_cand] rows of x_stride; a, b: [n_req][n_cand] rows of
+ *   ab_stride; o: [n_req][n_cand][h_v][d_v] fp32. */
+int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* params, int32_t layout,
+                        const void* x, int64_t x_stride,
+                        const void* a, const void* b, int64_t ab_stride,
+                        int32_t n_req, int32_t n_cand,
+                        const int32_t* req_page, const int32_t* num_accepted,
+                        const uint8_t* step_parity,
+                        void* pages, int64_t page_bytes, int32_t n_pages,
+                        gdn_conv_pool conv, float* o, int32_t* err, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,100 @@
+"""ctypes mirror of include/gdn.h and the loader of libgdn.so.
+
+The library is loaded after torch so that it binds to the HIP runtime torch
+already holds (both answer to the soname libamdhip64.so.7).  There is no
+fallback: a missing library or symbol raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+ABI_VERSION = 1
+
+GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
+GDN_F32, GDN_BF16 = 0, 1
+GDN_SPEC_ONEPAGE, GDN_SPEC_SLOTS = 0, 1
+GDN_DEVERR_PAGE, GDN_DEVERR_BATCH, GDN_DEVERR_ACCEPTED, GDN_DEVERR_PARITY = 1, 2, 4, 8
+
+SYMBOLS = ("gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout", "gdn_chunked_workspace_bytes",
+           "gdn_conv_update", "gdn_recurrent_seq", "gdn_chunked_prefill", "gdn_spec_verify")
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [("h_k", _i32), ("h_v", _i32), ("d_k", _i32), ("d_v", _i32), ("conv_w", _i32),
+                ("n_spec", _i32), ("act_dtype", _i32), ("state_dtype", _i32),
+                ("scale", ctypes.c_float), ("l2_eps", ctypes.c_float)]
+
+
+class GdnParams(ctypes.Structure):
+    _fields_ = [("conv_w", _vp), ("a_log", _vp), ("dt_bias", _vp)]
+
+
+class GdnBatch(ctypes.Structure):
+    _fields_ = [("cu_seqlens", _vp), ("page_idx", _vp), ("has_init", _vp), ("n_seqs", _i32),
+                ("max_seqlen", _i32), ("n_rows", _i64)]
+
+
+class GdnConvPool(ctypes.Structure):
+    _fields_ = [("base", _vp), ("page_stride", _i64), ("rows", _i32), ("n_pages", _i32), ("sync", _vp)]
+
+
+class GdnStatePool(ctypes.Structure):
+    _fields_ = [("base", _vp), ("page_stride", _i64), ("n_pages", _i32)]
+
+
+class GdnSpecLayout(ctypes.Structure):
+    _fields_ = [("page_bytes", ctypes.c_size_t), ("header_off", ctypes.c_size_t),
+                ("state_off", ctypes.c_size_t), ("record_off", ctypes.c_size_t),
+                ("record_row_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdn.so (after torch) and bind every entry point's signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- the HIP runtime must come from torch's process image
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_LOCAL)
+    missing = [s for s in SYMBOLS if not hasattr(L, s)]
+    if missing:
+        raise ImportError(f"libgdn.so lacks {missing}")
+    L.gdn_abi_version.restype = _i32
+    L.gdn_abi_version.argtypes = []
+    if L.gdn_abi_version() != ABI_VERSION:
+        raise ImportError(f"libgdn ABI {L.gdn_abi_version()} != {ABI_VERSION}")
+    L.gdn_status_str.restype = ctypes.c_char_p
+    L.gdn_status_str.argtypes = [_i32]
+    L.gdn_spec_page_layout.restype = _i32
+    L.gdn_spec_page_layout.argtypes = [ctypes.POINTER(GdnDims), _i32, ctypes.POINTER(GdnSpecLayout)]
+    L.gdn_chunked_workspace_bytes.restype = _i32
+    L.gdn_chunked_workspace_bytes.argtypes = [ctypes.POINTER(GdnDims), _i32, _i64, _i32,
+                                              ctypes.POINTER(ctypes.c_size_t)]
+    L.gdn_conv_update.restype = _i32
+    L.gdn_conv_update.argtypes = [ctypes.POINTER(GdnDims), _vp, _vp, _i64, ctypes.POINTER(GdnBatch),
+                                  GdnConvPool, _i32, _vp, _i32, _i64, _vp, _vp]
+    L.gdn_recurrent_seq.restype = _i32
+    L.gdn_recurrent_seq.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _vp, _i64, _vp, _vp,
+                                    _i64, ctypes.POINTER(GdnBatch), GdnConvPool, GdnStatePool, _vp, _vp, _vp]
+    L.gdn_chunked_prefill.restype = _i32
+    L.gdn_chunked_prefill.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _vp, _i64, _vp, _vp,
+                                      _i64, ctypes.POINTER(GdnBatch), GdnConvPool, GdnStatePool, _vp, _i32,
+                                      _vp, ctypes.c_size_t, _vp, _vp]
+    L.gdn_spec_verify.restype = _i32
+    L.gdn_spec_verify.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _i32, _vp, _i64, _vp,
+                                  _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, GdnConvPool, _vp,
+                                  _vp, _vp]
+    _lib = L
+    return L

@@ -1,0 +1,140 @@
+// gdn_device.hpp -- device helpers shared by the libgdn kernels (gfx950).
+//
+// Everything here is arithmetic the kernels must perform identically
+// wherever the same value is produced, so that the one-page verify, the
+// per-candidate-slot verify and the token-by-token sequence kernel agree
+// bit for bit: one conv op order, one reduction tree per quantity, one
+// gating formula and one state-update formula.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Activation / state element types: fp32 as float, bf16 as its raw bits.
+using bf16_t = uint16_t;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// Round through the storage type (identity for fp32).
+template <typename T> __device__ __forceinline__ float round_as(float v) { return to_f32(from_f32<T>(v)); }
+
+// ------------------------------------------------------------- gating (b)
+// SiLU(z) = z / (1 + e^{-z}).
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// softplus(u) = log(1 + e^u); for u > 20 it equals u to within 2e-9 relative.
+__device__ __forceinline__ float softplus(float u) { return u > 20.0f ? u : log1pf(expf(u)); }
+
+__device__ __forceinline__ float sigmoid(float b) { return 1.0f / (1.0f + expf(-b)); }
+
+// Depthwise causal conv of one channel, width 4: acc = 0, then one fused
+// multiply-add per tap, oldest row first (x3 oldest ... x0 newest).
+__device__ __forceinline__ float conv4(const float w[4], float x3, float x2, float x1, float x0) {
+    float acc = fmaf(w[0], x3, 0.0f);
+    acc = fmaf(w[1], x2, acc);
+    acc = fmaf(w[2], x1, acc);
+    acc = fmaf(w[3], x0, acc);
+    return acc;
+}
+
+// ------------------------------------------------------------- reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 8 lanes {l & ~7 .. l | 7}; every lane of the group receives
+// the same bits.  Tree: xor 1, xor 2, then the mirrored half-row.
+__device__ __forceinline__ float reduce8(float x) {
+    x = x + dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    x = x + dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    x = x + dpp_mov<0x141>(x);  // row_half_mirror
+    return x;
+}
+
+// Butterfly sum over the 64 lanes of a wave; every lane receives the same bits.
+__device__ __forceinline__ float reduce64(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = x + __shfl_xor(x, m, 64);
+    return x;
+}
+
+// --------------------------------------------------- the delta rule (c)
+// One token of the gated delta rule for the R rows x 1 column this lane
+// holds.  The 8 lanes of an aligned lane group hold the d_k = 8R rows of
+// one column.  k, q: this lane's rows of k-hat and scale*q-hat.  Single
+// pass over S_{t-1}: u = S^T k, w = S^T q, then
+//   delta = beta (v - e^g u),  o = e^g w + (k.q) delta,
+//   S <- e^g S + k delta^T.
+// Returns o (identical bits in the 8 lanes of the group).
+template <int R>
+__device__ __forceinline__ float delta_step(float (&s)[R], const float (&k)[R], const float (&q)[R],
+                                            float v, float eg, float beta, float kq) {
+    float u0 = 0.0f, u1 = 0.0f, w0 = 0.0f, w1 = 0.0f;
+#pragma unroll
+    for (int m = 0; m < R; m += 2) {
+        u0 = fmaf(s[m], k[m], u0);
+        w0 = fmaf(s[m], q[m], w0);
+        if (m + 1 < R) {
+            u1 = fmaf(s[m + 1], k[m + 1], u1);
+            w1 = fmaf(s[m + 1], q[m + 1], w1);
+        }
+    }
+    const float u = reduce8(u0 + u1);
+    const float w = reduce8(w0 + w1);
+    const float d = beta * (v - eg * u);
+    const float o = fmaf(kq, d, eg * w);
+#pragma unroll
+    for (int m = 0; m < R; ++m) s[m] = fmaf(k[m], d, eg * s[m]);
+    return o;
+}
+
+// Replay variant: the same state update without the output.
+template <int R>
+__device__ __forceinline__ void delta_update(float (&s)[R], const float (&k)[R], float v, float eg,
+                                             float beta) {
+    float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+    for (int m = 0; m < R; m += 2) {
+        u0 = fmaf(s[m], k[m], u0);
+        if (m + 1 < R) u1 = fmaf(s[m + 1], k[m + 1], u1);
+    }
+    const float u = reduce8(u0 + u1);
+    const float d = beta * (v - eg * u);
+#pragma unroll
+    for (int m = 0; m < R; ++m) s[m] = fmaf(k[m], d, eg * s[m]);
+}
+
+// ---------------------------------------------------------- arrival count
+// Workgroup arrival on a device-scope counter that returns to zero: the
+// last of `group` arrivals (in any order) gets true and resets the word.
+// Call from one thread after every read the arrival stands for is complete.
+__device__ __forceinline__ bool arrive_last(uint32_t* word, uint32_t group) {
+    const uint32_t prev = __hip_atomic_fetch_add(word, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev + 1u == group) {
+        __hip_atomic_store(word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    }
+    return false;
+}
+
+__device__ __forceinline__ void set_err(int32_t* err, uint32_t bit) {
+    if (err) __hip_atomic_fetch_or(err, (int32_t)bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace gdn

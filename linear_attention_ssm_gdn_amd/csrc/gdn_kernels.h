@@ -1,0 +1,76 @@
+// gdn_kernels.h -- kernel argument blocks and launchers (host side of the
+// kernels; the C ABI in gdn_api.cpp validates arguments and calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct SeqArgs {
+    const void* x; int64_t x_stride;
+    const void* a; const void* b; int64_t ab_stride;
+    int64_t n_rows;
+    const int32_t* cu; const int32_t* page_idx; const uint8_t* has_init; int32_t n_seqs;
+    const void* conv_w; const float* a_log; const float* dt_bias;
+    void* conv_base; int64_t conv_page_stride; int32_t conv_n_pages; uint32_t* sync;
+    void* state; int64_t state_page_stride; int32_t state_n_pages;
+    float* o;
+    int32_t* err;
+    int32_t h_k, h_v, d_v;
+    float scale, eps;
+};
+
+struct ConvArgs {
+    const void* x; int64_t x_stride;
+    int64_t n_rows;
+    const int32_t* cu; const int32_t* page_idx; const uint8_t* has_init; int32_t n_seqs;
+    const void* conv_w;
+    void* conv_base; int64_t conv_page_stride; int32_t conv_n_pages;
+    void* y; int64_t y_stride;
+    int32_t* err;
+    int32_t C;
+    int32_t activation;
+};
+
+struct VerifyArgs {
+    const void* x; int64_t x_stride;
+    const void* a; const void* b; int64_t ab_stride;
+    int32_t n_req, n_cand;
+    const int32_t* req_page; const int32_t* num_accepted; const uint8_t* step_parity;
+    uint8_t* pages; int64_t page_bytes; int32_t n_pages;
+    int64_t header_off, state_off, record_off, record_row_bytes;
+    const void* conv_w; const float* a_log; const float* dt_bias;
+    void* conv_base; int64_t conv_page_stride; int32_t conv_n_pages; uint32_t* sync;
+    float* o;
+    int32_t* err;
+    int32_t h_k, h_v, d_v, n_spec;
+    float scale, eps;
+};
+
+struct ChunkArgs {
+    const void* x; int64_t x_stride;
+    const void* a; const void* b; int64_t ab_stride;
+    int64_t n_rows;
+    const int32_t* cu; const int32_t* page_idx; const uint8_t* has_init; int32_t n_seqs;
+    const void* conv_w; const float* a_log; const float* dt_bias;
+    void* conv_base; int64_t conv_page_stride; int32_t conv_n_pages; uint32_t* sync;
+    void* state; int64_t state_page_stride; int32_t state_n_pages;
+    float* o;
+    int32_t* err;
+    int32_t h_k, h_v, d_v;
+    float scale, eps;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_seq(const SeqArgs& a, int d_k, int act_dtype, int state_dtype, hipStream_t s);
+hipError_t launch_conv(const ConvArgs& a, int act_dtype, int y_dtype, int max_seqlen, hipStream_t s);
+hipError_t launch_verify(const VerifyArgs& a, int d_k, int act_dtype, int state_dtype, int layout,
+                         hipStream_t s);
+hipError_t launch_chunked(const ChunkArgs& a, int d_k, int act_dtype, int state_dtype, hipStream_t s);
+
+// Which (d_k, d_v) the kernels are compiled for.
+bool seq_supported(int d_k, int d_v);
+bool chunked_supported(int d_k, int d_v, int chunk);
+
+}  // namespace gdn

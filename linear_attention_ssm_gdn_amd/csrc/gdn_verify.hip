@@ -1,0 +1,326 @@
+// gdn_verify.hip -- one speculative verify step (Gated DeltaNet part (d)).
+//
+// The one-page design of "r9700-stack v0.2.4: one GDN state page per
+// request" (section "What it does"): each request keeps one state
+// checkpoint plus a record of the previous step's candidate rows (post-conv
+// q|k|v and the a/b gate inputs) in two slots and a flag word (live slot,
+// parity, done counter).  A step replays the accepted rows of the live slot
+// into the checkpoint, stores it, then runs the new candidates from the
+// stored value and records them in the other slot.  The comparison design
+// keeps one state page per candidate instead.  Both designs run through this
+// one kernel template and the same per-token functions, which is what makes
+// them bit-identical.
+//
+// Grid: one workgroup per (request, value head, block of 32 value columns),
+// the lane layout of gdn_block.hpp.  Candidates per step <= 16 (one chunk).
+#include "gdn_block.hpp"
+#include "gdn_kernels.h"
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+constexpr int VER_TT = 16;
+
+template <typename ActT, typename StT, int DK, int LAYOUT>
+__global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A) {
+    constexpr int TT = VER_TT;
+    constexpr int R = DK / 8;
+    constexpr int NLC = 2 * DK + BV;
+    constexpr int NCH = (NLC + BLOCK_THREADS - 1) / BLOCK_THREADS;
+    __shared__ __attribute__((aligned(16))) float smem[TT * (2 * DK + BV + 4) + DK * STAGE_LD];
+    __shared__ int sh_last;
+    float* sq = smem;
+    float* sk = sq + TT * DK;
+    float* sv = sk + TT * DK;
+    float* ssc = sv + TT * BV;
+    float* stage = ssc + TT * 4;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nblk = A.d_v / BV;
+    int bid = blockIdx.x;
+    const int blk = bid % nblk;
+    bid /= nblk;
+    const int h = bid % A.h_v;
+    const int req = bid / A.h_v;
+    const int rr = A.h_v / A.h_k;
+    const int ki = h / rr;
+    const int colbase = blk * BV;
+    const int64_t C = 2 * (int64_t)A.h_k * DK + (int64_t)A.h_v * A.d_v;
+    const bool reporter = (h == 0 && blk == 0 && tid == 0);
+
+    const int page = A.req_page[req];
+    if (page < 0) return;
+    if (page >= A.n_pages || page >= A.conv_n_pages) {
+        if (reporter) set_err(A.err, GDN_DEVERR_PAGE);
+        return;
+    }
+    uint8_t* pg = A.pages + (int64_t)page * A.page_bytes;
+    gdn_spec_header* hdr = reinterpret_cast<gdn_spec_header*>(pg + A.header_off);
+    const uint32_t flag = hdr->flag;
+    const int L = (int)(flag & 1u);
+    const int P = (int)((flag >> 1) & 1u);
+    const int nr = (int)hdr->n_rows[L];
+    const int par = A.step_parity[req] & 1;
+    if (par == P) {
+        if (reporter) set_err(A.err, GDN_DEVERR_PARITY);
+        return;
+    }
+    int acc = 0;
+    if (nr > 0) {
+        acc = A.num_accepted[req];
+        if (acc < 0 || acc >= nr || nr > A.n_spec + 1) {
+            if (reporter) set_err(A.err, GDN_DEVERR_ACCEPTED);
+            return;
+        }
+    }
+    const int n_replay = (LAYOUT == GDN_SPEC_ONEPAGE && nr > 0) ? acc + 1 : 0;
+    const int nc = A.n_cand;
+
+    const int64_t head_elems = (int64_t)DK * A.d_v;
+    StT* __restrict__ st_base = reinterpret_cast<StT*>(pg + A.state_off);
+    StT* __restrict__ Sload = (LAYOUT == GDN_SPEC_ONEPAGE)
+                                  ? st_base + (int64_t)h * head_elems + colbase
+                                  : st_base + ((int64_t)acc * A.h_v + h) * head_elems + colbase;
+    ActT* __restrict__ cbuf = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
+    const ActT* __restrict__ Wc = static_cast<const ActT*>(A.conv_w);
+
+    // ---- conv channels: weights, the window rows acc..acc+2 of the conv buffer
+    int64_t gc[NCH];
+    float w[NCH][4], xw0[NCH], xw1[NCH], xw2[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int lc = tid + j * BLOCK_THREADS;
+        gc[j] = -1;
+        if (lc < NLC) {
+            gc[j] = lc < DK ? (int64_t)ki * DK + lc
+                  : lc < 2 * DK ? (int64_t)A.h_k * DK + (int64_t)ki * DK + (lc - DK)
+                  : 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + (lc - 2 * DK);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[j][e] = to_f32(Wc[gc[j] * 4 + e]);
+            xw0[j] = to_f32(cbuf[(int64_t)(acc + 0) * C + gc[j]]);
+            xw1[j] = to_f32(cbuf[(int64_t)(acc + 1) * C + gc[j]]);
+            xw2[j] = to_f32(cbuf[(int64_t)(acc + 2) * C + gc[j]]);
+        }
+    }
+    const float exp_alog = expf(A.a_log[h]);
+    const float dtb = A.dt_bias[h];
+
+    // ---- candidate inputs (loaded early; consumed after the replay)
+    float xp[NCH][TT];
+    float pa[TT / 4], pb[TT / 4];
+    {
+        const ActT* X = static_cast<const ActT*>(A.x);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                xp[j][tt] = (gc[j] >= 0 && tt < nc)
+                                ? to_f32(X[((int64_t)req * nc + tt) * A.x_stride + gc[j]]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < TT / 4; ++i) {
+            const int tt = wv + 4 * i;
+            const bool ok = tt < nc;
+            const int64_t row = ((int64_t)req * nc + tt) * A.ab_stride + h;
+            pa[i] = ok ? to_f32(static_cast<const ActT*>(A.a)[row]) : 0.0f;
+            pb[i] = ok ? to_f32(static_cast<const ActT*>(A.b)[row]) : 0.0f;
+        }
+    }
+
+    // ---- starting state
+    float s[R];
+    load_state_block<StT, DK>(Sload, A.d_v, stage, s, tid);
+
+    const int col = lane_col(tid), rb = lane_rowgroup(tid) * R;
+    auto load_kq = [&](int tt, float (&k)[R], float (&q)[R]) {
+#pragma unroll
+        for (int m = 0; m < R; m += 4) {
+            const float4 kv4 = *reinterpret_cast<const float4*>(sk + tt * DK + rb + m);
+            const float4 qv4 = *reinterpret_cast<const float4*>(sq + tt * DK + rb + m);
+            k[m] = kv4.x; k[m + 1] = kv4.y; k[m + 2] = kv4.z; k[m + 3] = kv4.w;
+            q[m] = qv4.x; q[m + 1] = qv4.y; q[m + 2] = qv4.z; q[m + 3] = qv4.w;
+        }
+    };
+    const int64_t row_bytes = A.record_row_bytes;
+    const int64_t rows_per_slot = A.n_spec + 1;
+
+    // ---- one-page: replay rows 0..acc of the live record, store the checkpoint
+    if (LAYOUT == GDN_SPEC_ONEPAGE) {
+        if (n_replay > 0) {
+            const uint8_t* rec = pg + A.record_off + (int64_t)L * rows_per_slot * row_bytes;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                if (gc[j] < 0) continue;
+                const int lc = tid + j * BLOCK_THREADS;
+                float* dst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
+                const int ld = lc < 2 * DK ? DK : BV;
+                for (int i = 0; i < n_replay; ++i)
+                    dst[i * ld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc[j]];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ii = 0; ii < TT / 4; ++ii) {
+                const int tt = wv + 4 * ii;
+                if (tt < n_replay) {
+                    const float* rrow = reinterpret_cast<const float*>(rec + tt * row_bytes);
+                    const float kq = gate_qk<DK>(sq + tt * DK, sk + tt * DK, A.scale, A.eps, lane);
+                    (void)kq;
+                    float eg, beta;
+                    gate_scalars(rrow[C + h], rrow[C + A.h_v + h], exp_alog, dtb, eg, beta);
+                    if (lane == 0) {
+                        ssc[tt * 4 + 0] = eg;
+                        ssc[tt * 4 + 1] = beta;
+                    }
+                }
+            }
+            __syncthreads();
+            for (int tt = 0; tt < n_replay; ++tt) {
+                float k[R], q[R];
+                load_kq(tt, k, q);
+                delta_update<R>(s, k, sv[tt * BV + col], ssc[tt * 4 + 0], ssc[tt * 4 + 1]);
+            }
+            __syncthreads();
+        }
+        // the checkpoint; continue from its stored (rounded) value
+        store_state_block<StT, DK>(Sload, A.d_v, stage, s, tid);
+#pragma unroll
+        for (int m = 0; m < R; ++m) s[m] = round_as<StT>(s[m]);
+    }
+
+    // ---- candidates: conv (+ record), gating, recurrence
+    const bool qk_writer = (h == ki * rr) && (blk == 0);
+    uint8_t* recw = pg + A.record_off + (int64_t)(1 - L) * rows_per_slot * row_bytes;
+    if (nc > 0) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            if (gc[j] < 0) continue;
+            const int lc = tid + j * BLOCK_THREADS;
+            float* dst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
+            const int ld = lc < 2 * DK ? DK : BV;
+            const bool rec_this = (LAYOUT == GDN_SPEC_ONEPAGE) && (lc >= 2 * DK || qk_writer);
+            float x3 = xw0[j], x2 = xw1[j], x1 = xw2[j];
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                if (tt < nc) {
+                    const float x0 = xp[j][tt];
+                    const float y = silu(conv4(w[j], x3, x2, x1, x0));
+                    dst[tt * ld] = y;
+                    if (rec_this) reinterpret_cast<float*>(recw + tt * row_bytes)[gc[j]] = y;
+                    x3 = x2; x2 = x1; x1 = x0;
+                }
+            }
+        }
+    } else {
+        // commit only: make sure the window loads have landed before arriving
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+            if (gc[j] >= 0) sq[tid + j * BLOCK_THREADS] = xw0[j] + xw1[j] + xw2[j];
+    }
+    __syncthreads();
+    if (tid == 0)
+        sh_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk)) ? 1 : 0;
+    if (nc > 0) {
+#pragma unroll
+        for (int ii = 0; ii < TT / 4; ++ii) {
+            const int tt = wv + 4 * ii;
+            if (tt < nc) {
+                const float kq = gate_qk<DK>(sq + tt * DK, sk + tt * DK, A.scale, A.eps, lane);
+                float eg, beta;
+                gate_scalars(pa[ii], pb[ii], exp_alog, dtb, eg, beta);
+                if (lane == 0) {
+                    ssc[tt * 4 + 0] = eg;
+                    ssc[tt * 4 + 1] = beta;
+                    ssc[tt * 4 + 2] = kq;
+                    if (LAYOUT == GDN_SPEC_ONEPAGE && blk == 0) {
+                        float* rrow = reinterpret_cast<float*>(recw + tt * row_bytes);
+                        rrow[C + h] = pa[ii];
+                        rrow[C + A.h_v + h] = pb[ii];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        float* __restrict__ O = A.o + (int64_t)req * nc * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + col;
+        const int64_t o_stride = (int64_t)A.h_v * A.d_v;
+        for (int tt = 0; tt < nc; ++tt) {
+            float k[R], q[R];
+            load_kq(tt, k, q);
+            const float o = delta_step<R>(s, k, q, sv[tt * BV + col], ssc[tt * 4 + 0], ssc[tt * 4 + 1],
+                                          ssc[tt * 4 + 2]);
+            if (lane_rowgroup(tid) == 0) O[(int64_t)tt * o_stride] = o;
+            if (LAYOUT == GDN_SPEC_SLOTS)
+                store_state_block<StT, DK>(st_base + ((int64_t)tt * A.h_v + h) * head_elems + colbase, A.d_v,
+                                           stage, s, tid);
+        }
+    } else if (LAYOUT == GDN_SPEC_SLOTS) {
+        store_state_block<StT, DK>(st_base + (int64_t)h * head_elems + colbase, A.d_v, stage, s, tid);
+    }
+    __syncthreads();
+
+    // ---- conv buffer: [a'+1, a'+2, candidates] or [a', a'+1, a'+2]
+    const bool last = sh_last != 0;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        if (gc[j] < 0) continue;
+        const int lc = tid + j * BLOCK_THREADS;
+        if (lc < 2 * DK && !last) continue;
+        if (nc > 0) {
+            cbuf[0 * C + gc[j]] = from_f32<ActT>(xw1[j]);
+            cbuf[1 * C + gc[j]] = from_f32<ActT>(xw2[j]);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                if (tt < nc) cbuf[(int64_t)(2 + tt) * C + gc[j]] = from_f32<ActT>(xp[j][tt]);
+        } else {
+            cbuf[0 * C + gc[j]] = from_f32<ActT>(xw0[j]);
+            cbuf[1 * C + gc[j]] = from_f32<ActT>(xw1[j]);
+            cbuf[2 * C + gc[j]] = from_f32<ActT>(xw2[j]);
+        }
+    }
+
+    // ---- done counter: the last workgroup of the request flips the flag
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t total = (uint32_t)(A.h_v * nblk);
+        const uint32_t prev = __hip_atomic_fetch_add(&hdr->flag, 256u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if ((prev >> 8) + 1u == total) {
+            hdr->n_rows[1 - L] = (uint32_t)nc;
+            hdr->accepted = (uint32_t)acc;
+            __hip_atomic_store(&hdr->flag, (uint32_t)((1 - L) | (par << 1)), __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <typename ActT, typename StT, int DK>
+static hipError_t launch_verify_t(const VerifyArgs& a, int layout, hipStream_t s) {
+    const int nblk = a.d_v / BV;
+    const int64_t grid = (int64_t)a.n_req * a.h_v * nblk;
+    if (grid == 0) return hipSuccess;
+    if (layout == GDN_SPEC_ONEPAGE)
+        hipLaunchKernelGGL((k_gdn_verify<ActT, StT, DK, GDN_SPEC_ONEPAGE>), dim3((unsigned)grid),
+                           dim3(BLOCK_THREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_gdn_verify<ActT, StT, DK, GDN_SPEC_SLOTS>), dim3((unsigned)grid),
+                           dim3(BLOCK_THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename ActT, typename StT>
+static hipError_t launch_verify_dk(const VerifyArgs& a, int d_k, int layout, hipStream_t s) {
+    switch (d_k) {
+        case 32: return launch_verify_t<ActT, StT, 32>(a, layout, s);
+        case 64: return launch_verify_t<ActT, StT, 64>(a, layout, s);
+        case 128: return launch_verify_t<ActT, StT, 128>(a, layout, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_verify(const VerifyArgs& a, int d_k, int act_dtype, int state_dtype, int layout,
+                         hipStream_t s) {
+    if (act_dtype == GDN_BF16)
+        return state_dtype == GDN_BF16 ? launch_verify_dk<bf16_t, bf16_t>(a, d_k, layout, s)
+                                       : launch_verify_dk<bf16_t, float>(a, d_k, layout, s);
+    return state_dtype == GDN_BF16 ? launch_verify_dk<float, bf16_t>(a, d_k, layout, s)
+                                   : launch_verify_dk<float, float>(a, d_k, layout, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,212 @@
+"""GPU parity of the token-by-token core (gdn_recurrent_seq) and the conv
+update (gdn_conv_update) against the fp64 oracle, plus the bit-exact
+properties between launches.  Tolerance: max relative error 1e-4 per
+(tensor, sequence, head) slice for the fp32-state path."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_workloads as wk
+from gpu_util import (DEV, dev, dims_of, gdn, host, make_batch, max_slice_rel_S, max_slice_rel_o,
+                      oracle_seq, params_of, rel, run_seq, seq_pools)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _check(ora, wl, inp, pages=None, has_init=None, tol=TOL):
+    o, conv, state = run_seq(wl, inp, pages=pages, has_init=has_init)
+    o_ref, win_ref, S_ref = oracle_seq(ora, wl, inp, has_init=has_init)
+    pages = list(range(len(wl.seqlens))) if pages is None else pages
+    idx = [p for p in pages]
+    assert max_slice_rel_o(host(o), o_ref, inp["cu_seqlens"]) <= tol
+    S = host(state.buf)[idx]
+    assert max_slice_rel_S(S, S_ref) <= tol
+    np.testing.assert_array_equal(host(conv.buf)[idx], win_ref)  # rolled window: exact data movement
+    assert int(conv.sync.abs().sum()) == 0
+    return o, conv, state
+
+
+def test_tiny_parity(ora):
+    wl = wk.TINY
+    _check(ora, wl, wk.make_sequence_inputs(wl))
+
+
+def test_decode_parity(ora):
+    wl = wk.DECODE
+    _check(ora, wl, wk.make_sequence_inputs(wl))
+
+
+def test_short_prefill_parity(ora):
+    wl = wk.SHORT_PREFILL
+    _check(ora, wl, wk.make_sequence_inputs(wl))
+
+
+@pytest.mark.parametrize("lens", [(1, 2, 3, 17, 33), (0, 5, 0, 16), (2,), (47,)])
+def test_ragged_edges(ora, lens):
+    wl = wk.DECODE.replace(seqlens=lens, seed=7)
+    _check(ora, wl, wk.make_sequence_inputs(wl))
+
+
+def test_has_init_zero_and_padding(ora):
+    wl = wk.DECODE.replace(seqlens=(5, 9, 3, 6), seed=8)
+    inp = wk.make_sequence_inputs(wl)
+    has = np.array([0, 1, 0, 1], np.uint8)
+    g = gdn()
+    # padding row (-1) skipped: nothing of it read or written
+    pages = [3, -1, 0, 2]
+    o, conv, state = run_seq(wl, inp, pages=pages, n_pages=5, has_init=has)
+    o_ref, win_ref, S_ref = oracle_seq(ora, wl, inp, has_init=has)
+    cu = inp["cu_seqlens"]
+    oh = host(o)
+    for s, p in enumerate(pages):
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        if p < 0:
+            assert np.isnan(oh[rows]).all()
+            continue
+        assert max_slice_rel_o(oh[rows], o_ref[rows], [0, cu[s + 1] - cu[s]]) <= TOL
+        assert max_slice_rel_S(host(state.buf)[p:p + 1], S_ref[s:s + 1]) <= TOL
+        np.testing.assert_array_equal(host(conv.buf)[p], win_ref[s])
+    # pages 1 and 4 were never touched
+    assert float(state.buf[1].abs().sum()) == 0.0 and float(state.buf[4].abs().sum()) == 0.0
+
+
+def test_d_k_64_and_scale(ora):
+    wl = wk.Workload("d64", h_k=4, h_v=8, d_k=64, d_v=64, conv_w=4, act_dtype=wk.BF16,
+                     state_dtype=wk.F32, seqlens=(7, 30), seed=9, scale=64 ** -0.5)
+    _check(ora, wl, wk.make_sequence_inputs(wl))
+
+
+def test_mild_decay_long_memory(ora):
+    """Weak decay keeps far history in the state, so state propagation errors
+    cannot hide behind the workload's strong decay."""
+    wl = wk.DECODE.replace(seqlens=(200, 61), seed=10)
+    inp = wk.make_sequence_inputs(wl)
+    inp["a_log"] = np.full_like(inp["a_log"], np.log(0.02))
+    _check(ora, wl, inp)
+
+
+def test_bf16_state(ora):
+    wl = wk.DECODE.replace(seqlens=(9, 1, 20), state_dtype=wk.BF16, seed=11)
+    inp = wk.make_sequence_inputs(wl)
+    o, conv, state = run_seq(wl, inp)
+    o_ref, win_ref, S_ref = oracle_seq(ora, wl, inp)
+    assert max_slice_rel_o(host(o), o_ref, inp["cu_seqlens"]) <= TOL
+    # the state is stored once, rounded to bf16 (relative step 2^-8)
+    assert max_slice_rel_S(host(state.buf), S_ref) <= 2.0 ** -8
+
+
+def test_one_launch_equals_token_launches():
+    """T tokens in one launch == T launches of one token, bit for bit (fp32
+    state): the per-token arithmetic does not depend on how tokens are batched."""
+    g = gdn()
+    wl = wk.DECODE.replace(seqlens=(21, 6), seed=12)
+    inp = wk.make_sequence_inputs(wl)
+    o_all, conv_all, st_all = run_seq(wl, inp)
+    params = params_of(inp, wl)
+    dims, conv, state = seq_pools(wl, inp, [0, 1], 2)
+    x = dev(inp["x"], dims.act_torch)
+    a = dev(inp["a"], dims.act_torch)
+    b = dev(inp["b"], dims.act_torch)
+    cu = inp["cu_seqlens"]
+    o_tok = torch.full_like(o_all, float("nan"))
+    for s in range(2):
+        for t in range(int(cu[s]), int(cu[s + 1])):
+            batch = make_batch([0, 1], [s], 1)
+            g.gdn_recurrent_seq(dims, params, x[t:t + 1], a[t:t + 1], b[t:t + 1], batch, conv, state,
+                                o=o_tok[t:t + 1])
+    torch.cuda.synchronize()
+    assert torch.equal(o_tok, o_all)
+    assert torch.equal(state.buf, st_all.buf)
+    assert torch.equal(conv.buf, conv_all.buf)
+
+
+def test_deterministic_and_batch_independent():
+    """Two runs agree bit for bit, and a sequence gives the same bits alone
+    as inside a batch (identical copies in lockstep agree with the lone run)."""
+    wl = wk.DECODE.replace(seqlens=(13, 13, 13), seed=13)
+    inp = wk.make_sequence_inputs(wl)
+    for k in ("window0", "S0"):
+        inp[k][1] = inp[k][0]
+        inp[k][2] = inp[k][0]
+    T = 13
+    inp["x"][T:2 * T] = inp["x"][:T]
+    inp["x"][2 * T:] = inp["x"][:T]
+    for k in ("a", "b"):
+        inp[k][T:2 * T] = inp[k][:T]
+        inp[k][2 * T:] = inp[k][:T]
+    o1, c1, s1 = run_seq(wl, inp)
+    o2, c2, s2 = run_seq(wl, inp)
+    assert torch.equal(o1, o2) and torch.equal(s1.buf, s2.buf) and torch.equal(c1.buf, c2.buf)
+    assert torch.equal(o1[:T], o1[T:2 * T]) and torch.equal(o1[:T], o1[2 * T:])
+    lone = wl.replace(seqlens=(13,))
+    inp1 = {k: (v[:1] if k in ("window0", "S0") else v[:T] if k in ("x", "a", "b") else v)
+            for k, v in inp.items()}
+    inp1["cu_seqlens"] = np.array([0, T], np.int32)
+    o3, c3, s3 = run_seq(lone, inp1)
+    assert torch.equal(o3, o1[:T]) and torch.equal(s3.buf[0], s1.buf[0])
+
+
+def test_device_errors_skip_and_report():
+    g = gdn()
+    wl = wk.DECODE.replace(seqlens=(4, 4), seed=14)
+    inp = wk.make_sequence_inputs(wl)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    # page 7 does not exist in a 2-page pool
+    o, conv, state = run_seq(wl, inp, pages=[0, 7], n_pages=2, err=err)
+    assert int(err.item()) & g.GDN_DEVERR_PAGE
+    assert np.isnan(host(o)[4:]).all() and not np.isnan(host(o)[:4]).any()
+
+
+# ------------------------------------------------------------- conv update
+def _conv_call(wl, inp, act, y_dtype, max_seqlen=None, has_init=None):
+    g = gdn()
+    dims = dims_of(wl)
+    n = len(wl.seqlens)
+    conv = g.ConvPool.alloc(dims, n, 3, DEV)
+    for s in range(n):
+        conv.buf[s] = dev(inp["window0"][s], dims.act_torch)
+    x = dev(inp["x"], dims.act_torch)
+    batch = make_batch(inp["cu_seqlens"], list(range(n)), x.shape[0], has_init, max_seqlen)
+    y = g.gdn_conv_update(dims, dev(inp["conv_w"], dims.act_torch), x, batch, conv, activation=act,
+                          y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    return y, conv
+
+
+@pytest.mark.parametrize("max_seqlen", [None, 0])
+def test_conv_update_bit_exact_fp32_model(ora, max_seqlen):
+    """activation off, fp32 output: bit-exact against the fp32 op-order model."""
+    wl = wk.SHORT_PREFILL.replace(seqlens=(45, 200, 0, 3), act_dtype=wk.F32, seed=15)
+    inp = wk.make_sequence_inputs(wl)
+    y, conv = _conv_call(wl, inp, False, "f32", max_seqlen)
+    cu = inp["cu_seqlens"]
+    yh = y.cpu().numpy()
+    for s in range(len(wl.seqlens)):
+        r0, r1 = int(cu[s]), int(cu[s + 1])
+        ref = ora.conv_f32_model(inp["x"][r0:r1], inp["conv_w"], inp["window0"][s])
+        np.testing.assert_array_equal(yh[r0:r1], ref)
+    _, win_ref = ora.conv_update(inp["x"], inp["conv_w"], cu, inp["window0"])
+    np.testing.assert_array_equal(host(conv.buf), win_ref)
+
+
+def test_conv_update_silu_parity(ora):
+    wl = wk.SHORT_PREFILL.replace(seqlens=(45, 83, 159, 1, 2), seed=16)
+    inp = wk.make_sequence_inputs(wl)
+    has = np.array([1, 0, 1, 1, 0], np.uint8)
+    y, conv = _conv_call(wl, inp, True, "f32", has_init=has)
+    y_ref, win_ref = ora.conv_update(inp["x"], inp["conv_w"], inp["cu_seqlens"], inp["window0"], has)
+    assert rel(host(y), y_ref) <= 1e-6
+    np.testing.assert_array_equal(host(conv.buf), win_ref)
+    yb, _ = _conv_call(wl, inp, True, "bf16", has_init=has)
+    assert rel(host(yb), y_ref) <= 2.0 ** -8
+
+
+def test_fused_conv_window_equals_conv_update():
+    """The fused kernel rolls the window exactly as gdn_conv_update does."""
+    wl = wk.SHORT_PREFILL.replace(seqlens=(45, 2, 70), seed=17)
+    inp = wk.make_sequence_inputs(wl)
+    _, conv_fused, _ = run_seq(wl, inp)
+    _, conv_alone = _conv_call(wl, inp, True, "f32")
+    assert torch.equal(conv_fused.buf, conv_alone.buf)
