@@ -1,0 +1,219 @@
+"""GPU tests of speculative verify (gdn_spec_verify): the one-page record
+design against the per-candidate-slot design (bit-exact, fp32 state first,
+then bf16), both against the oracle's verify semantics, the flag-word and
+record bookkeeping, and the device error paths."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_workloads as wk
+from gpu_util import DEV, dev, dims_of, gdn, host, max_slice_rel_o, params_of, run_seq
+
+pytestmark = pytest.mark.gpu
+
+ONEPAGE, SLOTS = 0, 1
+
+
+class VerifyRun:
+    """A request batch stepping through speculative verify on the GPU."""
+
+    def __init__(self, wl, inp, layout, state_dtype, pages_of=None, n_pages=None):
+        g = gdn()
+        self.g, self.wl, self.inp = g, wl, inp
+        self.dims = dims_of(wl, state_dtype=state_dtype, n_spec=wl.n_cand - 1)
+        R = wl.n_req
+        self.req_page = list(range(R)) if pages_of is None else list(pages_of)
+        n_pages = n_pages or (max(self.req_page) + 1)
+        self.pages = g.SpecPages.alloc(self.dims, layout, n_pages, DEV)
+        self.conv = g.ConvPool.alloc(self.dims, n_pages, 3 + self.dims.n_spec, DEV)
+        st = self.pages.states()
+        for r, p in enumerate(self.req_page):
+            if p < 0:
+                continue
+            st[p, 0] = dev(inp["S0"][r], self.dims.state_torch)
+            self.conv.buf[p, :3] = dev(inp["window0"][r], self.dims.act_torch)
+        self.params = params_of(inp, wl)
+        self.rp = torch.tensor(self.req_page, dtype=torch.int32, device=DEV)
+        self.err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.step_no = 0
+
+    def step(self, s, accepted_prev, n_cand=None, parity=None):
+        wl, inp = self.wl, self.inp
+        R, K = wl.n_req, wl.n_cand if n_cand is None else n_cand
+        C = wl.c_conv
+        acc = torch.tensor(np.asarray(accepted_prev, np.int32), device=DEV)
+        par = (self.step_no + 1) & 1 if parity is None else parity
+        pt = torch.full((R,), par, dtype=torch.uint8, device=DEV)
+        if K > 0:
+            x = dev(inp["x"][s][:, :K].reshape(R * K, C), self.dims.act_torch)
+            a = dev(inp["a"][s][:, :K].reshape(R * K, wl.h_v), self.dims.act_torch)
+            b = dev(inp["b"][s][:, :K].reshape(R * K, wl.h_v), self.dims.act_torch)
+            o = torch.full((R * K, wl.h_v, wl.d_v), float("nan"), device=DEV)
+        else:
+            x = a = b = o = None
+        self.g.gdn_spec_verify(self.dims, self.params, self.pages, x, a, b, R, K, self.rp, acc, pt, self.conv,
+                               o=o, err=self.err)
+        if parity is None:
+            self.step_no += 1
+        torch.cuda.synchronize()
+        return None if o is None else o.view(R, K, wl.h_v, wl.d_v)
+
+    def run(self):
+        wl, inp = self.wl, self.inp
+        outs = []
+        for s in range(wl.n_steps):
+            prev = inp["accepted"][s - 1] if s > 0 else np.zeros(wl.n_req, np.int32)
+            outs.append(self.step(s, prev))
+        self.step(0, inp["accepted"][wl.n_steps - 1], n_cand=0)  # commit the last acceptance
+        return torch.stack(outs)  # [steps][R][K][h_v][d_v]
+
+    def committed_state(self):
+        return self.pages.states()[self.req_page, 0]
+
+    def committed_window(self):
+        return self.conv.buf[self.req_page, :3]
+
+
+def _inputs(wl, state_dtype):
+    inp = wk.make_verify_inputs(wl)
+    inp["S0"] = wk.round_to(inp["S0"], state_dtype)
+    return inp
+
+
+def _small(**kw):
+    base = dict(n_req=6, n_steps=5, seed=31)
+    base.update(kw)
+    return wk.SPEC_VERIFY.replace(**base)
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])  # fp32 first: it exposes 1-ulp differences
+def test_onepage_equals_slots_bit_exact(state_dtype):
+    wl = wk.SPEC_VERIFY
+    inp = _inputs(wl, state_dtype)
+    one = VerifyRun(wl, inp, ONEPAGE, state_dtype)
+    slots = VerifyRun(wl, inp, SLOTS, state_dtype)
+    o1, o2 = one.run(), slots.run()
+    assert not torch.isnan(o1).any()
+    assert torch.equal(o1, o2)
+    assert torch.equal(one.committed_state(), slots.committed_state())
+    assert torch.equal(one.conv.buf, slots.conv.buf)
+    assert int(one.err.item()) == 0 and int(slots.err.item()) == 0
+    assert int(one.conv.sync.abs().sum()) == 0 and int(slots.conv.sync.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("state_dtype,tol", [(wk.F32, 1e-4), (wk.BF16, 3e-3)])
+def test_verify_oracle_parity(ora, state_dtype, tol):
+    wl = wk.SPEC_VERIFY
+    inp = _inputs(wl, state_dtype)
+    run = VerifyRun(wl, inp, ONEPAGE, state_dtype)
+    o = host(run.run())
+    dm = ora.dims_of(wl)
+    o_ref, win_ref, S_ref = ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"],
+                                       inp["b"], inp["accepted"], inp["window0"], inp["S0"],
+                                       state_bf16=(state_dtype == wk.BF16))
+    worst = 0.0
+    for r in range(wl.n_req):
+        for h in range(wl.h_v):
+            y, ref = o[:, r, :, h], o_ref[:, r, :, h]
+            worst = max(worst, float(np.abs(y - ref).max() / np.abs(ref).max()))
+    assert worst <= tol, worst
+    S = host(run.committed_state())
+    worstS = max(float(np.abs(S[r, h] - S_ref[r, h]).max() / np.abs(S_ref[r, h]).max())
+                 for r in range(wl.n_req) for h in range(wl.h_v))
+    assert worstS <= tol, worstS
+    np.testing.assert_array_equal(host(run.committed_window()), win_ref)
+
+
+def test_header_bookkeeping():
+    wl = _small()
+    inp = _inputs(wl, wk.F32)
+    run = VerifyRun(wl, inp, ONEPAGE, wk.F32)
+    L = 0
+    for s in range(wl.n_steps):
+        prev = inp["accepted"][s - 1] if s > 0 else np.zeros(wl.n_req, np.int32)
+        run.step(s, prev)
+        hdr = run.pages.header().cpu().numpy()
+        L = 1 - L
+        par = (s + 1) & 1
+        for r in range(wl.n_req):
+            assert hdr[r, 0] == (L | (par << 1))          # live slot, parity, done counter back at 0
+            assert hdr[r, 1 + L] == wl.n_cand            # rows held by the new live slot
+            assert hdr[r, 3] == (prev[r] if s > 0 else 0)  # acceptance echo
+    # record rows: post-conv values of the last step's candidates (fp32), then a and b
+    lay = run.pages.lay
+    rec = run.pages.buf[0, lay["record_off"]:].view(torch.float32)
+    row = lay["record_row_bytes"] // 4
+    slot = L * wl.n_cand
+    a_last = torch.tensor(inp["a"][wl.n_steps - 1][0], device=DEV)
+    got_a = rec[slot * row: (slot + wl.n_cand) * row].view(wl.n_cand, row)[:, wl.c_conv:wl.c_conv + wl.h_v]
+    assert torch.equal(got_a, a_last)
+
+
+def test_all_accepted_chain_equals_sequence_kernel():
+    """With every draft accepted, verify's outputs are the token-by-token
+    kernel's outputs on the concatenated stream, bit for bit (fp32 state)."""
+    wl = _small(n_req=4)
+    inp = _inputs(wl, wk.F32)
+    inp["accepted"][:] = wl.n_cand - 1
+    run = VerifyRun(wl, inp, ONEPAGE, wk.F32)
+    o_ver = run.run()
+    T = wl.n_steps * wl.n_cand
+    sw = wk.DECODE.replace(seqlens=(T,) * wl.n_req)
+    sinp = {"conv_w": inp["conv_w"], "a_log": inp["a_log"], "dt_bias": inp["dt_bias"],
+            "S0": inp["S0"], "window0": inp["window0"],
+            "x": inp["x"].transpose(1, 0, 2, 3).reshape(-1, wl.c_conv),
+            "a": inp["a"].transpose(1, 0, 2, 3).reshape(-1, wl.h_v),
+            "b": inp["b"].transpose(1, 0, 2, 3).reshape(-1, wl.h_v),
+            "cu_seqlens": np.arange(wl.n_req + 1, dtype=np.int32) * T}
+    o_seq, conv_seq, st_seq = run_seq(sw, sinp)
+    o_seq = o_seq.view(wl.n_req, wl.n_steps, wl.n_cand, wl.h_v, wl.d_v).transpose(0, 1)
+    assert torch.equal(o_ver, o_seq)
+    assert torch.equal(run.committed_state(), st_seq.buf)
+    assert torch.equal(run.committed_window(), conv_seq.buf)
+
+
+def test_lockstep_copies_equal_lone_request():
+    wl = _small(n_req=3)
+    inp = _inputs(wl, wk.BF16)
+    for k in ("S0", "window0"):
+        inp[k][1:] = inp[k][:1]
+    for k in ("x", "a", "b"):
+        inp[k][:, 1:] = inp[k][:, :1]
+    inp["accepted"][:, 1:] = inp["accepted"][:, :1]
+    o3 = VerifyRun(wl, inp, ONEPAGE, wk.BF16).run()
+    lone = wl.replace(n_req=1)
+    inp1 = {k: (v[:1] if k in ("S0", "window0") else v[:, :1] if k in ("x", "a", "b", "accepted") else v)
+            for k, v in inp.items()}
+    o1 = VerifyRun(lone, inp1, ONEPAGE, wk.BF16).run()
+    for r in range(3):
+        assert torch.equal(o3[:, r], o1[:, 0])
+
+
+def test_relaunch_and_bad_acceptance_are_rejected():
+    g = gdn()
+    wl = _small(n_req=3)
+    inp = _inputs(wl, wk.F32)
+    run = VerifyRun(wl, inp, ONEPAGE, wk.F32)
+    run.step(0, np.zeros(3, np.int32))
+    snap = run.pages.buf.clone(), run.conv.buf.clone()
+    # the same step again (same parity) is refused and changes nothing
+    run.step(1, np.zeros(3, np.int32), parity=1)
+    assert int(run.err.item()) & g.GDN_DEVERR_PARITY
+    assert torch.equal(run.pages.buf, snap[0]) and torch.equal(run.conv.buf, snap[1])
+    run.err.zero_()
+    # an acceptance beyond the record's rows is refused
+    run.step(1, np.array([0, wl.n_cand, 1], np.int32))
+    assert int(run.err.item()) & g.GDN_DEVERR_ACCEPTED
+    hdr = run.pages.header().cpu().numpy()
+    assert hdr[1, 0] == snap[0][1, :4].view(torch.int32)[0].item()   # request 1 untouched
+    assert hdr[0, 0] != snap[0][0, :4].view(torch.int32)[0].item()   # the others advanced
+
+
+def test_padding_requests_are_skipped():
+    wl = _small(n_req=4)
+    inp = _inputs(wl, wk.F32)
+    run = VerifyRun(wl, inp, ONEPAGE, wk.F32, pages_of=[2, -1, 0, 3], n_pages=5)
+    before = run.pages.buf.clone()
+    o = run.step(0, np.zeros(4, np.int32))
+    assert torch.isnan(o[1]).all() and not torch.isnan(o[0]).any()
+    assert torch.equal(run.pages.buf[1], before[1]) and torch.equal(run.pages.buf[4], before[4])
