@@ -1,0 +1,386 @@
+"""Benchmark of the GDN layer core on one MI355X.
+
+Headline: the decode workload (64 sequences x 1 token, H_k=16, H_v=32,
+d_k=d_v=128, bf16 activations, fp32 state), one fused conv + gating +
+delta-rule launch per step, reported in microseconds per step for one
+layer, against the HBM roofline of its algorithmic bytes.  The other
+workloads (short ragged prefill, long chunked prefill, speculative verify)
+are reported beside it under "other_workloads".
+
+Inputs are seeded synthetic data (gdn_workloads) already resident in HBM when
+the timed region starts.  State/input pools rotate every step so that the
+working set (>= 512 MiB) cannot sit in the 256 MB last-level cache.  Kernel
+time is taken with HIP events on the stream the kernels are launched on.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gdn_workloads as wk  # noqa: E402
+
+METRIC = "GDN tokens/s/layer (prefill) + decode/verify µs/step at B=64; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix cores
+FP32_VALU_PEAK_TFLOPS = 157.3    # fp32 vector (256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz)
+POOLS = 4
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ byte / flop models
+def decode_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one token-by-token launch: every byte the
+    layer must read or write once."""
+    n = len(wl.seqlens)
+    N = wl.n_tokens
+    act = 2 if wl.act_dtype == wk.BF16 else 4
+    st = 2 if wl.state_dtype == wk.BF16 else 4
+    state = n * wl.h_v * wl.d_k * wl.d_v * st * 2          # read + write
+    x = N * wl.c_conv * act
+    window = n * (wl.conv_w - 1) * wl.c_conv * act * 2    # read + write
+    o = N * wl.h_v * wl.d_v * 4
+    w = wl.c_conv * wl.conv_w * act
+    ab = N * wl.h_v * act * 2
+    params = wl.h_v * 4 * 2
+    return state + x + window + o + w + ab + params
+
+
+def recurrence_flops(wl) -> int:
+    """fp32 flops of the token-by-token recurrence: per token and value head
+    7 d_k d_v (S^T k and S^T q: 2 each; decay, outer product, add: 3)."""
+    return wl.n_tokens * wl.h_v * 7 * wl.d_k * wl.d_v
+
+
+def chunked_flops(wl) -> int:
+    """Canonical flops of the chunked WY/UT form: per value head and token
+    6 d_k d_v + 2C d_k + 4C d_v + 2C^2/3, plus per key head and token 4C d_k."""
+    C, dk, dv = wl.chunk, wl.d_k, wl.d_v
+    per_v = 6 * dk * dv + 2 * C * dk + 4 * C * dv + 2 * C * C / 3
+    per_k = 4 * C * dk
+    return int(wl.n_tokens * (wl.h_v * per_v + wl.h_k * per_k))
+
+
+def chunked_bytes(wl) -> int:
+    n = len(wl.seqlens)
+    N = wl.n_tokens
+    act = 2 if wl.act_dtype == wk.BF16 else 4
+    return (N * wl.c_conv * act + N * wl.h_v * wl.d_v * 4 + N * wl.h_v * act * 2
+            + n * wl.h_v * wl.d_k * wl.d_v * 4 * 2 + n * (wl.conv_w - 1) * wl.c_conv * act * 2)
+
+
+def verify_bytes(wl, state_dtype, mean_replay) -> int:
+    """Algorithmic bytes of one one-page verify step: checkpoint read+write,
+    replayed record rows read, new record rows written, candidate rows, conv
+    buffer (window read + rolled buffer written), outputs."""
+    R, K = wl.n_req, wl.n_cand
+    st = 2 if state_dtype == wk.BF16 else 4
+    act = 2 if wl.act_dtype == wk.BF16 else 4
+    row = (wl.c_conv + 2 * wl.h_v) * 4
+    state = R * wl.h_v * wl.d_k * wl.d_v * st * 2
+    rec = R * (mean_replay + K) * row
+    x = R * K * (wl.c_conv + 2 * wl.h_v) * act
+    conv = R * (3 + 2 + K) * wl.c_conv * act
+    o = R * K * wl.h_v * wl.d_v * 4
+    return int(state + rec + x + conv + o)
+
+
+# ------------------------------------------------------------------- runners
+class Timer:
+    """Per-launch HIP event pairs on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def time(self, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+
+
+def _upload(torch, arr, dt):
+    return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to("cuda").to(dt)
+
+
+class SeqWorkload:
+    """Token-by-token (or chunked) layer over one ragged batch; POOLS copies."""
+
+    def __init__(self, g, torch, wl, chunk=0):
+        self.g, self.torch, self.wl, self.chunk = g, torch, wl, chunk
+        inp = wk.make_sequence_inputs(wl)
+        self.inp = inp
+        d = g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.conv_w, 0, wl.act_dtype, wl.state_dtype, wl.scale,
+                   wl.l2_eps)
+        self.dims = d
+        self.params = g.Params(_upload(torch, inp["conv_w"], d.act_torch), _upload(torch, inp["a_log"], torch.float32),
+                               _upload(torch, inp["dt_bias"], torch.float32))
+        n = len(wl.seqlens)
+        lens = np.diff(inp["cu_seqlens"])
+        self.batch = g.Batch(torch.from_numpy(inp["cu_seqlens"]).cuda(), torch.arange(n, dtype=torch.int32).cuda(),
+                             None, int(lens.max()), int(wl.n_tokens))
+        self.sets = []
+        x = _upload(torch, inp["x"], d.act_torch)
+        a = _upload(torch, inp["a"], d.act_torch)
+        b = _upload(torch, inp["b"], d.act_torch)
+        S0 = _upload(torch, inp["S0"], d.state_torch)
+        W0 = _upload(torch, inp["window0"], d.act_torch)
+        for _ in range(POOLS):
+            conv = g.ConvPool.alloc(d, n, wl.conv_w - 1, "cuda")
+            conv.buf.copy_(W0)
+            state = g.StatePool(S0.clone())
+            o = torch.empty((wl.n_tokens, wl.h_v, wl.d_v), device="cuda")
+            self.sets.append((x.clone(), a.clone(), b.clone(), conv, state, o))
+        self.i = 0
+
+    def launch(self):
+        x, a, b, conv, state, o = self.sets[self.i % POOLS]
+        self.i += 1
+        if self.chunk:
+            self.g.gdn_chunked_prefill(self.dims, self.params, x, a, b, self.batch, conv, state, chunk=self.chunk,
+                                       o=o)
+        else:
+            self.g.gdn_recurrent_seq(self.dims, self.params, x, a, b, self.batch, conv, state, o=o)
+
+
+class VerifyWorkload:
+    """One-page speculative verify steps over n_req requests; POOLS page sets."""
+
+    def __init__(self, g, torch, wl, state_dtype, layout=0):
+        self.g, self.torch, self.wl = g, torch, wl
+        inp = wk.make_verify_inputs(wl)
+        d = g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.conv_w, wl.n_cand - 1, wl.act_dtype, state_dtype,
+                   wl.scale, wl.l2_eps)
+        self.dims = d
+        self.params = g.Params(_upload(torch, inp["conv_w"], d.act_torch), _upload(torch, inp["a_log"], torch.float32),
+                               _upload(torch, inp["dt_bias"], torch.float32))
+        R, K, C = wl.n_req, wl.n_cand, wl.c_conv
+        self.x = [_upload(torch, inp["x"][s].reshape(R * K, C), d.act_torch) for s in range(wl.n_steps)]
+        self.a = [_upload(torch, inp["a"][s].reshape(R * K, wl.h_v), d.act_torch) for s in range(wl.n_steps)]
+        self.b = [_upload(torch, inp["b"][s].reshape(R * K, wl.h_v), d.act_torch) for s in range(wl.n_steps)]
+        self.acc = [torch.from_numpy(inp["accepted"][s]).cuda() for s in range(wl.n_steps)]
+        self.mean_replay = float(np.mean(inp["accepted"]) + 1.0)
+        self.rp = torch.arange(R, dtype=torch.int32, device="cuda")
+        self.sets = []
+        for _ in range(POOLS):
+            pages = g.SpecPages.alloc(d, layout, R, "cuda")
+            pages.states()[:, 0] = _upload(torch, inp["S0"], d.state_torch)
+            conv = g.ConvPool.alloc(d, R, 3 + d.n_spec, "cuda")
+            conv.buf[:, :3] = _upload(torch, inp["window0"], d.act_torch)
+            o = torch.empty((R * K, wl.h_v, wl.d_v), device="cuda")
+            self.sets.append([pages, conv, o, 0])
+        self.i = 0
+        self.par = [torch.full((R,), p, dtype=torch.uint8, device="cuda") for p in (0, 1)]
+
+    def launch(self):
+        st = self.sets[self.i % POOLS]
+        self.i += 1
+        pages, conv, o, n = st
+        s = n % self.wl.n_steps
+        acc = self.acc[(n - 1) % self.wl.n_steps] if n > 0 else self.acc[0] * 0
+        self.g.gdn_spec_verify(self.dims, self.params, pages, self.x[s], self.a[s], self.b[s], self.wl.n_req,
+                               self.wl.n_cand, self.rp, acc, self.par[(n + 1) & 1], conv, o=o)
+        st[3] = n + 1
+
+
+def measure(torch, wload, steps, warmup):
+    for _ in range(warmup):
+        wload.launch()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        timer.time(wload.launch)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    return timer.mean_ms(), wall * 1e3
+
+
+# --------------------------------------------------------------- traffic file
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_ssm_gdn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/hbm_traffic.txt, if they were taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    src = kernel_source_hash()
+    for line in open(path):
+        f = line.split()
+        if len(f) < 4 or f[0] != "traffic" or f[1] != kernel or f[2] != workload:
+            continue
+        kv = dict(t.split("=", 1) for t in f[3:] if "=" in t)
+        if kv.get("src") == src:
+            return float(kv["bytes"])
+    return None
+
+
+# ---------------------------------------------------------------- cpu leg
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle on the decode workload, repeated for about budget_s."""
+    import oracle as ora
+    inp = wk.make_sequence_inputs(wl)
+    dm = ora.dims_of(wl)
+    args = (inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"], inp["b"], inp["cu_seqlens"],
+            inp["window0"], inp["S0"])
+    ora.layer(dm, *args)  # load + warm
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        ora.layer(dm, *args)
+        n += 1
+    dt = (time.perf_counter() - t0) / n
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"the full decode step ({len(wl.seqlens)} seqs x 1 token, all {wl.h_v} heads), "
+                      f"repeated {n} times in {budget_s:.0f} s"}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default="decode,short_prefill,long_prefill,spec_verify")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the GDN core shards by head or request with no exchange, "
+              "and this build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import linear_attention_ssm_gdn_amd as g
+    g.load()
+    only = set(args.only.split(","))
+    result = {"metric": METRIC}
+    other = {}
+
+    # ---- headline: decode
+    wl = wk.DECODE
+    log("decode: building pools")
+    dec = SeqWorkload(g, torch, wl)
+    k_ms, wall_ms = measure(torch, dec, args.steps, args.warmup)
+    us = k_ms * 1e3
+    nbytes = decode_bytes(wl)
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    traffic = read_traffic("k_gdn_seq", "decode")
+    log(f"decode: {us:.2f} us/step kernel, {wall_ms * 1e3:.2f} us/step wall, {achieved:.0f} GB/s")
+    result.update({
+        "value": round(us, 3), "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode", "n_seqs": len(wl.seqlens), "tokens_per_seq": 1, "h_k": wl.h_k,
+                   "h_v": wl.h_v, "d_k": wl.d_k, "d_v": wl.d_v, "conv_w": wl.conv_w, "act_dtype": wl.act_dtype,
+                   "state_dtype": wl.state_dtype, "tokens_per_s_per_layer": round(len(wl.seqlens) / (k_ms * 1e-3)),
+                   "state_pools_rotated": POOLS},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_gdn_seq", "algorithmic_bytes": nbytes},
+    })
+    del dec
+    torch.cuda.empty_cache()
+
+    # ---- short ragged prefill (token by token)
+    if "short_prefill" in only:
+        wl = wk.SHORT_PREFILL
+        log("short_prefill")
+        w = SeqWorkload(g, torch, wl)
+        k_ms, wall_ms = measure(torch, w, max(args.steps // 4, 10), 5)
+        fl = recurrence_flops(wl)
+        tf = fl / (k_ms * 1e-3) / 1e12
+        other["short_prefill"] = {
+            "value": round(wl.n_tokens / (k_ms * 1e-3)), "unit": "tokens/s/layer", "us_per_call": round(k_ms * 1e3, 2),
+            "us_per_token_critical_path": round(k_ms * 1e3 / max(wl.seqlens), 4),
+            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": read_traffic("k_gdn_seq", "short_prefill"),
+                         "kernel": "k_gdn_seq", "algorithmic_flops": fl},
+            "config": {"seqlens": list(wl.seqlens)}}
+        log(f"short_prefill: {k_ms * 1e3:.1f} us, {tf:.2f} TFLOP/s")
+        del w
+        torch.cuda.empty_cache()
+
+    # ---- long chunked prefill
+    if "long_prefill" in only:
+        wl = wk.LONG_PREFILL
+        try:
+            g.gdn_chunked_workspace_bytes(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v), len(wl.seqlens), wl.n_tokens,
+                                          wl.chunk)
+            log("long_prefill")
+            w = SeqWorkload(g, torch, wl, chunk=wl.chunk)
+            k_ms, wall_ms = measure(torch, w, max(args.steps // 20, 5), 2)
+            fl = chunked_flops(wl)
+            tf = fl / (k_ms * 1e-3) / 1e12
+            other["long_prefill"] = {
+                "value": round(wl.n_tokens / (k_ms * 1e-3)), "unit": "tokens/s/layer", "us_per_call": round(k_ms * 1e3, 1),
+                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                             "traffic": read_traffic("k_gdn_chunk", "long_prefill"), "kernel": "k_gdn_chunk",
+                             "algorithmic_flops": fl,
+                             "hbm_frac": round(chunked_bytes(wl) / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                "config": {"n_seqs": len(wl.seqlens), "seqlen": wl.seqlens[0], "chunk": wl.chunk}}
+            log(f"long_prefill: {k_ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+            del w
+            torch.cuda.empty_cache()
+        except g.GdnError as e:
+            other["long_prefill"] = {"value": None, "note": f"not available: {e}"}
+
+    # ---- speculative verify (one page), fp32 and bf16 state
+    if "spec_verify" in only:
+        wl = wk.SPEC_VERIFY
+        res = {}
+        for sd in (wk.F32, wk.BF16):
+            log(f"spec_verify {sd}")
+            w = VerifyWorkload(g, torch, wl, sd)
+            k_ms, wall_ms = measure(torch, w, max(args.steps // 2, 10), 10)
+            nb = verify_bytes(wl, sd, w.mean_replay)
+            gbs = nb / (k_ms * 1e-3) / 1e9
+            res[sd] = {"value": round(k_ms * 1e3, 2), "unit": "us/step",
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                    "traffic": read_traffic("k_gdn_verify", "spec_verify_" + sd),
+                                    "kernel": "k_gdn_verify", "algorithmic_bytes": nb}}
+            log(f"spec_verify {sd}: {k_ms * 1e3:.2f} us/step, {gbs:.0f} GB/s")
+            del w
+            torch.cuda.empty_cache()
+        lay1 = g.gdn_spec_page_layout(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, n_spec=wl.n_cand - 1), 0)["page_bytes"]
+        lay8 = g.gdn_spec_page_layout(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, n_spec=wl.n_cand - 1), 1)["page_bytes"]
+        other["spec_verify"] = {"state_f32": res[wk.F32], "state_bf16": res[wk.BF16],
+                                "page_bytes_onepage_f32": lay1, "page_bytes_slots_f32": lay8,
+                                "config": {"n_req": wl.n_req, "n_cand": wl.n_cand}}
+
+    result["other_workloads"] = other
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wk.DECODE)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

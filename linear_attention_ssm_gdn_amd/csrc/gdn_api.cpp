@@ -163,7 +163,8 @@ GDN_EXPORT int32_t gdn_recurrent_seq(const gdn_dims* dims, const gdn_params* par
     A.state = state.base; A.state_page_stride = state.page_stride; A.state_n_pages = state.n_pages;
     A.o = o; A.err = err; A.h_k = dims->h_k; A.h_v = dims->h_v; A.d_v = dims->d_v;
     A.scale = dims->scale; A.eps = dims->l2_eps;
-    return from_hip(gdn::launch_seq(A, dims->d_k, dims->act_dtype, dims->state_dtype, (hipStream_t)stream));
+    return from_hip(gdn::launch_seq(A, dims->d_k, dims->act_dtype, dims->state_dtype, batch->max_seqlen,
+                                    (hipStream_t)stream));
 }
 
 GDN_EXPORT int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* params, const void* x,

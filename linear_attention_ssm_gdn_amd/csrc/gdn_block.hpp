@@ -1,30 +1,34 @@
 // gdn_block.hpp -- workgroup-level pieces shared by the token-by-token and
 // verify kernels.
 //
-// Work layout: one workgroup of 256 threads (4 waves of 64) owns one value
-// head's BV = 32 state columns for one sequence (or request).  In the
-// recurrence every lane holds R = d_k/8 rows of one column: lane l of wave
-// w owns column 8w + (l >> 3) and rows (l & 7)*R .. (l & 7)*R + R - 1, so
-// the d_k-long dot products reduce inside an aligned group of 8 lanes with
-// three DPP steps and no LDS round trip.  State blocks move between HBM and
-// this layout through an LDS stage so that global accesses stay 16-byte and
-// row-contiguous.
+// Work layout: one workgroup of 512 threads (8 waves of 64) owns BV = 32*CPL
+// state columns of one value head for one sequence (or request).  The 16
+// lanes of a DPP row hold the d_k rows of the same CPL columns, R = d_k/16
+// rows per lane, so each d_k-long dot product reduces inside the row with
+// four DPP steps and no LDS traffic:
+//   wave w, lane l:  row group rg = l & 15  (rows rg*R .. rg*R+R-1),
+//                    column group cg = 4w + (l >> 4)  (columns cg*CPL .. +CPL-1).
+// CPL = 1 suits long token loops (fewest operations per token on the
+// critical path); CPL = 4 suits decode and verify (a whole 128-column head
+// per workgroup, loaded with 16-byte vector loads straight into registers).
 #pragma once
 
 #include "gdn_device.hpp"
 
 namespace gdn {
 
-constexpr int BLOCK_THREADS = 256;
-constexpr int BV = 32;  // value columns per workgroup
+constexpr int BLOCK_THREADS = 512;
 
-__device__ __forceinline__ int lane_col(int tid) { return ((tid >> 6) << 3) + ((tid & 63) >> 3); }
-__device__ __forceinline__ int lane_rowgroup(int tid) { return tid & 7; }
+__device__ __forceinline__ int lane_rowgroup(int tid) { return tid & 15; }
+__device__ __forceinline__ int lane_colgroup(int tid) { return ((tid >> 6) << 2) + ((tid & 63) >> 4); }
 
-// 16-byte vector of state elements.
-template <typename StT> struct Vec16;
-template <> struct Vec16<float> {
-    static constexpr int N = 4;
+// CPL consecutive state elements of one row.
+template <typename StT, int CPL> struct RowVec;
+template <> struct RowVec<float, 1> {
+    __device__ static void load(const float* p, float (&v)[1]) { v[0] = *p; }
+    __device__ static void store(float* p, const float (&v)[1]) { *p = v[0]; }
+};
+template <> struct RowVec<float, 4> {
     __device__ static void load(const float* p, float (&v)[4]) {
         const float4 t = *reinterpret_cast<const float4*>(p);
         v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
@@ -33,72 +37,82 @@ template <> struct Vec16<float> {
         *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     }
 };
-template <> struct Vec16<bf16_t> {
-    static constexpr int N = 8;
-    __device__ static void load(const bf16_t* p, float (&v)[8]) {
-        const uint4 t = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
+template <> struct RowVec<bf16_t, 1> {
+    __device__ static void load(const bf16_t* p, float (&v)[1]) { v[0] = to_f32(*p); }
+    __device__ static void store(bf16_t* p, const float (&v)[1]) { *p = f32_to_bf16(v[0]); }
+};
+template <> struct RowVec<bf16_t, 4> {
+    __device__ static void load(const bf16_t* p, float (&v)[4]) {
+        const uint2 t = *reinterpret_cast<const uint2*>(p);
+        v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
+        v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
     }
-    __device__ static void store(bf16_t* p, const float (&v)[8]) {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
-        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    __device__ static void store(bf16_t* p, const float (&v)[4]) {
+        const uint32_t a = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t b = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
     }
 };
 
-constexpr int STAGE_LD = BV + 1;  // padded LDS row of the state stage
-
-// Load a d_k x BV state block (row stride ld elements) into the lane layout.
-// `stage` holds DK * STAGE_LD floats; the call ends with a barrier so the
-// stage may be reused.
-template <typename StT, int DK>
-__device__ __forceinline__ void load_state_block(const StT* __restrict__ src, int64_t ld, float* stage,
-                                                 float (&s)[DK / 8], int tid) {
-    using V = Vec16<StT>;
-    constexpr int TPR = BV / V::N;             // threads per row
-    constexpr int RPP = BLOCK_THREADS / TPR;   // rows per pass
-    const int c = (tid % TPR) * V::N;
-    for (int r = tid / TPR; r < DK; r += RPP) {
-        float v[V::N];
-        V::load(src + (int64_t)r * ld + c, v);
+// Load this lane's R x CPL part of a state block; `blk` points at row 0,
+// column 0 of the workgroup's block, rows ld elements apart.
+template <typename StT, int DK, int CPL>
+__device__ __forceinline__ void load_state(const StT* __restrict__ blk, int64_t ld, float (&s)[CPL][DK / 16],
+                                           int tid) {
+    constexpr int R = DK / 16;
+    const StT* p = blk + (int64_t)(lane_rowgroup(tid) * R) * ld + lane_colgroup(tid) * CPL;
 #pragma unroll
-        for (int e = 0; e < V::N; ++e) stage[r * STAGE_LD + c + e] = v[e];
+    for (int m = 0; m < R; ++m) {
+        float v[CPL];
+        RowVec<StT, CPL>::load(p + (int64_t)m * ld, v);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) s[c][m] = v[c];
     }
-    __syncthreads();
-    constexpr int R = DK / 8;
-    const int col = lane_col(tid), rb = lane_rowgroup(tid) * R;
-#pragma unroll
-    for (int m = 0; m < R; ++m) s[m] = stage[(rb + m) * STAGE_LD + col];
-    __syncthreads();
 }
 
-// Store the lane-layout block back (rounded to StT); ends with a barrier.
-template <typename StT, int DK>
-__device__ __forceinline__ void store_state_block(StT* __restrict__ dst, int64_t ld, float* stage,
-                                                  const float (&s)[DK / 8], int tid) {
-    using V = Vec16<StT>;
-    constexpr int R = DK / 8;
-    const int col = lane_col(tid), rb = lane_rowgroup(tid) * R;
+template <typename StT, int DK, int CPL>
+__device__ __forceinline__ void store_state(StT* __restrict__ blk, int64_t ld, const float (&s)[CPL][DK / 16],
+                                            int tid) {
+    constexpr int R = DK / 16;
+    StT* p = blk + (int64_t)(lane_rowgroup(tid) * R) * ld + lane_colgroup(tid) * CPL;
 #pragma unroll
-    for (int m = 0; m < R; ++m) stage[(rb + m) * STAGE_LD + col] = s[m];
-    __syncthreads();
-    constexpr int TPR = BV / V::N;
-    constexpr int RPP = BLOCK_THREADS / TPR;
-    const int c = (tid % TPR) * V::N;
-    for (int r = tid / TPR; r < DK; r += RPP) {
-        float v[V::N];
+    for (int m = 0; m < R; ++m) {
+        float v[CPL];
 #pragma unroll
-        for (int e = 0; e < V::N; ++e) v[e] = stage[r * STAGE_LD + c + e];
-        V::store(dst + (int64_t)r * ld + c, v);
+        for (int c = 0; c < CPL; ++c) v[c] = s[c][m];
+        RowVec<StT, CPL>::store(p + (int64_t)m * ld, v);
     }
-    __syncthreads();
+}
+
+// This lane's R rows of a d_k-long LDS row.
+template <int R>
+__device__ __forceinline__ void lds_rows(const float* row, int tid, float (&out)[R]) {
+    const float* p = row + lane_rowgroup(tid) * R;
+    if constexpr (R % 4 == 0) {
+#pragma unroll
+        for (int m = 0; m < R; m += 4) {
+            const float4 t = *reinterpret_cast<const float4*>(p + m);
+            out[m] = t.x; out[m + 1] = t.y; out[m + 2] = t.z; out[m + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < R; m += 2) {
+            const float2 t = *reinterpret_cast<const float2*>(p + m);
+            out[m] = t.x; out[m + 1] = t.y;
+        }
+    }
+}
+
+template <int CPL>
+__device__ __forceinline__ void lds_cols(const float* row, int tid, float (&out)[CPL]) {
+    const float* p = row + lane_colgroup(tid) * CPL;
+    if constexpr (CPL == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(p);
+        out[0] = t.x; out[1] = t.y; out[2] = t.z; out[3] = t.w;
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) out[c] = p[c];
+    }
 }
 
 // Gating of one token by one wave (part (b)): L2-normalise the post-conv q

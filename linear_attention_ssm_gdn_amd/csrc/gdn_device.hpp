@@ -58,12 +58,15 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 8 lanes {l & ~7 .. l | 7}; every lane of the group receives
-// the same bits.  Tree: xor 1, xor 2, then the mirrored half-row.
-__device__ __forceinline__ float reduce8(float x) {
+// Sum over the 16 lanes of an aligned DPP row; every lane of the row
+// receives the same bits.  Tree: xor 1, xor 2, mirrored half-row (the other
+// quad of the 8), mirrored row (the other 8):
+//   (((x0+x1)+(x2+x3)) + ((x4+x5)+(x6+x7))) + (same over x8..x15).
+__device__ __forceinline__ float reduce16(float x) {
     x = x + dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
     x = x + dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
     x = x + dpp_mov<0x141>(x);  // row_half_mirror
+    x = x + dpp_mov<0x140>(x);  // row_mirror
     return x;
 }
 
@@ -75,57 +78,72 @@ __device__ __forceinline__ float reduce64(float x) {
 }
 
 // --------------------------------------------------- the delta rule (c)
-// One token of the gated delta rule for the R rows x 1 column this lane
-// holds.  The 8 lanes of an aligned lane group hold the d_k = 8R rows of
-// one column.  k, q: this lane's rows of k-hat and scale*q-hat.  Single
-// pass over S_{t-1}: u = S^T k, w = S^T q, then
+// One token of the gated delta rule for CPL state columns.  The 16 lanes of
+// a DPP row together hold the d_k = 16R rows of each of their columns; this
+// lane holds rows rg*R .. rg*R+R-1 (rg = lane & 15) of CPL columns.
+// k, q: this lane's rows of k-hat and scale*q-hat.  Per column, a single pass
+// over S_{t-1}: u = S^T k and w = S^T q (each lane: even rows and odd rows in
+// two fused multiply-add chains, then reduce16), then
 //   delta = beta (v - e^g u),  o = e^g w + (k.q) delta,
 //   S <- e^g S + k delta^T.
-// Returns o (identical bits in the 8 lanes of the group).
-template <int R>
-__device__ __forceinline__ float delta_step(float (&s)[R], const float (&k)[R], const float (&q)[R],
-                                            float v, float eg, float beta, float kq) {
-    float u0 = 0.0f, u1 = 0.0f, w0 = 0.0f, w1 = 0.0f;
+// The operations per column do not depend on CPL, so every kernel built on
+// this function produces the same bits for the same column.
+template <int R, int CPL>
+__device__ __forceinline__ void delta_step(float (&s)[CPL][R], const float (&k)[R], const float (&q)[R],
+                                           const float (&v)[CPL], float eg, float beta, float kq,
+                                           float (&o)[CPL]) {
 #pragma unroll
-    for (int m = 0; m < R; m += 2) {
-        u0 = fmaf(s[m], k[m], u0);
-        w0 = fmaf(s[m], q[m], w0);
-        if (m + 1 < R) {
-            u1 = fmaf(s[m + 1], k[m + 1], u1);
-            w1 = fmaf(s[m + 1], q[m + 1], w1);
+    for (int c = 0; c < CPL; ++c) {
+        float u0 = 0.0f, u1 = 0.0f, w0 = 0.0f, w1 = 0.0f;
+#pragma unroll
+        for (int m = 0; m < R; m += 2) {
+            u0 = fmaf(s[c][m], k[m], u0);
+            w0 = fmaf(s[c][m], q[m], w0);
+            if (m + 1 < R) {
+                u1 = fmaf(s[c][m + 1], k[m + 1], u1);
+                w1 = fmaf(s[c][m + 1], q[m + 1], w1);
+            }
         }
-    }
-    const float u = reduce8(u0 + u1);
-    const float w = reduce8(w0 + w1);
-    const float d = beta * (v - eg * u);
-    const float o = fmaf(kq, d, eg * w);
+        const float u = reduce16(u0 + u1);
+        const float w = reduce16(w0 + w1);
+        const float d = beta * (v[c] - eg * u);
+        o[c] = fmaf(kq, d, eg * w);
 #pragma unroll
-    for (int m = 0; m < R; ++m) s[m] = fmaf(k[m], d, eg * s[m]);
-    return o;
+        for (int m = 0; m < R; ++m) s[c][m] = fmaf(k[m], d, eg * s[c][m]);
+    }
 }
 
 // Replay variant: the same state update without the output.
-template <int R>
-__device__ __forceinline__ void delta_update(float (&s)[R], const float (&k)[R], float v, float eg,
-                                             float beta) {
-    float u0 = 0.0f, u1 = 0.0f;
+template <int R, int CPL>
+__device__ __forceinline__ void delta_update(float (&s)[CPL][R], const float (&k)[R], const float (&v)[CPL],
+                                             float eg, float beta) {
 #pragma unroll
-    for (int m = 0; m < R; m += 2) {
-        u0 = fmaf(s[m], k[m], u0);
-        if (m + 1 < R) u1 = fmaf(s[m + 1], k[m + 1], u1);
+    for (int c = 0; c < CPL; ++c) {
+        float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+        for (int m = 0; m < R; m += 2) {
+            u0 = fmaf(s[c][m], k[m], u0);
+            if (m + 1 < R) u1 = fmaf(s[c][m + 1], k[m + 1], u1);
+        }
+        const float u = reduce16(u0 + u1);
+        const float d = beta * (v[c] - eg * u);
+#pragma unroll
+        for (int m = 0; m < R; ++m) s[c][m] = fmaf(k[m], d, eg * s[c][m]);
     }
-    const float u = reduce8(u0 + u1);
-    const float d = beta * (v - eg * u);
-#pragma unroll
-    for (int m = 0; m < R; ++m) s[m] = fmaf(k[m], d, eg * s[m]);
 }
 
 // ---------------------------------------------------------- arrival count
 // Workgroup arrival on a device-scope counter that returns to zero: the
 // last of `group` arrivals (in any order) gets true and resets the word.
-// Call from one thread after every read the arrival stands for is complete.
+// Call from one thread after a workgroup barrier that follows every read the
+// arrival stands for, with each read value already consumed (so the loads
+// have completed).  No data moves between workgroups through memory inside
+// the kernel: the last arrival only writes what the others have finished
+// reading, and the end of the kernel publishes those writes.  The atomic is
+// therefore relaxed; an acquire/release at device scope would write back and
+// invalidate the whole L2 of the XCD for every workgroup.
 __device__ __forceinline__ bool arrive_last(uint32_t* word, uint32_t group) {
-    const uint32_t prev = __hip_atomic_fetch_add(word, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev + 1u == group) {
         __hip_atomic_store(word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return true;

@@ -63,7 +63,7 @@ struct ChunkArgs {
 };
 
 // Each returns hipSuccess or the launch error.
-hipError_t launch_seq(const SeqArgs& a, int d_k, int act_dtype, int state_dtype, hipStream_t s);
+hipError_t launch_seq(const SeqArgs& a, int d_k, int act_dtype, int state_dtype, int max_seqlen, hipStream_t s);
 hipError_t launch_conv(const ConvArgs& a, int act_dtype, int y_dtype, int max_seqlen, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs& a, int d_k, int act_dtype, int state_dtype, int layout,
                          hipStream_t s);

@@ -11,8 +11,8 @@
 // one kernel template and the same per-token functions, which is what makes
 // them bit-identical.
 //
-// Grid: one workgroup per (request, value head, block of 32 value columns),
-// the lane layout of gdn_block.hpp.  Candidates per step <= 16 (one chunk).
+// Grid: one workgroup per (request, value head, block of 32*CPL value
+// columns), the lane layout of gdn_block.hpp.  Candidates per step <= 16.
 #include "gdn_block.hpp"
 #include "gdn_kernels.h"
 #include "../../include/gdn.h"
@@ -21,19 +21,19 @@ namespace gdn {
 
 constexpr int VER_TT = 16;
 
-template <typename ActT, typename StT, int DK, int LAYOUT>
+template <typename ActT, typename StT, int DK, int CPL, int LAYOUT>
 __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A) {
     constexpr int TT = VER_TT;
-    constexpr int R = DK / 8;
+    constexpr int R = DK / 16;
+    constexpr int BV = 32 * CPL;
     constexpr int NLC = 2 * DK + BV;
-    constexpr int NCH = (NLC + BLOCK_THREADS - 1) / BLOCK_THREADS;
-    __shared__ __attribute__((aligned(16))) float smem[TT * (2 * DK + BV + 4) + DK * STAGE_LD];
+    constexpr int NA = (TT + 7) / 8;
+    static_assert(NLC <= BLOCK_THREADS, "one conv channel per thread");
+    __shared__ __attribute__((aligned(16))) float sq[TT * DK];
+    __shared__ __attribute__((aligned(16))) float sk[TT * DK];
+    __shared__ __attribute__((aligned(16))) float sv[TT * BV];
+    __shared__ float ssc[TT * 4];
     __shared__ int sh_last;
-    float* sq = smem;
-    float* sk = sq + TT * DK;
-    float* sv = sk + TT * DK;
-    float* ssc = sv + TT * BV;
-    float* stage = ssc + TT * 4;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nblk = A.d_v / BV;
@@ -76,49 +76,47 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     const int n_replay = (LAYOUT == GDN_SPEC_ONEPAGE && nr > 0) ? acc + 1 : 0;
     const int nc = A.n_cand;
 
+    // ---- starting state: the checkpoint, or slot[acc]
     const int64_t head_elems = (int64_t)DK * A.d_v;
     StT* __restrict__ st_base = reinterpret_cast<StT*>(pg + A.state_off);
     StT* __restrict__ Sload = (LAYOUT == GDN_SPEC_ONEPAGE)
                                   ? st_base + (int64_t)h * head_elems + colbase
                                   : st_base + ((int64_t)acc * A.h_v + h) * head_elems + colbase;
-    ActT* __restrict__ cbuf = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
-    const ActT* __restrict__ Wc = static_cast<const ActT*>(A.conv_w);
+    float s[CPL][R];
+    load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
 
-    // ---- conv channels: weights, the window rows acc..acc+2 of the conv buffer
-    int64_t gc[NCH];
-    float w[NCH][4], xw0[NCH], xw1[NCH], xw2[NCH];
+    // ---- this thread's conv channel: weights, window rows acc..acc+2 of the conv buffer
+    ActT* __restrict__ cbuf = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
+    const int lc = tid;
+    int64_t gc = -1;
+    float w[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xw0 = 0.0f, xw1 = 0.0f, xw2 = 0.0f;
+    if (lc < NLC) {
+        gc = lc < DK ? (int64_t)ki * DK + lc
+           : lc < 2 * DK ? (int64_t)A.h_k * DK + (int64_t)ki * DK + (lc - DK)
+           : 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + (lc - 2 * DK);
+        const ActT* Wc = static_cast<const ActT*>(A.conv_w) + gc * 4;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        const int lc = tid + j * BLOCK_THREADS;
-        gc[j] = -1;
-        if (lc < NLC) {
-            gc[j] = lc < DK ? (int64_t)ki * DK + lc
-                  : lc < 2 * DK ? (int64_t)A.h_k * DK + (int64_t)ki * DK + (lc - DK)
-                  : 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + (lc - 2 * DK);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[j][e] = to_f32(Wc[gc[j] * 4 + e]);
-            xw0[j] = to_f32(cbuf[(int64_t)(acc + 0) * C + gc[j]]);
-            xw1[j] = to_f32(cbuf[(int64_t)(acc + 1) * C + gc[j]]);
-            xw2[j] = to_f32(cbuf[(int64_t)(acc + 2) * C + gc[j]]);
-        }
+        for (int e = 0; e < 4; ++e) w[e] = to_f32(Wc[e]);
+        xw0 = to_f32(cbuf[(int64_t)(acc + 0) * C + gc]);
+        xw1 = to_f32(cbuf[(int64_t)(acc + 1) * C + gc]);
+        xw2 = to_f32(cbuf[(int64_t)(acc + 2) * C + gc]);
     }
+    float* ydst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
+    const int yld = lc < 2 * DK ? DK : BV;
     const float exp_alog = expf(A.a_log[h]);
     const float dtb = A.dt_bias[h];
 
     // ---- candidate inputs (loaded early; consumed after the replay)
-    float xp[NCH][TT];
-    float pa[TT / 4], pb[TT / 4];
+    float xp[TT];
+    float pa[NA], pb[NA];
     {
         const ActT* X = static_cast<const ActT*>(A.x);
 #pragma unroll
-        for (int j = 0; j < NCH; ++j)
+        for (int tt = 0; tt < TT; ++tt)
+            xp[tt] = (gc >= 0 && tt < nc) ? to_f32(X[((int64_t)req * nc + tt) * A.x_stride + gc]) : 0.0f;
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                xp[j][tt] = (gc[j] >= 0 && tt < nc)
-                                ? to_f32(X[((int64_t)req * nc + tt) * A.x_stride + gc[j]]) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < TT / 4; ++i) {
-            const int tt = wv + 4 * i;
+        for (int i = 0; i < NA; ++i) {
+            const int tt = wv + 8 * i;
             const bool ok = tt < nc;
             const int64_t row = ((int64_t)req * nc + tt) * A.ab_stride + h;
             pa[i] = ok ? to_f32(static_cast<const ActT*>(A.a)[row]) : 0.0f;
@@ -126,20 +124,6 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
         }
     }
 
-    // ---- starting state
-    float s[R];
-    load_state_block<StT, DK>(Sload, A.d_v, stage, s, tid);
-
-    const int col = lane_col(tid), rb = lane_rowgroup(tid) * R;
-    auto load_kq = [&](int tt, float (&k)[R], float (&q)[R]) {
-#pragma unroll
-        for (int m = 0; m < R; m += 4) {
-            const float4 kv4 = *reinterpret_cast<const float4*>(sk + tt * DK + rb + m);
-            const float4 qv4 = *reinterpret_cast<const float4*>(sq + tt * DK + rb + m);
-            k[m] = kv4.x; k[m + 1] = kv4.y; k[m + 2] = kv4.z; k[m + 3] = kv4.w;
-            q[m] = qv4.x; q[m + 1] = qv4.y; q[m + 2] = qv4.z; q[m + 3] = qv4.w;
-        }
-    };
     const int64_t row_bytes = A.record_row_bytes;
     const int64_t rows_per_slot = A.n_spec + 1;
 
@@ -147,23 +131,16 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     if (LAYOUT == GDN_SPEC_ONEPAGE) {
         if (n_replay > 0) {
             const uint8_t* rec = pg + A.record_off + (int64_t)L * rows_per_slot * row_bytes;
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                if (gc[j] < 0) continue;
-                const int lc = tid + j * BLOCK_THREADS;
-                float* dst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
-                const int ld = lc < 2 * DK ? DK : BV;
+            if (gc >= 0)
                 for (int i = 0; i < n_replay; ++i)
-                    dst[i * ld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc[j]];
-            }
+                    ydst[i * yld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc];
             __syncthreads();
 #pragma unroll
-            for (int ii = 0; ii < TT / 4; ++ii) {
-                const int tt = wv + 4 * ii;
+            for (int ii = 0; ii < NA; ++ii) {
+                const int tt = wv + 8 * ii;
                 if (tt < n_replay) {
                     const float* rrow = reinterpret_cast<const float*>(rec + tt * row_bytes);
-                    const float kq = gate_qk<DK>(sq + tt * DK, sk + tt * DK, A.scale, A.eps, lane);
-                    (void)kq;
+                    (void)gate_qk<DK>(sq + tt * DK, sk + tt * DK, A.scale, A.eps, lane);
                     float eg, beta;
                     gate_scalars(rrow[C + h], rrow[C + A.h_v + h], exp_alog, dtb, eg, beta);
                     if (lane == 0) {
@@ -174,54 +151,50 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
             }
             __syncthreads();
             for (int tt = 0; tt < n_replay; ++tt) {
-                float k[R], q[R];
-                load_kq(tt, k, q);
-                delta_update<R>(s, k, sv[tt * BV + col], ssc[tt * 4 + 0], ssc[tt * 4 + 1]);
+                float k[R], v[CPL];
+                lds_rows<R>(sk + tt * DK, tid, k);
+                lds_cols<CPL>(sv + tt * BV, tid, v);
+                delta_update<R, CPL>(s, k, v, ssc[tt * 4 + 0], ssc[tt * 4 + 1]);
             }
             __syncthreads();
         }
         // the checkpoint; continue from its stored (rounded) value
-        store_state_block<StT, DK>(Sload, A.d_v, stage, s, tid);
+        store_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
 #pragma unroll
-        for (int m = 0; m < R; ++m) s[m] = round_as<StT>(s[m]);
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int m = 0; m < R; ++m) s[c][m] = round_as<StT>(s[c][m]);
     }
 
     // ---- candidates: conv (+ record), gating, recurrence
     const bool qk_writer = (h == ki * rr) && (blk == 0);
     uint8_t* recw = pg + A.record_off + (int64_t)(1 - L) * rows_per_slot * row_bytes;
-    if (nc > 0) {
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            if (gc[j] < 0) continue;
-            const int lc = tid + j * BLOCK_THREADS;
-            float* dst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
-            const int ld = lc < 2 * DK ? DK : BV;
+    if (gc >= 0) {
+        if (nc > 0) {
             const bool rec_this = (LAYOUT == GDN_SPEC_ONEPAGE) && (lc >= 2 * DK || qk_writer);
-            float x3 = xw0[j], x2 = xw1[j], x1 = xw2[j];
+            float x3 = xw0, x2 = xw1, x1 = xw2;
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
                 if (tt < nc) {
-                    const float x0 = xp[j][tt];
-                    const float y = silu(conv4(w[j], x3, x2, x1, x0));
-                    dst[tt * ld] = y;
-                    if (rec_this) reinterpret_cast<float*>(recw + tt * row_bytes)[gc[j]] = y;
+                    const float x0 = xp[tt];
+                    const float y = silu(conv4(w, x3, x2, x1, x0));
+                    ydst[tt * yld] = y;
+                    if (rec_this) reinterpret_cast<float*>(recw + tt * row_bytes)[gc] = y;
                     x3 = x2; x2 = x1; x1 = x0;
                 }
             }
+        } else {
+            // commit only: consume the window loads before arriving
+            ydst[0] = xw0 + xw1 + xw2;
         }
-    } else {
-        // commit only: make sure the window loads have landed before arriving
-#pragma unroll
-        for (int j = 0; j < NCH; ++j)
-            if (gc[j] >= 0) sq[tid + j * BLOCK_THREADS] = xw0[j] + xw1[j] + xw2[j];
     }
     __syncthreads();
-    if (tid == 0)
-        sh_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk)) ? 1 : 0;
+    bool my_last = false;
+    if (tid == 0) my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
     if (nc > 0) {
 #pragma unroll
-        for (int ii = 0; ii < TT / 4; ++ii) {
-            const int tt = wv + 4 * ii;
+        for (int ii = 0; ii < NA; ++ii) {
+            const int tt = wv + 8 * ii;
             if (tt < nc) {
                 const float kq = gate_qk<DK>(sq + tt * DK, sk + tt * DK, A.scale, A.eps, lane);
                 float eg, beta;
@@ -239,77 +212,93 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
             }
         }
         __syncthreads();
-        float* __restrict__ O = A.o + (int64_t)req * nc * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + col;
+        const int cg = lane_colgroup(tid);
+        const bool writer = lane_rowgroup(tid) == 0;
+        float* __restrict__ O = A.o + (int64_t)req * nc * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + cg * CPL;
         const int64_t o_stride = (int64_t)A.h_v * A.d_v;
         for (int tt = 0; tt < nc; ++tt) {
-            float k[R], q[R];
-            load_kq(tt, k, q);
-            const float o = delta_step<R>(s, k, q, sv[tt * BV + col], ssc[tt * 4 + 0], ssc[tt * 4 + 1],
-                                          ssc[tt * 4 + 2]);
-            if (lane_rowgroup(tid) == 0) O[(int64_t)tt * o_stride] = o;
+            float k[R], q[R], v[CPL], o[CPL];
+            lds_rows<R>(sk + tt * DK, tid, k);
+            lds_rows<R>(sq + tt * DK, tid, q);
+            lds_cols<CPL>(sv + tt * BV, tid, v);
+            delta_step<R, CPL>(s, k, q, v, ssc[tt * 4 + 0], ssc[tt * 4 + 1], ssc[tt * 4 + 2], o);
+            if (writer) {
+                float* dst = O + (int64_t)tt * o_stride;
+                if constexpr (CPL == 4) {
+                    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) dst[c] = o[c];
+                }
+            }
             if (LAYOUT == GDN_SPEC_SLOTS)
-                store_state_block<StT, DK>(st_base + ((int64_t)tt * A.h_v + h) * head_elems + colbase, A.d_v,
-                                           stage, s, tid);
+                store_state<StT, DK, CPL>(st_base + ((int64_t)tt * A.h_v + h) * head_elems + colbase, A.d_v, s,
+                                          tid);
         }
     } else if (LAYOUT == GDN_SPEC_SLOTS) {
-        store_state_block<StT, DK>(st_base + (int64_t)h * head_elems + colbase, A.d_v, stage, s, tid);
+        store_state<StT, DK, CPL>(st_base + (int64_t)h * head_elems + colbase, A.d_v, s, tid);
     }
+    if (tid == 0) sh_last = my_last ? 1 : 0;
     __syncthreads();
 
     // ---- conv buffer: [a'+1, a'+2, candidates] or [a', a'+1, a'+2]
-    const bool last = sh_last != 0;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        if (gc[j] < 0) continue;
-        const int lc = tid + j * BLOCK_THREADS;
-        if (lc < 2 * DK && !last) continue;
+    if (gc >= 0 && (lc >= 2 * DK || sh_last)) {
         if (nc > 0) {
-            cbuf[0 * C + gc[j]] = from_f32<ActT>(xw1[j]);
-            cbuf[1 * C + gc[j]] = from_f32<ActT>(xw2[j]);
+            cbuf[0 * C + gc] = from_f32<ActT>(xw1);
+            cbuf[1 * C + gc] = from_f32<ActT>(xw2);
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
-                if (tt < nc) cbuf[(int64_t)(2 + tt) * C + gc[j]] = from_f32<ActT>(xp[j][tt]);
+                if (tt < nc) cbuf[(int64_t)(2 + tt) * C + gc] = from_f32<ActT>(xp[tt]);
         } else {
-            cbuf[0 * C + gc[j]] = from_f32<ActT>(xw0[j]);
-            cbuf[1 * C + gc[j]] = from_f32<ActT>(xw1[j]);
-            cbuf[2 * C + gc[j]] = from_f32<ActT>(xw2[j]);
+            cbuf[0 * C + gc] = from_f32<ActT>(xw0);
+            cbuf[1 * C + gc] = from_f32<ActT>(xw1);
+            cbuf[2 * C + gc] = from_f32<ActT>(xw2);
         }
     }
 
-    // ---- done counter: the last workgroup of the request flips the flag
+    // ---- done counter: the last workgroup of the request flips the flag.
+    // Every workgroup read the header at its start (values consumed), so the
+    // last arrival may rewrite it; relaxed for the reason given at arrive_last.
     __syncthreads();
     if (tid == 0) {
         const uint32_t total = (uint32_t)(A.h_v * nblk);
-        const uint32_t prev = __hip_atomic_fetch_add(&hdr->flag, 256u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev = __hip_atomic_fetch_add(&hdr->flag, 256u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((prev >> 8) + 1u == total) {
             hdr->n_rows[1 - L] = (uint32_t)nc;
             hdr->accepted = (uint32_t)acc;
-            __hip_atomic_store(&hdr->flag, (uint32_t)((1 - L) | (par << 1)), __ATOMIC_RELEASE,
+            __hip_atomic_store(&hdr->flag, (uint32_t)((1 - L) | (par << 1)), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-template <typename ActT, typename StT, int DK>
+template <typename ActT, typename StT, int DK, int CPL>
 static hipError_t launch_verify_t(const VerifyArgs& a, int layout, hipStream_t s) {
-    const int nblk = a.d_v / BV;
+    const int nblk = a.d_v / (32 * CPL);
     const int64_t grid = (int64_t)a.n_req * a.h_v * nblk;
     if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (layout == GDN_SPEC_ONEPAGE)
-        hipLaunchKernelGGL((k_gdn_verify<ActT, StT, DK, GDN_SPEC_ONEPAGE>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((k_gdn_verify<ActT, StT, DK, CPL, GDN_SPEC_ONEPAGE>), dim3((unsigned)grid),
                            dim3(BLOCK_THREADS), 0, s, a);
     else
-        hipLaunchKernelGGL((k_gdn_verify<ActT, StT, DK, GDN_SPEC_SLOTS>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((k_gdn_verify<ActT, StT, DK, CPL, GDN_SPEC_SLOTS>), dim3((unsigned)grid),
                            dim3(BLOCK_THREADS), 0, s, a);
     return hipGetLastError();
+}
+
+template <typename ActT, typename StT, int DK>
+static hipError_t launch_verify_shape(const VerifyArgs& a, int layout, hipStream_t s) {
+    if (a.d_v % 128 == 0) return launch_verify_t<ActT, StT, DK, 4>(a, layout, s);
+    return launch_verify_t<ActT, StT, DK, 1>(a, layout, s);
 }
 
 template <typename ActT, typename StT>
 static hipError_t launch_verify_dk(const VerifyArgs& a, int d_k, int layout, hipStream_t s) {
     switch (d_k) {
-        case 32: return launch_verify_t<ActT, StT, 32>(a, layout, s);
-        case 64: return launch_verify_t<ActT, StT, 64>(a, layout, s);
-        case 128: return launch_verify_t<ActT, StT, 128>(a, layout, s);
+        case 32: return launch_verify_shape<ActT, StT, 32>(a, layout, s);
+        case 64: return launch_verify_shape<ActT, StT, 64>(a, layout, s);
+        case 128: return launch_verify_shape<ActT, StT, 128>(a, layout, s);
         default: return hipErrorInvalidValue;
     }
 }
