@@ -188,8 +188,10 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         const int n = (T - c0 < CH) ? (T - c0) : CH;
         // ================================================================ P1
         {
+            // loads are unconditional (row and channel clamped into range) so the
+            // compiler can keep all of them in flight; padded values are zeroed
             const ActT* xq = X + (int64_t)(r0 + c0) * A.x_stride + gq;
-            const ActT* xv = X + (int64_t)(r0 + c0) * A.x_stride + gv;
+            const ActT* xv = X + (int64_t)(r0 + c0) * A.x_stride + (has_v ? gv : gq);
             __bf16* qkh = is_q ? Qh + tid : Kh + (tid - DK);
             __bf16* qkl = is_q ? Ql + tid : Kl + (tid - DK);
             for (int t0 = 0; t0 < CH; t0 += 16) {
@@ -197,8 +199,11 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int t = t0 + i;
-                    xs[i] = t < n ? to_f32(xq[(int64_t)t * A.x_stride]) : 0.0f;
-                    vs[i] = (has_v && t < n) ? to_f32(xv[(int64_t)t * A.x_stride]) : 0.0f;
+                    const int64_t tr = (int64_t)(t < n ? t : n - 1) * A.x_stride;
+                    const float xa = to_f32(xq[tr]);
+                    const float xb = to_f32(xv[tr]);
+                    xs[i] = t < n ? xa : 0.0f;
+                    vs[i] = (has_v && t < n) ? xb : 0.0f;
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -263,14 +268,11 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             // gates and the cumulative decay: wave 0, lane = token
             if (wv == 0) {
                 const int t = lane;
-                float g = 0.0f, beta = 0.0f;
-                if (t < n) {
-                    const int64_t row = (int64_t)(r0 + c0 + t) * A.ab_stride + h;
-                    const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
-                    const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
-                    g = -exp_alog * softplus(av + dtb);
-                    beta = sigmoid(bv);
-                }
+                const int64_t row = (int64_t)(r0 + c0 + (t < n ? t : n - 1)) * A.ab_stride + h;
+                const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
+                const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
+                const float g = t < n ? -exp_alog * softplus(av + dtb) : 0.0f;
+                const float beta = t < n ? sigmoid(bv) : 0.0f;
                 float G = g;
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {

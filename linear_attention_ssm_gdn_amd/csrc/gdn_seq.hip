@@ -104,17 +104,26 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
     // ---- chunk inputs, loaded one chunk ahead
     float xp[TT];
     float pa[NA], pb[NA];
+    // Loads are unconditional (row and channel clamped into range) so all of
+    // them stay in flight together; values past the sequence are zeroed.
+    const int64_t gcl = gc >= 0 ? gc : 0;
     auto prefetch = [&](int t0) {
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-            xp[tt] = (gc >= 0 && t0 + tt < T) ? to_f32(X[(int64_t)(r0 + t0 + tt) * A.x_stride + gc]) : 0.0f;
+        for (int tt = 0; tt < TT; ++tt) {
+            const int t = t0 + tt < T ? t0 + tt : T - 1;
+            const float xv = to_f32(X[(int64_t)(r0 + t) * A.x_stride + gcl]);
+            xp[tt] = (gc >= 0 && t0 + tt < T) ? xv : 0.0f;
+        }
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             const int tt = wv + 8 * i;
             const bool ok = tt < TT && t0 + tt < T;
-            const int64_t row = (int64_t)(r0 + t0 + tt) * A.ab_stride + h;
-            pa[i] = ok ? to_f32(static_cast<const ActT*>(A.a)[row]) : 0.0f;
-            pb[i] = ok ? to_f32(static_cast<const ActT*>(A.b)[row]) : 0.0f;
+            const int t = ok ? t0 + tt : T - 1;
+            const int64_t row = (int64_t)(r0 + t) * A.ab_stride + h;
+            const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
+            const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
+            pa[i] = ok ? av : 0.0f;
+            pb[i] = ok ? bv : 0.0f;
         }
     };
     prefetch(0);

@@ -110,17 +110,32 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     float xp[TT];
     float pa[NA], pb[NA];
     {
+        // unconditional loads (row and channel clamped into range) stay in flight
+        // together; values past the candidates are zeroed
         const ActT* X = static_cast<const ActT*>(A.x);
+        const int64_t gcl = gc >= 0 ? gc : 0;
+        if (nc > 0) {
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-            xp[tt] = (gc >= 0 && tt < nc) ? to_f32(X[((int64_t)req * nc + tt) * A.x_stride + gc]) : 0.0f;
+            for (int tt = 0; tt < TT; ++tt) {
+                const int t = tt < nc ? tt : nc - 1;
+                const float xv = to_f32(X[((int64_t)req * nc + t) * A.x_stride + gcl]);
+                xp[tt] = (gc >= 0 && tt < nc) ? xv : 0.0f;
+            }
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int tt = wv + 8 * i;
-            const bool ok = tt < nc;
-            const int64_t row = ((int64_t)req * nc + tt) * A.ab_stride + h;
-            pa[i] = ok ? to_f32(static_cast<const ActT*>(A.a)[row]) : 0.0f;
-            pb[i] = ok ? to_f32(static_cast<const ActT*>(A.b)[row]) : 0.0f;
+            for (int i = 0; i < NA; ++i) {
+                const int tt = wv + 8 * i;
+                const bool ok = tt < nc;
+                const int64_t row = ((int64_t)req * nc + (ok ? tt : nc - 1)) * A.ab_stride + h;
+                const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
+                const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
+                pa[i] = ok ? av : 0.0f;
+                pb[i] = ok ? bv : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) xp[tt] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NA; ++i) pa[i] = pb[i] = 0.0f;
         }
     }
 
