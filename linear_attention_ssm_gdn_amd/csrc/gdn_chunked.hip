@@ -35,6 +35,7 @@
 namespace gdn {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -62,7 +63,8 @@ constexpr int OFF_PH = OFF_VTL + BVC * LT * 2; // [64][72]
 constexpr int OFF_PL = OFF_PH + CH * LT * 2;
 constexpr int OFF_SC = OFF_PL + CH * LT * 2;   // 8 x [64] fp32 scalars
 constexpr int OFF_KLAST = OFF_SC + 8 * CH * 4; // [128] fp32
-constexpr int LDS_BYTES = OFF_KLAST + DK * 4;
+constexpr int OFF_WV = OFF_KLAST + DK * 4;       // [64][4] fp32 v-channel conv taps
+constexpr int LDS_BYTES = OFF_WV + BVC * 4 * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(CH * LAF * 4 <= SZ_REG && CH * LQK * 2 <= SZ_REG, "region sizes");
 
@@ -117,6 +119,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     __bf16* Wm = reinterpret_cast<__bf16*>(lds + OFF_QL);                  // after P5
     float* sc = reinterpret_cast<float*>(lds + OFF_SC);
     float* klast = reinterpret_cast<float*>(lds + OFF_KLAST);
+    float* wv4 = reinterpret_cast<float*>(lds + OFF_WV);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;  // MFMA row-in-tile / lane group
@@ -164,8 +167,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     const int64_t gq = is_q ? (int64_t)ki * DK + tid : (int64_t)A.h_k * DK + (int64_t)ki * DK + (tid - DK);
     const bool has_v = tid < BVC;
     const int64_t gv = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + tid;
-    float wq[4], wvv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float q3 = 0.0f, q2 = 0.0f, q1 = 0.0f, v3 = 0.0f, v2 = 0.0f, v1 = 0.0f;
+    float wq[4];
+    float q3 = 0.0f, q2 = 0.0f, q1 = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) wq[e] = to_f32(Wc[gq * 4 + e]);
     if (init) {
@@ -173,11 +176,9 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     }
     if (has_v) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wvv[e] = to_f32(Wc[gv * 4 + e]);
-        if (init) {
-            v3 = to_f32(win[0 * C + gv]); v2 = to_f32(win[1 * C + gv]); v1 = to_f32(win[2 * C + gv]);
-        }
+        for (int e = 0; e < 4; ++e) wv4[4 * tid + e] = to_f32(Wc[gv * 4 + e]);
     }
+    __syncthreads();
     const float exp_alog = expf(A.a_log[h]);
     const float dtb = A.dt_bias[h];
     bool my_last = false;
@@ -188,48 +189,80 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         const int n = (T - c0 < CH) ? (T - c0) : CH;
         // ================================================================ P1
         {
-            // loads are unconditional (row and channel clamped into range) so the
-            // compiler can keep all of them in flight; padded values are zeroed
+            // q/k: channel `tid` over the 64 tokens in order (the window slides in
+            // registers).  Loads are unconditional (row clamped into range) so a
+            // batch of 32 stays in flight; padded values are zeroed.
             const ActT* xq = X + (int64_t)(r0 + c0) * A.x_stride + gq;
-            const ActT* xv = X + (int64_t)(r0 + c0) * A.x_stride + (has_v ? gv : gq);
             __bf16* qkh = is_q ? Qh + tid : Kh + (tid - DK);
             __bf16* qkl = is_q ? Ql + tid : Kl + (tid - DK);
-            for (int t0 = 0; t0 < CH; t0 += 16) {
-                float xs[16], vs[16];
+            for (int t0 = 0; t0 < CH; t0 += 32) {
+                float xs[32];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
+                for (int i = 0; i < 32; ++i) {
                     const int t = t0 + i;
-                    const int64_t tr = (int64_t)(t < n ? t : n - 1) * A.x_stride;
-                    const float xa = to_f32(xq[tr]);
-                    const float xb = to_f32(xv[tr]);
+                    const float xa = to_f32(xq[(int64_t)(t < n ? t : n - 1) * A.x_stride]);
                     xs[i] = t < n ? xa : 0.0f;
-                    vs[i] = (has_v && t < n) ? xb : 0.0f;
                 }
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = t0 + i;
-                    float y = 0.0f, yv = 0.0f;
-                    if (t < n) {
-                        y = silu_fast(conv4(wq, q3, q2, q1, xs[i]));
-                        q3 = q2; q2 = q1; q1 = xs[i];
-                        if (has_v) {
-                            yv = silu_fast(conv4(wvv, v3, v2, v1, vs[i]));
-                            v3 = v2; v2 = v1; v1 = vs[i];
+                for (int i = 0; i < 32; i += 2) {
+                    float y[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int t = t0 + i + u;
+                        y[u] = 0.0f;
+                        if (t < n) {
+                            y[u] = silu_fast(conv4(wq, q3, q2, q1, xs[i + u]));
+                            q3 = q2; q2 = q1; q1 = xs[i + u];
                         }
                     }
-                    const __bf16 hi = (__bf16)y;
-                    const __bf16 lo = (__bf16)(y - (float)hi);
-                    qkh[t * LQK] = hi;
-                    qkl[t * LQK] = lo;
+                    const __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1];
+                    const __bf16 l0 = (__bf16)(y[0] - (float)h0), l1 = (__bf16)(y[1] - (float)h1);
+                    const int t = t0 + i;
+                    qkh[t * LQK] = h0; qkh[(t + 1) * LQK] = h1;
+                    qkl[t * LQK] = l0; qkl[(t + 1) * LQK] = l1;
                     if (!is_q) {
-                        KTh[(tid - DK) * LT + t] = hi;
-                        KTl[(tid - DK) * LT + t] = lo;
+                        const bf16x2 ph = {h0, h1}, pl = {l0, l1};
+                        *reinterpret_cast<bf16x2*>(KTh + (tid - DK) * LT + t) = ph;
+                        *reinterpret_cast<bf16x2*>(KTl + (tid - DK) * LT + t) = pl;
                     }
-                    if (has_v) {
-                        const __bf16 vh = (__bf16)yv;
-                        VTh[tid * LT + t] = vh;
-                        VTl[tid * LT + t] = (__bf16)(yv - (float)vh);
+                }
+            }
+            // v: channel (tid & 63), tokens 16 (tid >> 6) .. +15, with the three rows
+            // before them loaded (from x, or the window before the first token)
+            {
+                const int vc = tid & 63, tq = tid >> 6;
+                const int64_t gvc = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + vc;
+                const float* wvc = wv4 + 4 * vc;
+                float hx[3];
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const int t = c0 + 16 * tq - 3 + j;  // sequence-relative row
+                    const int tc = t < 0 ? 0 : (t < T ? t : T - 1);
+                    const float xa = to_f32(X[(int64_t)(r0 + tc) * A.x_stride + gvc]);
+                    const float wa = init ? to_f32(win[(int64_t)(3 + (t < 0 ? t : -1)) * C + gvc]) : 0.0f;
+                    hx[j] = t >= 0 ? xa : wa;
+                }
+                float xs[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = 16 * tq + i;
+                    const float xa = to_f32(X[(int64_t)(r0 + c0 + (t < n ? t : n - 1)) * A.x_stride + gvc]);
+                    xs[i] = t < n ? xa : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    float y[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int t = 16 * tq + i + u;
+                        y[u] = t < n ? silu_fast(conv4(wvc, hx[0], hx[1], hx[2], xs[i + u])) : 0.0f;
+                        hx[0] = hx[1]; hx[1] = hx[2]; hx[2] = xs[i + u];
                     }
+                    const __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1];
+                    const bf16x2 ph = {h0, h1};
+                    const bf16x2 pl = {(__bf16)(y[0] - (float)h0), (__bf16)(y[1] - (float)h1)};
+                    *reinterpret_cast<bf16x2*>(VTh + vc * LT + 16 * tq + i) = ph;
+                    *reinterpret_cast<bf16x2*>(VTl + vc * LT + 16 * tq + i) = pl;
                 }
             }
         }
@@ -548,9 +581,18 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         win[2 * C + gq] = from_f32<ActT>(q1);
     }
     if (has_v) {
-        win[0 * C + gv] = from_f32<ActT>(v3);
-        win[1 * C + gv] = from_f32<ActT>(v2);
-        win[2 * C + gv] = from_f32<ActT>(v1);
+        // rolled v window: the last three rows of (window ++ sequence), read
+        // before any write (this workgroup alone owns these channels)
+        float vw[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int t = T - 3 + j;
+            const float xa = to_f32(X[(int64_t)(r0 + (t < 0 ? 0 : t)) * A.x_stride + gv]);
+            const float wa = init ? to_f32(win[(int64_t)(3 + (t < 0 ? t : -1)) * C + gv]) : 0.0f;
+            vw[j] = t >= 0 ? xa : wa;
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) win[(int64_t)j * C + gv] = from_f32<ActT>(vw[j]);
     }
 }
 
