@@ -1,0 +1,229 @@
+"""CPU tests of the libgdn boundary: the library loads and exports every
+entry point include/gdn.h declares, the ctypes mirror matches the C struct
+layouts, page layouts follow their definition, and host-side validation
+answers with the documented status codes before anything is launched
+(no GPU is touched by any call made here)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+FAKE = 0x10000  # a non-null, 256-aligned address: validation never dereferences it
+
+
+@pytest.fixture(scope="module")
+def L():
+    import linear_attention_ssm_gdn_amd._lib as lib
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.skip("libgdn.so not built")
+    return lib
+
+
+@pytest.fixture(scope="module")
+def so(L):
+    return L.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    src = tmp_path / "h.c"
+    src.write_text('#include "gdn.h"\nint main(void) { return GDN_ABI_VERSION == 1 ? 0 : 1; }\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(tmp_path / "h")], check=True)
+    subprocess.run([str(tmp_path / "h")], check=True)
+
+
+def test_every_declared_symbol_is_exported(so):
+    names = declared_functions()
+    assert set(names) == {"gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout",
+                          "gdn_chunked_workspace_bytes", "gdn_conv_update", "gdn_recurrent_seq",
+                          "gdn_chunked_prefill", "gdn_spec_verify"}
+    for n in names:
+        assert hasattr(so, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "linear_attention_ssm_gdn_amd",
+                                                                       "libgdn.so")],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("gdn_")}
+    assert exported == set(names)
+
+
+def test_struct_layouts_match_c(L, tmp_path):
+    structs = {"gdn_dims": L.GdnDims, "gdn_params": L.GdnParams, "gdn_batch": L.GdnBatch,
+               "gdn_conv_pool": L.GdnConvPool, "gdn_state_pool": L.GdnStatePool,
+               "gdn_spec_layout": L.GdnSpecLayout}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gdn.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append('  printf("gdn_spec_header %zu\\n", sizeof(gdn_spec_header));')
+    lines.append("  return 0; }")
+    (tmp_path / "l.c").write_text("\n".join(lines))
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(tmp_path / "l.c"), "-o",
+                    str(tmp_path / "l")], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(tmp_path / "l")], capture_output=True, text=True,
+                                                          check=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, (cname, f)
+    assert int(got["gdn_spec_header"]) == 256
+
+
+def test_version_and_status_strings(so, L):
+    assert so.gdn_abi_version() == L.ABI_VERSION == 1
+    for code, text in ((0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
+                       (3, b"kernel launch failed"), (99, b"unknown status")):
+        assert so.gdn_status_str(code) == text
+
+
+def _dims(L, **kw):
+    d = dict(h_k=16, h_v=32, d_k=128, d_v=128, conv_w=4, n_spec=7, act_dtype=1, state_dtype=0, scale=1.0,
+             l2_eps=1e-6)
+    d.update(kw)
+    return L.GdnDims(**d)
+
+
+def test_spec_page_layout_definition(so, L):
+    for sd, es in ((0, 4), (1, 2)):
+        d = _dims(L, state_dtype=sd)
+        one, slots = L.GdnSpecLayout(), L.GdnSpecLayout()
+        assert so.gdn_spec_page_layout(ctypes.byref(d), 0, ctypes.byref(one)) == 0
+        assert so.gdn_spec_page_layout(ctypes.byref(d), 1, ctypes.byref(slots)) == 0
+        head = 128 * 128 * es
+        C = 2 * 16 * 128 + 32 * 128
+        assert one.header_off == 0 and one.state_off == 256
+        assert one.record_row_bytes == (C + 2 * 32) * 4
+        assert one.record_off == 256 + 32 * head
+        assert one.page_bytes == ((one.record_off + 2 * 8 * one.record_row_bytes + 255) // 256) * 256
+        assert slots.state_off == 256 and slots.page_bytes == 256 + 8 * 32 * head
+        # the one-page layout is the smaller one (fp32: 2.5 MiB vs 16 MiB per request)
+        assert slots.page_bytes / one.page_bytes > (5.0 if sd == 1 else 6.0)
+    bad = _dims(L, n_spec=16)
+    assert so.gdn_spec_page_layout(ctypes.byref(bad), 0, ctypes.byref(L.GdnSpecLayout())) == 2
+    assert so.gdn_spec_page_layout(ctypes.byref(_dims(L)), 5, ctypes.byref(L.GdnSpecLayout())) == 1
+
+
+def _seq_args(L, d, **over):
+    C = 2 * d.h_k * d.d_k + d.h_v * d.d_v
+    batch = L.GdnBatch(FAKE, FAKE, None, 2, 8, 16)
+    conv = L.GdnConvPool(FAKE, 3 * C, 3, 4, FAKE)
+    state = L.GdnStatePool(FAKE, d.h_v * d.d_k * d.d_v, 4)
+    params = L.GdnParams(FAKE, FAKE, FAKE)
+    a = dict(dims=d, params=params, x=FAKE, x_stride=C, a=FAKE, b=FAKE, ab_stride=d.h_v, batch=batch, conv=conv,
+             state=state, o=FAKE)
+    a.update(over)
+    return a
+
+
+def _call_seq(so, a):
+    return so.gdn_recurrent_seq(ctypes.byref(a["dims"]), ctypes.byref(a["params"]) if a["params"] else None,
+                                a["x"], a["x_stride"], a["a"], a["b"], a["ab_stride"],
+                                ctypes.byref(a["batch"]) if a["batch"] else None, a["conv"], a["state"], a["o"],
+                                None, None)
+
+
+def test_recurrent_seq_validation(so, L):
+    d = _dims(L)
+    C = 2 * 16 * 128 + 32 * 128
+    cases = [
+        (dict(params=None), 1),
+        (dict(batch=None), 1),
+        (dict(x=None), 1),
+        (dict(x_stride=C - 1), 1),
+        (dict(ab_stride=31), 1),
+        (dict(conv=L.GdnConvPool(FAKE, 3 * C, 2, 4, FAKE)), 1),      # fewer than W-1 window rows
+        (dict(conv=L.GdnConvPool(FAKE, 3 * C, 3, 4, None)), 1),      # no sync words
+        (dict(conv=L.GdnConvPool(FAKE, 3 * C - 1, 3, 4, FAKE)), 1),  # page stride too small
+        (dict(state=L.GdnStatePool(FAKE + 4, 32 * 128 * 128, 4)), 1),  # misaligned state base
+        (dict(state=L.GdnStatePool(FAKE, 32 * 128 * 128 - 1, 4)), 1),
+        (dict(dims=_dims(L, h_v=24)), 1),                            # h_v % h_k != 0
+        (dict(dims=_dims(L, l2_eps=-1.0)), 1),
+        (dict(dims=_dims(L, act_dtype=7)), 1),
+        (dict(dims=_dims(L, conv_w=3)), 2),
+        (dict(dims=_dims(L, d_k=96)), 2),
+        (dict(dims=_dims(L, d_v=100)), 2),
+    ]
+    for over, want in cases:
+        assert _call_seq(so, _seq_args(L, d, **over)) == want, over
+    # an empty batch is a no-op that returns OK without launching
+    assert _call_seq(so, _seq_args(L, d, batch=L.GdnBatch(None, None, None, 0, 0, 0))) == 0
+
+
+def test_chunked_validation(so, L):
+    d = _dims(L)
+    a = _seq_args(L, d)
+
+    def call(chunk=64, ws_bytes=0, dims=d):
+        return so.gdn_chunked_prefill(ctypes.byref(dims), ctypes.byref(a["params"]), a["x"], a["x_stride"], a["a"],
+                                      a["b"], a["ab_stride"], ctypes.byref(a["batch"]), a["conv"], a["state"],
+                                      a["o"], chunk, None, ws_bytes, None, None)
+    assert call(chunk=0) == 1
+    assert call(chunk=32) == 2
+    assert call(dims=_dims(L, d_k=64)) == 2
+    out = ctypes.c_size_t(123)
+    assert so.gdn_chunked_workspace_bytes(ctypes.byref(d), 4, 32768, 64, ctypes.byref(out)) == 0
+    assert out.value == 0
+
+
+def test_verify_validation(so, L):
+    d = _dims(L)
+    C = 2 * 16 * 128 + 32 * 128
+    lay = L.GdnSpecLayout()
+    assert so.gdn_spec_page_layout(ctypes.byref(d), 0, ctypes.byref(lay)) == 0
+    params = L.GdnParams(FAKE, FAKE, FAKE)
+
+    def call(layout=0, n_req=2, n_cand=8, pages=FAKE, page_bytes=None, conv_rows=10, x=FAKE, dims=d):
+        conv = L.GdnConvPool(FAKE, conv_rows * C, conv_rows, 4, FAKE)
+        return so.gdn_spec_verify(ctypes.byref(dims), ctypes.byref(params), layout, x, C, FAKE, FAKE, 32, n_req,
+                                  n_cand, FAKE, FAKE, FAKE, pages, page_bytes or lay.page_bytes, 4, conv, FAKE, None,
+                                  None)
+    assert call(n_cand=9) == 1                       # more than n_spec + 1 candidates
+    assert call(conv_rows=9) == 1                    # conv buffer narrower than W-1+n_spec rows
+    assert call(page_bytes=lay.page_bytes - 256) == 1
+    assert call(pages=FAKE + 16) == 1                # pages not 256-aligned
+    assert call(layout=3) == 1
+    assert call(x=None) == 1
+    assert call(n_req=0) == 0                        # nothing to do
+
+
+def test_conv_update_validation(so, L):
+    d = _dims(L)
+    C = 2 * 16 * 128 + 32 * 128
+    batch = L.GdnBatch(FAKE, FAKE, None, 2, 8, 16)
+
+    def call(act=1, y_dtype=0, y_stride=C, rows=3):
+        conv = L.GdnConvPool(FAKE, rows * C, rows, 4, None)
+        return so.gdn_conv_update(ctypes.byref(d), FAKE, FAKE, C, ctypes.byref(batch), conv, act, FAKE, y_dtype,
+                                  y_stride, None, None)
+    assert call(act=2) == 1
+    assert call(y_dtype=5) == 1
+    assert call(y_stride=C - 8) == 1
+    assert call(rows=2) == 1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = textwrap.dedent(f"""
+        import sys; sys.path.insert(0, {ROOT!r})
+        import linear_attention_ssm_gdn_amd._lib as L
+        L.LIB_PATH = {str(tmp_path / 'absent.so')!r}
+        try:
+            L.load()
+        except ImportError as e:
+            print('raised', e)
+            sys.exit(0)
+        sys.exit(1)
+    """)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "not built" in r.stdout
