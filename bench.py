@@ -270,6 +270,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="decode,short_prefill,long_prefill,spec_verify")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="first run a plain 1 GiB device copy (the byte-counter calibration kernel)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the GDN core shards by head or request with no exchange, "
@@ -280,6 +282,14 @@ def main():
     g.load()
     only = set(args.only.split(","))
     result = {"metric": METRIC}
+    if args.copy_calib:
+        src = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 x {src.numel() * 4} bytes read and written")
+        del src, dst
     other = {}
 
     # ---- headline: decode
