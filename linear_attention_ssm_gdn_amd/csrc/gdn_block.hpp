@@ -28,13 +28,16 @@ template <> struct RowVec<float, 1> {
     __device__ static void load(const float* p, float (&v)[1]) { v[0] = *p; }
     __device__ static void store(float* p, const float (&v)[1]) { *p = v[0]; }
 };
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 template <> struct RowVec<float, 4> {
     __device__ static void load(const float* p, float (&v)[4]) {
-        const float4 t = *reinterpret_cast<const float4*>(p);
-        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+        const f32x4v t = *reinterpret_cast<const f32x4v*>(p);
+        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
     }
     __device__ static void store(float* p, const float (&v)[4]) {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        const f32x4v t = {v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4v*>(p) = t;
     }
 };
 template <> struct RowVec<bf16_t, 1> {
@@ -43,14 +46,14 @@ template <> struct RowVec<bf16_t, 1> {
 };
 template <> struct RowVec<bf16_t, 4> {
     __device__ static void load(const bf16_t* p, float (&v)[4]) {
-        const uint2 t = *reinterpret_cast<const uint2*>(p);
-        v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
-        v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+        const u32x2v t = *reinterpret_cast<const u32x2v*>(p);
+        v[0] = __uint_as_float(t[0] << 16); v[1] = __uint_as_float(t[0] & 0xffff0000u);
+        v[2] = __uint_as_float(t[1] << 16); v[3] = __uint_as_float(t[1] & 0xffff0000u);
     }
     __device__ static void store(bf16_t* p, const float (&v)[4]) {
-        const uint32_t a = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        const uint32_t b = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
+        const u32x2v t = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                          (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+        *reinterpret_cast<u32x2v*>(p) = t;
     }
 };
 
@@ -115,37 +118,39 @@ __device__ __forceinline__ void lds_cols(const float* row, int tid, float (&out)
     }
 }
 
-// Gating of one token by one wave (part (b)): L2-normalise the post-conv q
-// and k rows of the key head in place (q also takes the output scale) and
-// return k-hat . (scale q-hat).  Reduction order is fixed: each lane sums its
-// elements lane, lane+64, ... with fused multiply-adds, then a 64-lane
-// butterfly.
+// Gating of one token by the 16 lanes of a DPP row (part (b)): L2-normalise
+// the post-conv q and k rows of the key head in place (q also takes the output
+// scale) and return k-hat . (scale q-hat).  Lane l16 holds elements
+// l16*E .. l16*E+E-1 (E = d_k/16); each lane sums its elements with fused
+// multiply-adds in order, then reduce16 combines the 16 partial sums.
 template <int DK>
-__device__ __forceinline__ float gate_qk(float* qrow, float* krow, float scale, float eps, int lane) {
-    constexpr int J = (DK + 63) / 64;
-    float qv[J], kv[J];
+__device__ __forceinline__ float gate_qk(float* qrow, float* krow, float scale, float eps, int l16) {
+    constexpr int E = DK / 16;
+    float qv[E], kv[E];
+    lds_rows<E>(qrow + 0, l16, qv);
+    lds_rows<E>(krow + 0, l16, kv);
     float sq = 0.0f, sk = 0.0f;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int e = lane + 64 * j;
-        qv[j] = (e < DK) ? qrow[e] : 0.0f;
-        kv[j] = (e < DK) ? krow[e] : 0.0f;
-        sq = fmaf(qv[j], qv[j], sq);
-        sk = fmaf(kv[j], kv[j], sk);
+    for (int e = 0; e < E; ++e) {
+        sq = fmaf(qv[e], qv[e], sq);
+        sk = fmaf(kv[e], kv[e], sk);
     }
-    sq = reduce64(sq);
-    sk = reduce64(sk);
+    sq = reduce16(sq);
+    sk = reduce16(sk);
     const float rq = scale / sqrtf(sq + eps);
     const float rk = 1.0f / sqrtf(sk + eps);
     float kq = 0.0f;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int e = lane + 64 * j;
-        const float qn = qv[j] * rq, kn = kv[j] * rk;
-        if (e < DK) { qrow[e] = qn; krow[e] = kn; }
-        kq = fmaf(kn, qn, kq);
+    for (int e = 0; e < E; ++e) {
+        qv[e] *= rq;
+        kv[e] *= rk;
+        kq = fmaf(kv[e], qv[e], kq);
     }
-    return reduce64(kq);
+    float* qd = qrow + l16 * E;
+    float* kd = krow + l16 * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) { qd[e] = qv[e]; kd[e] = kv[e]; }
+    return reduce16(kq);
 }
 
 // Decay factor e^g and beta of one (token, value head) (part (b)).

@@ -3,8 +3,9 @@
 //
 // Grid: one workgroup per (sequence, value head h, block of 32*CPL value
 // columns).  The state block stays in VGPRs for the whole sequence; it is
-// loaded first thing, straight into the lane layout of gdn_block.hpp, so its
-// bytes are in flight while the conv inputs arrive.  Tokens are processed in
+// loaded straight into the lane layout of gdn_block.hpp right after the small
+// conv inputs, so its bytes are in flight while the first chunk's conv and
+// gating run.  Tokens are processed in
 // chunks of TT:
 //   A1  conv + SiLU of the chunk for the key head's q and k channels and the
 //       block's v channels, one channel per thread, the window in registers;
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
     constexpr int R = DK / 16;
     constexpr int BV = 32 * CPL;
     constexpr int NLC = 2 * DK + BV;  // local conv channels: q, k (key head), v (block)
-    constexpr int NA = (TT + 7) / 8;  // gate inputs per wave and chunk
+    static_assert(TT <= 32, "one 16-lane row per token of a chunk");
     static_assert(NLC <= BLOCK_THREADS, "one conv channel per thread");
     __shared__ __attribute__((aligned(16))) float sq[TT * DK];   // scale * q-hat
     __shared__ __attribute__((aligned(16))) float sk[TT * DK];   // k-hat
@@ -64,19 +65,6 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
     if (T == 0) return;
     const bool init = A.has_init ? (A.has_init[seq] != 0) : true;
 
-    // ---- state block into registers (issued first)
-    StT* __restrict__ Sg = static_cast<StT*>(A.state) + (int64_t)page * A.state_page_stride +
-                           (int64_t)h * DK * A.d_v + colbase;
-    float s[CPL][R];
-    if (init) {
-        load_state<StT, DK, CPL>(Sg, A.d_v, s, tid);
-    } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-#pragma unroll
-            for (int m = 0; m < R; ++m) s[c][m] = 0.0f;
-    }
-
     // ---- this thread's conv channel
     const ActT* __restrict__ X = static_cast<const ActT*>(A.x);
     ActT* __restrict__ win = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
@@ -103,7 +91,8 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
 
     // ---- chunk inputs, loaded one chunk ahead
     float xp[TT];
-    float pa[NA], pb[NA];
+    float pa = 0.0f, pb = 0.0f;   // gate inputs of this row's token (tt = 4 wv + lane/16)
+    const int gtok = (wv << 2) + (lane >> 4);
     // Loads are unconditional (row and channel clamped into range) so all of
     // them stay in flight together; values past the sequence are zeroed.
     const int64_t gcl = gc >= 0 ? gc : 0;
@@ -114,19 +103,31 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
             const float xv = to_f32(X[(int64_t)(r0 + t) * A.x_stride + gcl]);
             xp[tt] = (gc >= 0 && t0 + tt < T) ? xv : 0.0f;
         }
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int tt = wv + 8 * i;
-            const bool ok = tt < TT && t0 + tt < T;
-            const int t = ok ? t0 + tt : T - 1;
-            const int64_t row = (int64_t)(r0 + t) * A.ab_stride + h;
-            const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
-            const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
-            pa[i] = ok ? av : 0.0f;
-            pb[i] = ok ? bv : 0.0f;
-        }
+        const bool ok = gtok < TT && t0 + gtok < T;
+        const int t = ok ? t0 + gtok : T - 1;
+        const int64_t row = (int64_t)(r0 + t) * A.ab_stride + h;
+        const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
+        const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
+        pa = ok ? av : 0.0f;
+        pb = ok ? bv : 0.0f;
     };
     prefetch(0);
+
+    // ---- state block into registers.  Issued after the small loads above:
+    // loads complete in order, so the conv and gating of the first chunk only
+    // wait for x, the window and the taps while the state is still in flight.
+    StT* __restrict__ Sg = static_cast<StT*>(A.state) + (int64_t)page * A.state_page_stride +
+                           (int64_t)h * DK * A.d_v + colbase;
+    float s[CPL][R];
+    if (init) {
+        load_state<StT, DK, CPL>(Sg, A.d_v, s, tid);
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int m = 0; m < R; ++m) s[c][m] = 0.0f;
+    }
+
 
     const int cg = lane_colgroup(tid);
     const bool writer = lane_rowgroup(tid) == 0;
@@ -152,19 +153,15 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
         __syncthreads();
         if (t0 == 0 && tid == 0)  // every window read of this workgroup has been consumed
             my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
-        // A2: gating, one wave per token
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int tt = wv + 8 * i;
-            if (tt < nt) {
-                const float kq = gate_qk<DK>(sq + tt * DK, sk + tt * DK, A.scale, A.eps, lane);
-                float eg, beta;
-                gate_scalars(pa[i], pb[i], exp_alog, dtb, eg, beta);
-                if (lane == 0) {
-                    ssc[tt * 4 + 0] = eg;
-                    ssc[tt * 4 + 1] = beta;
-                    ssc[tt * 4 + 2] = kq;
-                }
+        // A2: gating, one 16-lane row per token
+        if (gtok < nt) {
+            const float kq = gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
+            float eg, beta;
+            gate_scalars(pa, pb, exp_alog, dtb, eg, beta);
+            if ((lane & 15) == 0) {
+                ssc[gtok * 4 + 0] = eg;
+                ssc[gtok * 4 + 1] = beta;
+                ssc[gtok * 4 + 2] = kq;
             }
         }
         __syncthreads();

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     constexpr int R = DK / 16;
     constexpr int BV = 32 * CPL;
     constexpr int NLC = 2 * DK + BV;
-    constexpr int NA = (TT + 7) / 8;
+    static_assert(TT <= 32, "one 16-lane row per token of a chunk");
     static_assert(NLC <= BLOCK_THREADS, "one conv channel per thread");
     __shared__ __attribute__((aligned(16))) float sq[TT * DK];
     __shared__ __attribute__((aligned(16))) float sk[TT * DK];
@@ -82,8 +82,6 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     StT* __restrict__ Sload = (LAYOUT == GDN_SPEC_ONEPAGE)
                                   ? st_base + (int64_t)h * head_elems + colbase
                                   : st_base + ((int64_t)acc * A.h_v + h) * head_elems + colbase;
-    float s[CPL][R];
-    load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
 
     // ---- this thread's conv channel: weights, window rows acc..acc+2 of the conv buffer
     ActT* __restrict__ cbuf = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
@@ -108,7 +106,8 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
 
     // ---- candidate inputs (loaded early; consumed after the replay)
     float xp[TT];
-    float pa[NA], pb[NA];
+    float pa = 0.0f, pb = 0.0f;   // gate inputs of this row's token (tt = 4 wv + lane/16)
+    const int gtok = (wv << 2) + (lane >> 4);
     {
         // unconditional loads (row and channel clamped into range) stay in flight
         // together; values past the candidates are zeroed
@@ -121,23 +120,24 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
                 const float xv = to_f32(X[((int64_t)req * nc + t) * A.x_stride + gcl]);
                 xp[tt] = (gc >= 0 && tt < nc) ? xv : 0.0f;
             }
-#pragma unroll
-            for (int i = 0; i < NA; ++i) {
-                const int tt = wv + 8 * i;
-                const bool ok = tt < nc;
-                const int64_t row = ((int64_t)req * nc + (ok ? tt : nc - 1)) * A.ab_stride + h;
+            {
+                const bool ok = gtok < nc;
+                const int64_t row = ((int64_t)req * nc + (ok ? gtok : nc - 1)) * A.ab_stride + h;
                 const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
                 const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
-                pa[i] = ok ? av : 0.0f;
-                pb[i] = ok ? bv : 0.0f;
+                pa = ok ? av : 0.0f;
+                pb = ok ? bv : 0.0f;
             }
         } else {
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) xp[tt] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < NA; ++i) pa[i] = pb[i] = 0.0f;
         }
     }
+
+    // the state last: loads complete in order, so the candidates' conv inputs
+    // above are usable while the state is still in flight
+    float s[CPL][R];
+    load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
 
     const int64_t row_bytes = A.record_row_bytes;
     const int64_t rows_per_slot = A.n_spec + 1;
@@ -150,18 +150,14 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
                 for (int i = 0; i < n_replay; ++i)
                     ydst[i * yld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc];
             __syncthreads();
-#pragma unroll
-            for (int ii = 0; ii < NA; ++ii) {
-                const int tt = wv + 8 * ii;
-                if (tt < n_replay) {
-                    const float* rrow = reinterpret_cast<const float*>(rec + tt * row_bytes);
-                    (void)gate_qk<DK>(sq + tt * DK, sk + tt * DK, A.scale, A.eps, lane);
-                    float eg, beta;
-                    gate_scalars(rrow[C + h], rrow[C + A.h_v + h], exp_alog, dtb, eg, beta);
-                    if (lane == 0) {
-                        ssc[tt * 4 + 0] = eg;
-                        ssc[tt * 4 + 1] = beta;
-                    }
+            if (gtok < n_replay) {
+                const float* rrow = reinterpret_cast<const float*>(rec + gtok * row_bytes);
+                (void)gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
+                float eg, beta;
+                gate_scalars(rrow[C + h], rrow[C + A.h_v + h], exp_alog, dtb, eg, beta);
+                if ((lane & 15) == 0) {
+                    ssc[gtok * 4 + 0] = eg;
+                    ssc[gtok * 4 + 1] = beta;
                 }
             }
             __syncthreads();
@@ -207,22 +203,18 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     bool my_last = false;
     if (tid == 0) my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
     if (nc > 0) {
-#pragma unroll
-        for (int ii = 0; ii < NA; ++ii) {
-            const int tt = wv + 8 * ii;
-            if (tt < nc) {
-                const float kq = gate_qk<DK>(sq + tt * DK, sk + tt * DK, A.scale, A.eps, lane);
-                float eg, beta;
-                gate_scalars(pa[ii], pb[ii], exp_alog, dtb, eg, beta);
-                if (lane == 0) {
-                    ssc[tt * 4 + 0] = eg;
-                    ssc[tt * 4 + 1] = beta;
-                    ssc[tt * 4 + 2] = kq;
-                    if (LAYOUT == GDN_SPEC_ONEPAGE && blk == 0) {
-                        float* rrow = reinterpret_cast<float*>(recw + tt * row_bytes);
-                        rrow[C + h] = pa[ii];
-                        rrow[C + A.h_v + h] = pb[ii];
-                    }
+        if (gtok < nc) {
+            const float kq = gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
+            float eg, beta;
+            gate_scalars(pa, pb, exp_alog, dtb, eg, beta);
+            if ((lane & 15) == 0) {
+                ssc[gtok * 4 + 0] = eg;
+                ssc[gtok * 4 + 1] = beta;
+                ssc[gtok * 4 + 2] = kq;
+                if (LAYOUT == GDN_SPEC_ONEPAGE && blk == 0) {
+                    float* rrow = reinterpret_cast<float*>(recw + gtok * row_bytes);
+                    rrow[C + h] = pa;
+                    rrow[C + A.h_v + h] = pb;
                 }
             }
         }
