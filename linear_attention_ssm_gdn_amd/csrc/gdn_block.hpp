@@ -87,6 +87,115 @@ __device__ __forceinline__ void store_state(StT* __restrict__ blk, int64_t ld, c
     }
 }
 
+// ------------------------------------------------------ LDS state staging
+// A state block can be fetched into LDS with gfx950's direct global->LDS
+// loads, which take no VGPRs while in flight: a workgroup holds one block
+// in registers and the next one in LDS at the same time.
+//
+// Each load instruction of a wave covers one contiguous run of the block
+// (fp32: 1 KiB = two rows; bf16: 256 B = one row): HBM serves such runs
+// markedly faster than the register layout's 16-row x 64-byte footprint.  The
+// lane that lands a piece in LDS is therefore not the lane that computes on
+// it, so after every wave's loads have completed a workgroup barrier must
+// precede reading, and another must separate reading from the next fetch.
+//
+// Where a piece lands: the hardware puts lane l of a wave's load at
+// wave_base + l * stride (stride 16 for 16-byte loads, 4 for 4-byte ones).
+// Which piece a lane loads is ours to choose: within a row the piece index is
+// XORed with a function of the row's row group, so that the 16 lanes of a DPP
+// row -- 16 row groups, one piece index -- read 16 different LDS banks.
+typedef __attribute__((address_space(1))) void gmem_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One activation element per lane into LDS.  For 1-, 2- and 4-byte loads
+// the hardware places lane l's data at wave_base + 4 l, zero-extended to a
+// dword (12- and 16-byte loads use a 16-byte lane stride); LDS_ELEM_SLOT is
+// that stride.  A 2-byte element reads back from the low half of its slot.
+constexpr int LDS_ELEM_SLOT = 4;
+__device__ __forceinline__ void load_lds_elem(const float* g, unsigned char* wave_base) {
+    __builtin_amdgcn_global_load_lds((gmem_void*)g, (lds_void*)wave_base, 4, 0, 0);
+}
+__device__ __forceinline__ void load_lds_elem(const bf16_t* g, unsigned char* wave_base) {
+    __builtin_amdgcn_global_load_lds((gmem_void*)g, (lds_void*)wave_base, 2, 0, 0);
+}
+
+template <typename StT, int DK, int CPL> struct StateStage;
+
+// fp32, 4 columns (a 128-column block): a row is 32 pieces of 16 bytes.
+// Load instruction m of wave w covers rows 2(wR+m) and 2(wR+m)+1; lane l
+// takes row 2(wR+m) + l/32, piece (l mod 32) ^ rowgroup(row), and lands at
+// m * 8 KiB + w * 1 KiB + 16 l.
+template <int DK> struct StateStage<float, DK, 4> {
+    static constexpr int R = DK / 16;
+    static constexpr int BYTES = R * BLOCK_THREADS * 16;
+    __device__ static void fetch(const float* blk, int64_t ld, unsigned char* stage, int tid) {
+        const int w = tid >> 6, l = tid & 63;
+        unsigned char* wbase = stage + w * 1024;
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            const int r = 2 * (w * R + m) + (l >> 5);
+            const int piece = (l & 31) ^ ((r / R) & 15);
+            __builtin_amdgcn_global_load_lds((gmem_void*)(blk + (int64_t)r * ld + piece * 4),
+                                             (lds_void*)(wbase + m * BLOCK_THREADS * 16), 16, 0, 0);
+        }
+    }
+    // This lane's rows rg*R .. rg*R+R-1, piece cg (columns 4cg .. 4cg+3).
+    __device__ static void read(const unsigned char* stage, int tid, float (&s)[4][R]) {
+        const int rg = lane_rowgroup(tid), cg = lane_colgroup(tid);
+#pragma unroll
+        for (int mm = 0; mm < R; ++mm) {
+            const int r = rg * R + mm;
+            const int w = (r >> 1) / R, m = (r >> 1) % R;
+            const int l = ((r & 1) << 5) | (cg ^ rg);
+            const f32x4v t = *reinterpret_cast<const f32x4v*>(stage + m * BLOCK_THREADS * 16 + w * 1024 + l * 16);
+            s[0][mm] = t[0]; s[1][mm] = t[1]; s[2][mm] = t[2]; s[3][mm] = t[3];
+        }
+    }
+};
+
+// bf16, 4 columns: a row is 64 pieces of 4 bytes (two columns each).  Load
+// instruction m of wave w covers row 2wR + m; lane l takes piece
+// l ^ 2 rowgroup(row) and lands at m * 2 KiB + w * 256 B + 4 l.  A lane's
+// four columns 4cg .. 4cg+3 are pieces 2cg and 2cg+1, which stay adjacent.
+template <int DK> struct StateStage<bf16_t, DK, 4> {
+    static constexpr int R = DK / 16;
+    static constexpr int BYTES = 2 * R * BLOCK_THREADS * 4;
+    __device__ static void fetch(const bf16_t* blk, int64_t ld, unsigned char* stage, int tid) {
+        const int w = tid >> 6, l = tid & 63;
+        unsigned char* wbase = stage + w * 256;
+#pragma unroll
+        for (int m = 0; m < 2 * R; ++m) {
+            const int r = 2 * R * w + m;
+            const int piece = l ^ (2 * ((r / R) & 15));
+            __builtin_amdgcn_global_load_lds((gmem_void*)(blk + (int64_t)r * ld + 2 * piece),
+                                             (lds_void*)(wbase + m * BLOCK_THREADS * 4), 4, 0, 0);
+        }
+    }
+    __device__ static void read(const unsigned char* stage, int tid, float (&s)[4][R]) {
+        const int rg = lane_rowgroup(tid), cg = lane_colgroup(tid);
+#pragma unroll
+        for (int mm = 0; mm < R; ++mm) {
+            const int r = rg * R + mm;
+            const int w = r / (2 * R), m = r % (2 * R);
+            const int l = (2 * cg) ^ (2 * rg);
+            const u32x2v t = *reinterpret_cast<const u32x2v*>(stage + m * BLOCK_THREADS * 4 + w * 256 + l * 4);
+            s[0][mm] = __uint_as_float(t[0] << 16); s[1][mm] = __uint_as_float(t[0] & 0xffff0000u);
+            s[2][mm] = __uint_as_float(t[1] << 16); s[3][mm] = __uint_as_float(t[1] & 0xffff0000u);
+        }
+    }
+};
+
+// Wait for every vector-memory operation of this wave, direct global->LDS
+// loads included.  The compiler does not reliably order reads of LDS
+// written by such loads when the loads were issued in an earlier loop
+// iteration, so code that stages through LDS waits explicitly.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until this wave's LDS reads have returned, so a following fetch may
+// overwrite the slots they read.  The memory clobber keeps the compiler from
+// moving those reads past the wait.
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // This lane's R rows of a d_k-long LDS row.
 template <int R>
 __device__ __forceinline__ void lds_rows(const float* row, int tid, float (&out)[R]) {

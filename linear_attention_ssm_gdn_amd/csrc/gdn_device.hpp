@@ -151,6 +151,68 @@ __device__ __forceinline__ bool arrive_last(uint32_t* word, uint32_t group) {
     return false;
 }
 
+// Split form of the same arrival for callers that want the atomic's result
+// late: arrive() issues it, arrived_last() (same thread, later) decides and
+// resets.  Reading the result is a wait on the vector-memory counter, which
+// completes in order, so reading it early would also wait for every load
+// issued before the atomic.
+__device__ __forceinline__ uint32_t arrive(uint32_t* word) {
+    return __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool arrived_last(uint32_t* word, uint32_t prev, uint32_t group) {
+    if (prev + 1u == group) {
+        __hip_atomic_store(word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    }
+    return false;
+}
+
+// ------------------------------------------------- ordering-light helpers
+// Workgroup barrier that orders LDS only: wait for this wave's LDS
+// accesses, then s_barrier.  __syncthreads() (and a workgroup fence, even one
+// restricted to LDS) also waits for outstanding vector-memory operations --
+// global stores, and direct global->LDS loads, which count as LDS writes --
+// and with an in-order counter that means every load in flight, including a
+// prefetch of the next block.  Use where waves exchange data through plain
+// LDS reads and writes alone.  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Workgroup-uniform loads through the scalar unit.  The compiler only picks
+// scalar loads when it can prove nothing earlier in the kernel stored to the
+// address; these are read-only kernel inputs, but a loop that also stores
+// defeats that proof and the fallback (a vector load, then a wait) stalls on
+// every vector load in flight.  `p` must be uniform and 4-byte aligned.
+__device__ __forceinline__ uint32_t sload_u32(const void* p) {
+    uint32_t v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+// Several such loads in flight together, one wait: a[i] = *p[i].
+template <int N>
+__device__ __forceinline__ void sload_u32_n(const void* const (&p)[N], uint32_t (&a)[N]);
+template <>
+__device__ __forceinline__ void sload_u32_n<6>(const void* const (&p)[6], uint32_t (&a)[6]) {
+    asm volatile(
+        "s_load_dword %0, %6, 0x0\n\t"
+        "s_load_dword %1, %7, 0x0\n\t"
+        "s_load_dword %2, %8, 0x0\n\t"
+        "s_load_dword %3, %9, 0x0\n\t"
+        "s_load_dword %4, %10, 0x0\n\t"
+        "s_load_dword %5, %11, 0x0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(a[0]), "=&s"(a[1]), "=&s"(a[2]), "=&s"(a[3]), "=&s"(a[4]), "=&s"(a[5])
+        : "s"(p[0]), "s"(p[1]), "s"(p[2]), "s"(p[3]), "s"(p[4]), "s"(p[5])
+        : "memory");
+}
+__device__ __forceinline__ int32_t sload_i32(const int32_t* p) { return (int32_t)sload_u32(p); }
+__device__ __forceinline__ float sload_f32(const float* p) { return __uint_as_float(sload_u32(p)); }
+// One byte: the aligned dword that holds it (same page, so always mapped).
+__device__ __forceinline__ uint32_t sload_u8(const uint8_t* p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return (sload_u32(reinterpret_cast<const void*>(a & ~(uintptr_t)3)) >> ((a & 3u) * 8u)) & 0xffu;
+}
+
 __device__ __forceinline__ void set_err(int32_t* err, uint32_t bit) {
     if (err) __hip_atomic_fetch_or(err, (int32_t)bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

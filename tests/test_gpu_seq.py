@@ -210,3 +210,54 @@ def test_fused_conv_window_equals_conv_update():
     _, conv_fused, _ = run_seq(wl, inp)
     _, conv_alone = _conv_call(wl, inp, True, "f32")
     assert torch.equal(conv_fused.buf, conv_alone.buf)
+
+
+def _check_pages(ora, wl, inp, pages, has, n_pages, s_tol=TOL):
+    o, conv, state = run_seq(wl, inp, pages=pages, n_pages=n_pages, has_init=has)
+    o_ref, win_ref, S_ref = oracle_seq(ora, wl, inp, has_init=has)
+    cu = inp["cu_seqlens"]
+    oh, Sh, Ch = host(o), host(state.buf), host(conv.buf)
+    used = set()
+    for s, p in enumerate(pages):
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        if p < 0:
+            assert np.isnan(oh[rows]).all()
+            continue
+        used.add(p)
+        assert max_slice_rel_o(oh[rows], o_ref[rows], [0, cu[s + 1] - cu[s]]) <= TOL
+        if cu[s + 1] == cu[s]:
+            continue  # an empty sequence leaves its page as it was
+        assert max_slice_rel_S(Sh[p:p + 1], S_ref[s:s + 1]) <= s_tol
+        np.testing.assert_array_equal(Ch[p], win_ref[s])
+    for p in range(n_pages):
+        if p not in used:
+            assert float(state.buf[p].abs().sum()) == 0.0
+    assert int(conv.sync.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
+def test_decode_stream_many_items(ora, state_dtype):
+    """Sequences of at most 4 tokens take the streaming kernel.  With 40
+    sequences x 32 heads there are more items than resident workgroups, so
+    each workgroup walks several items with the next one's state prefetched;
+    lengths 0..4, fresh and continuing states and padding rows are mixed so
+    skipped items fall between fetched ones."""
+    rng = np.random.default_rng(21)
+    n = 40
+    lens = tuple(int(x) for x in rng.integers(0, 5, size=n))
+    wl = wk.DECODE.replace(seqlens=lens, state_dtype=state_dtype, seed=21)
+    inp = wk.make_sequence_inputs(wl)
+    has = (rng.random(n) < 0.75).astype(np.uint8)
+    pages = list(range(n))
+    pages[5] = pages[17] = pages[18] = -1
+    _check_pages(ora, wl, inp, pages, has, n, s_tol=TOL if state_dtype == wk.F32 else 2.0 ** -8)
+
+
+def test_decode_stream_d64_two_blocks(ora):
+    """d_k = 64 and d_v = 256: two 128-column items per head share the key
+    head's conv window (arrival count 2 r)."""
+    wl = wk.Workload("d64v256", h_k=4, h_v=8, d_k=64, d_v=256, conv_w=4, act_dtype=wk.BF16,
+                     state_dtype=wk.F32, seqlens=(1, 2, 3, 4, 1, 0, 2) * 12, seed=22, scale=64 ** -0.5)
+    inp = wk.make_sequence_inputs(wl)
+    n = len(wl.seqlens)
+    _check_pages(ora, wl, inp, list(range(n)), None, n)
