@@ -156,9 +156,17 @@ __device__ __forceinline__ bool arrive_last(uint32_t* word, uint32_t group) {
 // resets.  Reading the result is a wait on the vector-memory counter, which
 // completes in order, so reading it early would also wait for every load
 // issued before the atomic.
-__device__ __forceinline__ uint32_t arrive(uint32_t* word) {
-    return __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Relaxed device-scope fetch-add by one lane whose result is read later.  A
+// zero offset passed through an empty asm hides that the address is uniform:
+// for a uniform address the compiler rewrites a one-lane atomic into a
+// wave-aggregated one plus a prefix sum, and that rewrite reads the result
+// right after issuing it.
+__device__ __forceinline__ uint32_t fetch_add_late(uint32_t* word, uint32_t v) {
+    uint32_t zero = 0;
+    asm volatile("" : "+v"(zero));
+    return __hip_atomic_fetch_add(word + zero, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t arrive(uint32_t* word) { return fetch_add_late(word, 1u); }
 __device__ __forceinline__ bool arrived_last(uint32_t* word, uint32_t prev, uint32_t group) {
     if (prev + 1u == group) {
         __hip_atomic_store(word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -76,6 +76,13 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     const int n_replay = (LAYOUT == GDN_SPEC_ONEPAGE && nr > 0) ? acc + 1 : 0;
     const int nc = A.n_cand;
 
+    // ---- done counter: the last workgroup of the request to get here flips the
+    // flag at the end.  The counter stands for "this workgroup has read the
+    // header", which is true now, so it is counted now; its result is read
+    // once the state has arrived (issued before it, so already back).
+    uint32_t done_before = 0;
+    if (tid == 0) done_before = fetch_add_late(&hdr->flag, 256u);
+
     // ---- starting state: the checkpoint, or slot[acc]
     const int64_t head_elems = (int64_t)DK * A.d_v;
     StT* __restrict__ st_base = reinterpret_cast<StT*>(pg + A.state_off);
@@ -108,6 +115,16 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     float xp[TT];
     float pa = 0.0f, pb = 0.0f;   // gate inputs of this row's token (tt = 4 wv + lane/16)
     const int gtok = (wv << 2) + (lane >> 4);
+    const int64_t row_bytes = A.record_row_bytes;
+    const int64_t rows_per_slot = A.n_spec + 1;
+    // gate inputs of this row's replayed record row, with the other small loads
+    float ra = 0.0f, rb = 0.0f;
+    if (n_replay > 0) {
+        const uint8_t* rec = pg + A.record_off + (int64_t)L * rows_per_slot * row_bytes;
+        const float* rrow = reinterpret_cast<const float*>(rec + (gtok < n_replay ? gtok : 0) * row_bytes);
+        ra = rrow[C + h];
+        rb = rrow[C + A.h_v + h];
+    }
     {
         // unconditional loads (row and channel clamped into range) stay in flight
         // together; values past the candidates are zeroed
@@ -139,36 +156,56 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     float s[CPL][R];
     load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
 
-    const int64_t row_bytes = A.record_row_bytes;
-    const int64_t rows_per_slot = A.n_spec + 1;
-
     // ---- one-page: replay rows 0..acc of the live record, store the checkpoint
     if (LAYOUT == GDN_SPEC_ONEPAGE) {
         if (n_replay > 0) {
+            // The replayed rows go straight into the LDS rows, all in flight at
+            // once: lane l of a wave lands at base + 4 l, and each region's base
+            // is chosen so that lane lc writes its own channel's slot.
             const uint8_t* rec = pg + A.record_off + (int64_t)L * rows_per_slot * row_bytes;
-            if (gc >= 0)
-                for (int i = 0; i < n_replay; ++i)
-                    ydst[i * yld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc];
-            __syncthreads();
+            const int wbase = tid & ~63;
+            for (int i = 0; i < n_replay; ++i) {
+                const float* row = reinterpret_cast<const float*>(rec + i * row_bytes);
+                if (lc < DK)
+                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
+                else if (lc < 2 * DK)
+                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
+                else if (lc < NLC)
+                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sv + i * BV + wbase - 2 * DK));
+            }
+            wait_vmem();
+            lds_barrier();
             if (gtok < n_replay) {
-                const float* rrow = reinterpret_cast<const float*>(rec + gtok * row_bytes);
                 (void)gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
                 float eg, beta;
-                gate_scalars(rrow[C + h], rrow[C + A.h_v + h], exp_alog, dtb, eg, beta);
+                gate_scalars(ra, rb, exp_alog, dtb, eg, beta);
                 if ((lane & 15) == 0) {
                     ssc[gtok * 4 + 0] = eg;
                     ssc[gtok * 4 + 1] = beta;
                 }
             }
-            __syncthreads();
+            lds_barrier();
             for (int tt = 0; tt < n_replay; ++tt) {
                 float k[R], v[CPL];
                 lds_rows<R>(sk + tt * DK, tid, k);
                 lds_cols<CPL>(sv + tt * BV, tid, v);
                 delta_update<R, CPL>(s, k, v, ssc[tt * 4 + 0], ssc[tt * 4 + 1]);
             }
-            __syncthreads();
         }
+    }
+
+    // ---- window arrival, before any store: the window values are in registers
+    // (their loads were issued before the state's, which has been consumed),
+    // and the barrier also separates the replay's LDS reads from the
+    // candidates' writes.  The atomic's result is read at the end: reading it
+    // is a wait on the in-order vector-memory counter, and by then the stores
+    // issued after it no longer stand in anyone's way.
+    asm volatile("" : "+v"(xw0), "+v"(xw1), "+v"(xw2), "+v"(done_before));
+    lds_barrier();
+    uint32_t arrived_before = 0;
+    if (tid == 0) arrived_before = arrive(A.sync + (int64_t)page * A.h_k + ki);
+
+    if (LAYOUT == GDN_SPEC_ONEPAGE) {
         // the checkpoint; continue from its stored (rounded) value
         store_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
 #pragma unroll
@@ -199,9 +236,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
             ydst[0] = xw0 + xw1 + xw2;
         }
     }
-    __syncthreads();
-    bool my_last = false;
-    if (tid == 0) my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
+    lds_barrier();
     if (nc > 0) {
         if (gtok < nc) {
             const float kq = gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
@@ -218,7 +253,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         const int cg = lane_colgroup(tid);
         const bool writer = lane_rowgroup(tid) == 0;
         float* __restrict__ O = A.o + (int64_t)req * nc * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + cg * CPL;
@@ -245,8 +280,10 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     } else if (LAYOUT == GDN_SPEC_SLOTS) {
         store_state<StT, DK, CPL>(st_base + (int64_t)h * head_elems + colbase, A.d_v, s, tid);
     }
-    if (tid == 0) sh_last = my_last ? 1 : 0;
-    __syncthreads();
+    asm volatile("" : "+v"(arrived_before));  // keep the read of the result here, not at the atomic
+    if (tid == 0)
+        sh_last = arrived_last(A.sync + (int64_t)page * A.h_k + ki, arrived_before, (uint32_t)(rr * nblk)) ? 1 : 0;
+    lds_barrier();
 
     // ---- conv buffer: [a'+1, a'+2, candidates] or [a', a'+1, a'+2]
     if (gc >= 0 && (lc >= 2 * DK || sh_last)) {
@@ -263,14 +300,12 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
         }
     }
 
-    // ---- done counter: the last workgroup of the request flips the flag.
-    // Every workgroup read the header at its start (values consumed), so the
-    // last arrival may rewrite it; relaxed for the reason given at arrive_last.
-    __syncthreads();
+    // ---- the last workgroup of the request to count itself flips the flag.
+    // Every workgroup of the request read the header before counting, so the
+    // last one may rewrite it; relaxed for the reason given at arrive_last.
     if (tid == 0) {
         const uint32_t total = (uint32_t)(A.h_v * nblk);
-        const uint32_t prev = __hip_atomic_fetch_add(&hdr->flag, 256u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((prev >> 8) + 1u == total) {
+        if ((done_before >> 8) + 1u == total) {
             hdr->n_rows[1 - L] = (uint32_t)nc;
             hdr->accepted = (uint32_t)acc;
             __hip_atomic_store(&hdr->flag, (uint32_t)((1 - L) | (par << 1)), __ATOMIC_RELAXED,
