@@ -185,14 +185,66 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     float* __restrict__ Og = A.o + (int64_t)r0 * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + 16 * wv + lr;
     const int64_t o_stride = (int64_t)A.h_v * A.d_v;
 
+    // ---- a chunk's raw inputs, loaded one chunk ahead into spare registers
+    // (issued once the current chunk's own loads are consumed, so no wait in
+    // a chunk ever covers them): x of channel gq for the 64 tokens, x of v
+    // channel (tid & 63) for tokens 16 (tid >> 6) .. +15 and the three rows
+    // before them, and the gate inputs of token `lane` (wave 0).  Rows are
+    // clamped into the sequence, so every load is unconditional.
+    ActT nq[CH], nv[16], nh[3], na = ActT(0), nb = ActT(0);
+    const int vc = tid & 63, tq = tid >> 6;
+    const int64_t gvc = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + vc;
+    auto prefetch = [&](int cs) {
+        const ActT* xq = X + (int64_t)r0 * A.x_stride + gq;
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            const int tt = cs + t < T ? cs + t : T - 1;
+            nq[t] = xq[(int64_t)tt * A.x_stride];
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int t = cs + 16 * tq - 3 + j;  // sequence-relative row
+            if (t >= 0) {                        // uniform per wave for cs > 0
+                nh[j] = X[(int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gvc];
+            } else {
+                nh[j] = init ? win[(int64_t)(3 + t) * C + gvc] : ActT(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = cs + 16 * tq + i;
+            nv[i] = X[(int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gvc];
+        }
+        if (wv == 0) {
+            const int t = cs + lane < T ? cs + lane : T - 1;
+            const int64_t row = (int64_t)(r0 + t) * A.ab_stride + h;
+            na = static_cast<const ActT*>(A.a)[row];
+            nb = static_cast<const ActT*>(A.b)[row];
+        }
+    };
+    prefetch(0);
+
+    // A chunk's output tile (wave w: columns 16 w .. +15) is stored during the
+    // next chunk, right after that chunk's prefetch is issued.
+    f32x4 o_tile[4];
+    int o_c0 = 0, o_n = 0;
+    auto store_o = [&]() {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * mt + 4 * lg + j;
+                if (t < o_n) Og[(int64_t)(o_c0 + t) * o_stride] = o_tile[mt][j];
+            }
+        o_n = 0;
+    };
+
     for (int c0 = 0; c0 < T; c0 += CH) {
         const int n = (T - c0 < CH) ? (T - c0) : CH;
         // ================================================================ P1
         {
             // q/k: channel `tid` over the 64 tokens in order (the window slides in
-            // registers).  Loads are unconditional (row clamped into range) so a
-            // batch of 32 stays in flight; padded values are zeroed.
-            const ActT* xq = X + (int64_t)(r0 + c0) * A.x_stride + gq;
+            // registers); padded values are zeroed.
             __bf16* qkh = is_q ? Qh + tid : Kh + (tid - DK);
             __bf16* qkl = is_q ? Ql + tid : Kl + (tid - DK);
             for (int t0 = 0; t0 < CH; t0 += 32) {
@@ -200,8 +252,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
                 for (int i = 0; i < 32; ++i) {
                     const int t = t0 + i;
-                    const float xa = to_f32(xq[(int64_t)(t < n ? t : n - 1) * A.x_stride]);
-                    xs[i] = t < n ? xa : 0.0f;
+                    xs[i] = t < n ? to_f32(nq[t]) : 0.0f;
                 }
 #pragma unroll
                 for (int i = 0; i < 32; i += 2) {
@@ -228,26 +279,17 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 }
             }
             // v: channel (tid & 63), tokens 16 (tid >> 6) .. +15, with the three rows
-            // before them loaded (from x, or the window before the first token)
+            // before them (from x, or the window before the first token)
             {
-                const int vc = tid & 63, tq = tid >> 6;
-                const int64_t gvc = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + vc;
                 const float* wvc = wv4 + 4 * vc;
                 float hx[3];
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const int t = c0 + 16 * tq - 3 + j;  // sequence-relative row
-                    const int tc = t < 0 ? 0 : (t < T ? t : T - 1);
-                    const float xa = to_f32(X[(int64_t)(r0 + tc) * A.x_stride + gvc]);
-                    const float wa = init ? to_f32(win[(int64_t)(3 + (t < 0 ? t : -1)) * C + gvc]) : 0.0f;
-                    hx[j] = t >= 0 ? xa : wa;
-                }
+                for (int j = 0; j < 3; ++j) hx[j] = to_f32(nh[j]);
                 float xs[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int t = 16 * tq + i;
-                    const float xa = to_f32(X[(int64_t)(r0 + c0 + (t < n ? t : n - 1)) * A.x_stride + gvc]);
-                    xs[i] = t < n ? xa : 0.0f;
+                    xs[i] = t < n ? to_f32(nv[i]) : 0.0f;
                 }
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
@@ -266,7 +308,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (c0 == 0 && tid == 0)  // every window read of this workgroup has been consumed
             my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
         // ================================================================ P2
@@ -301,9 +343,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             // gates and the cumulative decay: wave 0, lane = token
             if (wv == 0) {
                 const int t = lane;
-                const int64_t row = (int64_t)(r0 + c0 + (t < n ? t : n - 1)) * A.ab_stride + h;
-                const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
-                const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
+                const float av = to_f32(na);
+                const float bv = to_f32(nb);
                 const float g = t < n ? -exp_alog * softplus(av + dtb) : 0.0f;
                 const float beta = t < n ? sigmoid(bv) : 0.0f;
                 float G = g;
@@ -319,7 +360,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 sc[SC_WDR * CH + t] = expf(Glast - G);  // rk folded in below
             }
         }
-        __syncthreads();
+        lds_barrier();
         {
             const int t = tid & 63;
             if (tid < CH) {
@@ -333,7 +374,12 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 klast[tid] = sc[SC_RK * CH + tl] * ((float)KTh[tid * LT + tl] + (float)KTl[tid * LT + tl]);
             }
         }
-        __syncthreads();
+        lds_barrier();
+        // the next chunk's inputs: every load of this chunk has been consumed
+        if (c0 + CH < T) prefetch(c0 + CH);
+        // then the previous chunk's outputs: a wait for the prefetch above (in
+        // order) never covers stores issued after it
+        store_o();
         // ================================================================ P3
         {
             // the 10 tiles on or below the diagonal, round-robin over the waves
@@ -364,7 +410,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 accq[k] = aq; acck[k] = ak;
                 ++cnt;
             }
-            __syncthreads();  // Ql is about to be overwritten by A
+            lds_barrier();  // Ql is about to be overwritten by A
             for (int k = 0; k < 3; ++k) {
                 if (tmt[k] < 0) continue;
                 const int mt = tmt[k], nt = tnt[k];
@@ -388,7 +434,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             }
             (void)cnt;
         }
-        __syncthreads();
+        lds_barrier();
         // ================================================================ P4
         {
             // diagonal block b = wv: T_bb = (I - N)(I + N^2)(I + N^4)(I + N^8)
@@ -414,7 +460,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * b + lr] = (__bf16)R[j];
         }
-        __syncthreads();
+        lds_barrier();
         // off-diagonal blocks by sub-diagonal level: T_bc = -T_bb sum_{d=c}^{b-1} A_bd T_dc
         for (int lev = 1; lev < 4; ++lev) {
             if (wv < 4 - lev) {
@@ -436,7 +482,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * c + lr] = (__bf16)(-Yv[j]);
             }
-            __syncthreads();
+            lds_barrier();
         }
         // LT = T - I (strictly lower), column-scaled by beta and by beta e^G rk
         for (int e = tid; e < CH * CH; e += NTH) {
@@ -445,7 +491,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             LTb[t * LT + sidx] = (__bf16)(lt * sc[SC_BETA * CH + sidx]);
             LTbg[t * LT + sidx] = (__bf16)(lt * sc[SC_BGR * CH + sidx]);
         }
-        __syncthreads();
+        lds_barrier();
         // ================================================================ P5
         {
             // W[t][d] = bgr_t K[t][d] + (LTbg K)[t][d]; 32 tiles, 8 per wave
@@ -474,7 +520,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 for (int j = 0; j < 4; ++j) Wm[(16 * mt + 4 * lg + j) * LQK + 16 * dt + lr] = (__bf16)wacc[k][j];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ================================================================ P6
         {
             const int colv = 16 * wv + lr;  // this lane's column within the block
@@ -524,12 +570,10 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     o = mma16(ph, dl[kt], o);
                     o = mma16(pl, dh[kt], o);
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * mt + 4 * lg + j;
-                    if (t < n) Og[(int64_t)(c0 + t) * o_stride] = o[j];
-                }
+                o_tile[mt] = o;
             }
+            o_c0 = c0;
+            o_n = n;
             // S <- e^{G_last} S + K^T diag(rk e^{G_last - G}) D  (+ the last row exactly)
             bf16x4 wh[4], wl[4];
 #pragma unroll
@@ -565,8 +609,10 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 s[dt] = acc;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
+
+    store_o();  // the last chunk's outputs
 
     // ---- epilogue: state, then the rolled windows
 #pragma unroll
@@ -574,7 +620,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v] = from_f32<StT>(s[dt][j]);
     if (tid == 0) sh_last = my_last ? 1 : 0;
-    __syncthreads();
+    lds_barrier();
     if (sh_last) {
         win[0 * C + gq] = from_f32<ActT>(q3);
         win[1 * C + gq] = from_f32<ActT>(q2);
