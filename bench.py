@@ -300,7 +300,7 @@ def main():
     us = k_ms * 1e3
     nbytes = decode_bytes(wl)
     achieved = nbytes / (k_ms * 1e-3) / 1e9
-    traffic = read_traffic("k_gdn_seq", "decode")
+    traffic = read_traffic("k_gdn_seq_stream", "decode")
     log(f"decode: {us:.2f} us/step kernel, {wall_ms * 1e3:.2f} us/step wall, {achieved:.0f} GB/s")
     result.update({
         "value": round(us, 3), "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -312,7 +312,7 @@ def main():
                    "state_pools_rotated": POOLS},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_gdn_seq", "algorithmic_bytes": nbytes},
+                     "kernel": "k_gdn_seq_stream", "algorithmic_bytes": nbytes},
     })
     del dec
     torch.cuda.empty_cache()
