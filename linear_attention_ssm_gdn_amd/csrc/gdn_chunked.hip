@@ -7,15 +7,18 @@
 // of the fp32 state S (128 x 16) lives in MFMA accumulator registers for the
 // whole sequence.  Chunks of C = 64 tokens run in order.  Per chunk, with
 // chunk-local cumulative decay G and start state S0:
-//   P1  conv + SiLU, one channel per thread; raw post-conv q and k go to LDS
-//       as bf16 hi/lo pairs, token-major (for contractions over d) and k also
-//       transposed (for contractions over tokens); v transposed.
-//   P2  per-token norms (16 lanes per token), k.q, gates, the scan of G.  The
-//       L2 norms stay per-token factors rq (with the output scale) and rk,
+//   P1  conv + SiLU on register tiles (q/k: 8 channels x 8 tokens per thread,
+//       v: 4 x 4), fed by 16-byte row loads issued one chunk ahead.  Raw
+//       post-conv q and k go to LDS as bf16 hi/lo pairs, token-major (for
+//       contractions over d) and k also transposed (for contractions over
+//       tokens); v transposed.  The per-token sums of squares are reduced from
+//       the same registers (16 lanes hold one token group), giving the L2-norm
+//       factors rq (with the output scale) and rk, which stay per-token factors
 //       folded into every product below instead of rescaling the arrays.
+//       Wave 0 also takes the gates and the scan of the cumulative decay G.
 //   P3  Q K^T (three-pass hi/lo) and K K^T on MFMA; P_ts = rq_t rk_s (q_t.k_s)
 //       e^{G_t-G_s} and A_ts = beta_t rk_t rk_s (k_t.k_s) e^{G_t-G_s} for s < t,
-//       masked before the exponential.
+//       masked before the exponential; the diagonal gives k_t.q_t.
 //   P4  UT transform T = (I + A)^{-1}: 16x16 diagonal blocks by the doubling
 //       identity (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8) with both N-powers
 //       and their transposes in registers, then the three block sub-diagonals.
@@ -64,7 +67,8 @@ constexpr int OFF_PL = OFF_PH + CH * LT * 2;
 constexpr int OFF_SC = OFF_PL + CH * LT * 2;   // 8 x [64] fp32 scalars
 constexpr int OFF_KLAST = OFF_SC + 8 * CH * 4; // [128] fp32
 constexpr int OFF_WV = OFF_KLAST + DK * 4;       // [64][4] fp32 v-channel conv taps
-constexpr int LDS_BYTES = OFF_WV + BVC * 4 * 4;
+constexpr int OFF_WQK = OFF_WV + BVC * 4 * 4;    // [256][4] fp32 q and k channel conv taps
+constexpr int LDS_BYTES = OFF_WQK + 2 * DK * 4 * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(CH * LAF * 4 <= SZ_REG && CH * LQK * 2 <= SZ_REG, "region sizes");
 
@@ -97,6 +101,44 @@ __device__ __forceinline__ void split4(const f32x4& v, bf16x4& hi, bf16x4& lo) {
     lo = to_bf4(v[0] - (float)hi[0], v[1] - (float)hi[1], v[2] - (float)hi[2], v[3] - (float)hi[3]);
 }
 __device__ __forceinline__ float silu_fast(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
+__device__ __forceinline__ uint32_t pack_bf2(__bf16 a, __bf16 b) {
+    const bf16x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// K^T [128][LT] is stored with its token columns XOR-swizzled in blocks of 8
+// by bits 3..5 of the row, so that the conv threads' 16-byte column writes
+// (eight channels of one token block per lane group) spread over all banks.
+// Every 4- and 8-token operand read stays inside one block.
+__device__ __forceinline__ int kt_at(int row, int col) { return row * LT + (col ^ (row & 0x38)); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// N consecutive channels of one activation row, loaded as one vector.
+template <typename ActT, int N> struct RowVec;
+template <int N> struct RowVec<bf16_t, N> {
+    typedef uint32_t V __attribute__((ext_vector_type(N / 2)));
+    V v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const V*>(p); }
+    __device__ __forceinline__ void zero() { v = V(0u); }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = v[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <int N> struct RowVec<float, N> {
+    f32x4 v[N / 4];
+    __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) v[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) v[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    __device__ __forceinline__ float get(int e) const { return v[e >> 2][e & 3]; }
+};
 
 template <typename ActT, typename StT>
 __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
@@ -159,21 +201,16 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         for (int j = 0; j < 4; ++j)
             s[dt][j] = init ? to_f32(Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v]) : 0.0f;
 
-    // ---- conv channels: q/k channel `tid`, and v channel `tid` for tid < 64
+    // ---- conv taps to LDS: q/k channel `tid` (q for tid < 128), v channel `tid`
     const ActT* __restrict__ X = static_cast<const ActT*>(A.x);
     ActT* __restrict__ win = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
     const ActT* Wc = static_cast<const ActT*>(A.conv_w);
-    const bool is_q = tid < DK;
-    const int64_t gq = is_q ? (int64_t)ki * DK + tid : (int64_t)A.h_k * DK + (int64_t)ki * DK + (tid - DK);
+    const int64_t gq = tid < DK ? (int64_t)ki * DK + tid : (int64_t)A.h_k * DK + (int64_t)ki * DK + (tid - DK);
     const bool has_v = tid < BVC;
     const int64_t gv = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + tid;
-    float wq[4];
-    float q3 = 0.0f, q2 = 0.0f, q1 = 0.0f;
+    float* wqk = reinterpret_cast<float*>(lds + OFF_WQK);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wq[e] = to_f32(Wc[gq * 4 + e]);
-    if (init) {
-        q3 = to_f32(win[0 * C + gq]); q2 = to_f32(win[1 * C + gq]); q1 = to_f32(win[2 * C + gq]);
-    }
+    for (int e = 0; e < 4; ++e) wqk[4 * tid + e] = to_f32(Wc[gq * 4 + e]);
     if (has_v) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) wv4[4 * tid + e] = to_f32(Wc[gv * 4 + e]);
@@ -185,35 +222,57 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     float* __restrict__ Og = A.o + (int64_t)r0 * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + 16 * wv + lr;
     const int64_t o_stride = (int64_t)A.h_v * A.d_v;
 
+    // ---- conv tiles.  q/k: part (q, then k) = tid >> 7, tokens 8 tgp .. +7,
+    // channels 8 cgl .. +7 of the key head, so the 16 lanes of a DPP row hold
+    // one token group over all 128 channels.  v: tokens 4 tq4 .. +3, channels
+    // 4 vc4 .. +3 of the block.  The lane-derived offsets are recomputed at
+    // each use from an opaque copy of tid (cheap integer work) rather than
+    // hoisted out of the chunk loop, where they would hold registers for its
+    // whole length.
+    auto fresh_tid = [&]() {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
+    // the same for the MFMA phases' lane indices (the wave index made scalar)
+#define PHASE_IDS                                                                      \
+    const int tid = fresh_tid(), lane = tid & 63, lr = lane & 15, lg = lane >> 4;     \
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);                          \
+    (void)lane; (void)lr; (void)lg; (void)wv
+
     // ---- a chunk's raw inputs, loaded one chunk ahead into spare registers
     // (issued once the current chunk's own loads are consumed, so no wait in
-    // a chunk ever covers them): x of channel gq for the 64 tokens, x of v
-    // channel (tid & 63) for tokens 16 (tid >> 6) .. +15 and the three rows
-    // before them, and the gate inputs of token `lane` (wave 0).  Rows are
-    // clamped into the sequence, so every load is unconditional.
-    ActT nq[CH], nv[16], nh[3], na = ActT(0), nb = ActT(0);
-    const int vc = tid & 63, tq = tid >> 6;
-    const int64_t gvc = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + vc;
+    // a chunk ever covers them): each tile's rows with the three before them
+    // (from x, or the window before the first token), and the gate inputs of
+    // token `lane` (wave 0).  Rows past the end are clamped into the sequence
+    // (their outputs are masked), so every load is unconditional.
+    RowVec<ActT, 8> nqk[11];
+    RowVec<ActT, 4> nvv[7];
+    ActT na = ActT(0), nb = ActT(0);
     auto prefetch = [&](int cs) {
-        const ActT* xq = X + (int64_t)r0 * A.x_stride + gq;
+        const int ft = fresh_tid();
+        const int tgp = (ft >> 4) & 7, tq4 = ft & 15;
+        const int64_t gq8 = (int64_t)(ft >> 7) * A.h_k * DK + (int64_t)ki * DK + 8 * (ft & 15);
+        const int64_t gv4 = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + 4 * (ft >> 4);
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            const int tt = cs + t < T ? cs + t : T - 1;
-            nq[t] = xq[(int64_t)tt * A.x_stride];
+        for (int j = 0; j < 11; ++j) {
+            const int t = cs + 8 * tgp - 3 + j;  // sequence-relative row; < 0 only in the first chunk
+            if (t >= 0)
+                nqk[j].load(X + (int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gq8);
+            else if (init)
+                nqk[j].load(win + (int64_t)(3 + t) * C + gq8);
+            else
+                nqk[j].zero();
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int t = cs + 16 * tq - 3 + j;  // sequence-relative row
-            if (t >= 0) {                        // uniform per wave for cs > 0
-                nh[j] = X[(int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gvc];
-            } else {
-                nh[j] = init ? win[(int64_t)(3 + t) * C + gvc] : ActT(0);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = cs + 16 * tq + i;
-            nv[i] = X[(int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gvc];
+        for (int j = 0; j < 7; ++j) {
+            const int t = cs + 4 * tq4 - 3 + j;
+            if (t >= 0)
+                nvv[j].load(X + (int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gv4);
+            else if (init)
+                nvv[j].load(win + (int64_t)(3 + t) * C + gv4);
+            else
+                nvv[j].zero();
         }
         if (wv == 0) {
             const int t = cs + lane < T ? cs + lane : T - 1;
@@ -243,103 +302,97 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         const int n = (T - c0 < CH) ? (T - c0) : CH;
         // ================================================================ P1
         {
-            // q/k: channel `tid` over the 64 tokens in order (the window slides in
-            // registers); padded values are zeroed.
-            __bf16* qkh = is_q ? Qh + tid : Kh + (tid - DK);
-            __bf16* qkl = is_q ? Ql + tid : Kl + (tid - DK);
-            for (int t0 = 0; t0 < CH; t0 += 32) {
-                float xs[32];
+            // q/k tile: one channel at a time over the 8 tokens; the token-major
+            // rows are packed as they fill and stored once complete
+            const int ft = fresh_tid();
+            const int part = ft >> 7, tgp = (ft >> 4) & 7, cgl = ft & 15;
+            const int tq4 = ft & 15, vc4 = ft >> 4;
+            __bf16* rowh = (part ? Kh : Qh) + (8 * tgp) * LQK + 8 * cgl;
+            __bf16* rowl = (part ? Kl : Ql) + (8 * tgp) * LQK + 8 * cgl;
+            const float* wrow = wqk + 4 * (part * DK + 8 * cgl);
+            u32x4 ph[8], pl[8];
+            float ss[8];
 #pragma unroll
-                for (int i = 0; i < 32; ++i) {
-                    const int t = t0 + i;
-                    xs[i] = t < n ? to_f32(nq[t]) : 0.0f;
+            for (int i = 0; i < 8; ++i) ss[i] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 4 * e);
+                const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
+                float xv[11];
+#pragma unroll
+                for (int j = 0; j < 11; ++j) xv[j] = nqk[j].get(e);
+                __bf16 hb[8], lb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    // rows past the end hold clamped real inputs, so the value is finite and is masked by a select
+                    const float yc = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
+                    const float y = 8 * tgp + i < n ? yc : 0.0f;
+                    ss[i] = fmaf(y, y, ss[i]);
+                    hb[i] = (__bf16)y;
+                    lb[i] = (__bf16)(y - (float)hb[i]);
                 }
 #pragma unroll
-                for (int i = 0; i < 32; i += 2) {
-                    float y[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int t = t0 + i + u;
-                        y[u] = 0.0f;
-                        if (t < n) {
-                            y[u] = silu_fast(conv4(wq, q3, q2, q1, xs[i + u]));
-                            q3 = q2; q2 = q1; q1 = xs[i + u];
-                        }
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t mh = (uint32_t)__builtin_bit_cast(uint16_t, hb[i]);
+                    const uint32_t ml = (uint32_t)__builtin_bit_cast(uint16_t, lb[i]);
+                    if (e & 1) {
+                        ph[i][e >> 1] |= mh << 16;
+                        pl[i][e >> 1] |= ml << 16;
+                    } else {
+                        ph[i][e >> 1] = mh;
+                        pl[i][e >> 1] = ml;
                     }
-                    const __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1];
-                    const __bf16 l0 = (__bf16)(y[0] - (float)h0), l1 = (__bf16)(y[1] - (float)h1);
-                    const int t = t0 + i;
-                    qkh[t * LQK] = h0; qkh[(t + 1) * LQK] = h1;
-                    qkl[t * LQK] = l0; qkl[(t + 1) * LQK] = l1;
-                    if (!is_q) {
-                        const bf16x2 ph = {h0, h1}, pl = {l0, l1};
-                        *reinterpret_cast<bf16x2*>(KTh + (tid - DK) * LT + t) = ph;
-                        *reinterpret_cast<bf16x2*>(KTl + (tid - DK) * LT + t) = pl;
-                    }
+                }
+                if (part) {  // k also transposed: channel row, 8 tokens
+                    const int c = 8 * cgl + e;
+                    const u32x4 th = {pack_bf2(hb[0], hb[1]), pack_bf2(hb[2], hb[3]), pack_bf2(hb[4], hb[5]),
+                                      pack_bf2(hb[6], hb[7])};
+                    const u32x4 tl = {pack_bf2(lb[0], lb[1]), pack_bf2(lb[2], lb[3]), pack_bf2(lb[4], lb[5]),
+                                      pack_bf2(lb[6], lb[7])};
+                    *reinterpret_cast<u32x4*>(KTh + kt_at(c, 8 * tgp)) = th;
+                    *reinterpret_cast<u32x4*>(KTl + kt_at(c, 8 * tgp)) = tl;
                 }
             }
-            // v: channel (tid & 63), tokens 16 (tid >> 6) .. +15, with the three rows
-            // before them (from x, or the window before the first token)
-            {
-                const float* wvc = wv4 + 4 * vc;
-                float hx[3];
 #pragma unroll
-                for (int j = 0; j < 3; ++j) hx[j] = to_f32(nh[j]);
-                float xs[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = 16 * tq + i;
-                    xs[i] = t < n ? to_f32(nv[i]) : 0.0f;
-                }
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    float y[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int t = 16 * tq + i + u;
-                        y[u] = t < n ? silu_fast(conv4(wvc, hx[0], hx[1], hx[2], xs[i + u])) : 0.0f;
-                        hx[0] = hx[1]; hx[1] = hx[2]; hx[2] = xs[i + u];
-                    }
-                    const __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1];
-                    const bf16x2 ph = {h0, h1};
-                    const bf16x2 pl = {(__bf16)(y[0] - (float)h0), (__bf16)(y[1] - (float)h1)};
-                    *reinterpret_cast<bf16x2*>(VTh + vc * LT + 16 * tq + i) = ph;
-                    *reinterpret_cast<bf16x2*>(VTl + vc * LT + 16 * tq + i) = pl;
-                }
+            for (int i = 0; i < 8; ++i) {
+                *reinterpret_cast<u32x4*>(rowh + i * LQK) = ph[i];
+                *reinterpret_cast<u32x4*>(rowl + i * LQK) = pl[i];
             }
-        }
-        lds_barrier();
-        if (c0 == 0 && tid == 0)  // every window read of this workgroup has been consumed
-            my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
-        // ================================================================ P2
-        {
-            // norms: 16 lanes per token, tokens grp + 16 i
-            const int grp = tid >> 4, l16 = tid & 15;
+            // L2-norm factors: lane cgl (< 8) of the row writes token 8 tgp + cgl
+            float mine = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = grp + 16 * i;
-                float sq = 0.0f, sk = 0.0f, qk = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = 8 * l16 + e;
-                    const float qv = (float)Qh[t * LQK + d] + (float)Ql[t * LQK + d];
-                    const float kv = (float)Kh[t * LQK + d] + (float)Kl[t * LQK + d];
-                    sq = fmaf(qv, qv, sq);
-                    sk = fmaf(kv, kv, sk);
-                    qk = fmaf(qv, kv, qk);
-                }
-                sq = reduce16(sq);
-                sk = reduce16(sk);
-                qk = reduce16(qk);
-                if (l16 == 0) {
-                    const bool ok = t < n;
-                    const float rq = ok ? A.scale / sqrtf(sq + A.eps) : 0.0f;
-                    const float rk = ok ? 1.0f / sqrtf(sk + A.eps) : 0.0f;
-                    sc[SC_RQ * CH + t] = rq;
-                    sc[SC_RK * CH + t] = rk;
-                    sc[SC_KQ * CH + t] = rq * rk * qk;
-                }
+            for (int i = 0; i < 8; ++i) {
+                const float sum = reduce16(ss[i]);
+                if ((cgl & 7) == i) mine = sum;
             }
+            if (cgl < 8) {
+                const int t = 8 * tgp + cgl;
+                sc[(part ? SC_RK : SC_RQ) * CH + t] = t < n ? (part ? 1.0f : A.scale) / sqrtf(mine + A.eps) : 0.0f;
+            }
+
+            // v tile: channel by channel, 4 tokens each, stored transposed
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int col = 4 * vc4 + e;
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wv4 + 4 * col);
+                const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
+                float xv[7];
+#pragma unroll
+                for (int j = 0; j < 7; ++j) xv[j] = nvv[j].get(e);
+                __bf16 hb[4], lb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float yc = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
+                    const float y = 4 * tq4 + i < n ? yc : 0.0f;
+                    hb[i] = (__bf16)y;
+                    lb[i] = (__bf16)(y - (float)hb[i]);
+                }
+                const u32x2 th = {pack_bf2(hb[0], hb[1]), pack_bf2(hb[2], hb[3])};
+                const u32x2 tl = {pack_bf2(lb[0], lb[1]), pack_bf2(lb[2], lb[3])};
+                *reinterpret_cast<u32x2*>(VTh + col * LT + 4 * tq4) = th;
+                *reinterpret_cast<u32x2*>(VTl + col * LT + 4 * tq4) = tl;
+            }
+
             // gates and the cumulative decay: wave 0, lane = token
             if (wv == 0) {
                 const int t = lane;
@@ -361,20 +414,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             }
         }
         lds_barrier();
-        {
-            const int t = tid & 63;
-            if (tid < CH) {
-                const float rk = sc[SC_RK * CH + t];
-                sc[SC_BGR * CH + t] = sc[SC_BETA * CH + t] * sc[SC_GAM * CH + t] * rk;
-                // the last row of the chunk enters the state update exactly, not through the MFMA
-                sc[SC_WDR * CH + t] = (t == n - 1) ? 0.0f : sc[SC_WDR * CH + t] * rk;
-            }
-            if (tid < DK) {
-                const int tl = n - 1;
-                klast[tid] = sc[SC_RK * CH + tl] * ((float)KTh[tid * LT + tl] + (float)KTl[tid * LT + tl]);
-            }
-        }
-        lds_barrier();
+        if (c0 == 0 && tid == 0)  // every window read of this workgroup has been consumed
+            my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
         // the next chunk's inputs: every load of this chunk has been consumed
         if (c0 + CH < T) prefetch(c0 + CH);
         // then the previous chunk's outputs: a wait for the prefetch above (in
@@ -382,6 +423,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         store_o();
         // ================================================================ P3
         {
+            PHASE_IDS;
             // the 10 tiles on or below the diagonal, round-robin over the waves
             f32x4 accq[3], acck[3];
             int tmt[3], tnt[3];
@@ -411,6 +453,16 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 ++cnt;
             }
             lds_barrier();  // Ql is about to be overwritten by A
+            if (tid < CH) {
+                const int t = tid;
+                const float rk = sc[SC_RK * CH + t];
+                sc[SC_BGR * CH + t] = sc[SC_BETA * CH + t] * sc[SC_GAM * CH + t] * rk;
+                // the last row of the chunk enters the state update exactly, not through the MFMA
+                sc[SC_WDR * CH + t] = (t == n - 1) ? 0.0f : sc[SC_WDR * CH + t] * rk;
+            } else if (tid < CH + DK) {
+                const int d = tid - CH, tl = n - 1;
+                klast[d] = sc[SC_RK * CH + tl] * ((float)KTh[kt_at(d, tl)] + (float)KTl[kt_at(d, tl)]);
+            }
             for (int k = 0; k < 3; ++k) {
                 if (tmt[k] < 0) continue;
                 const int mt = tmt[k], nt = tnt[k];
@@ -426,6 +478,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                         p = sc[SC_RQ * CH + t] * rks * accq[k][j] * e;
                         a = sc[SC_BETA * CH + t] * rkt * rks * acck[k][j] * e;
                     }
+                    if (sidx == t) sc[SC_KQ * CH + t] = sc[SC_RQ * CH + t] * sc[SC_RK * CH + t] * accq[k][j];
                     const __bf16 ph = (__bf16)p;
                     Ph[t * LT + sidx] = ph;
                     Pl[t * LT + sidx] = (__bf16)(p - (float)ph);
@@ -437,6 +490,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         lds_barrier();
         // ================================================================ P4
         {
+            PHASE_IDS;
             // diagonal block b = wv: T_bb = (I - N)(I + N^2)(I + N^4)(I + N^8)
             const int b = wv;
             f32x4 nB, ntB, eye;
@@ -463,6 +517,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         lds_barrier();
         // off-diagonal blocks by sub-diagonal level: T_bc = -T_bb sum_{d=c}^{b-1} A_bd T_dc
         for (int lev = 1; lev < 4; ++lev) {
+            PHASE_IDS;
             if (wv < 4 - lev) {
                 const int c = wv, b = wv + lev;
                 const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -485,7 +540,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             lds_barrier();
         }
         // LT = T - I (strictly lower), column-scaled by beta and by beta e^G rk
-        for (int e = tid; e < CH * CH; e += NTH) {
+        for (int e = fresh_tid(); e < CH * CH; e += NTH) {
             const int t = e >> 6, sidx = e & 63;
             const float lt = (sidx < t) ? (float)Tm[t * LT + sidx] : 0.0f;
             LTb[t * LT + sidx] = (__bf16)(lt * sc[SC_BETA * CH + sidx]);
@@ -494,6 +549,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         lds_barrier();
         // ================================================================ P5
         {
+            PHASE_IDS;
             // W[t][d] = bgr_t K[t][d] + (LTbg K)[t][d]; 32 tiles, 8 per wave
             f32x4 wacc[8];
 #pragma unroll
@@ -503,12 +559,12 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int t = 16 * mt + 4 * lg + j;
-                    wacc[k][j] = sc[SC_BGR * CH + t] * ((float)KTh[d * LT + t] + (float)KTl[d * LT + t]);
+                    wacc[k][j] = sc[SC_BGR * CH + t] * ((float)KTh[kt_at(d, t)] + (float)KTl[kt_at(d, t)]);
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const bf16x8 aop = ld8(LTbg, LT, 16 * mt + lr, 32 * ks + 8 * lg);
-                    const bf16x8 bop = ld8(KTh, LT, d, 32 * ks + 8 * lg);
+                    const bf16x8 bop = *reinterpret_cast<const bf16x8*>(KTh + kt_at(d, 32 * ks + 8 * lg));
                     wacc[k] = mma32(aop, bop, wacc[k]);
                 }
             }
@@ -523,6 +579,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         lds_barrier();
         // ================================================================ P6
         {
+            PHASE_IDS;
             const int colv = 16 * wv + lr;  // this lane's column within the block
             bf16x4 sb[8];
 #pragma unroll
@@ -598,8 +655,9 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 f32x4 acc = s[dt] * glast;
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
-                    const bf16x4 kh = ld4(KTh, LT, 16 * dt + lr, 16 * kt + 4 * lg);
-                    const bf16x4 kl = ld4(KTl, LT, 16 * dt + lr, 16 * kt + 4 * lg);
+                    const int ko = kt_at(16 * dt + lr, 16 * kt + 4 * lg);
+                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(KTh + ko);
+                    const bf16x4 kl = *reinterpret_cast<const bf16x4*>(KTl + ko);
                     acc = mma16(kh, wh[kt], acc);
                     acc = mma16(kh, wl[kt], acc);
                     acc = mma16(kl, wh[kt], acc);
@@ -621,26 +679,28 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         for (int j = 0; j < 4; ++j) Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v] = from_f32<StT>(s[dt][j]);
     if (tid == 0) sh_last = my_last ? 1 : 0;
     lds_barrier();
-    if (sh_last) {
-        win[0 * C + gq] = from_f32<ActT>(q3);
-        win[1 * C + gq] = from_f32<ActT>(q2);
-        win[2 * C + gq] = from_f32<ActT>(q1);
-    }
-    if (has_v) {
-        // rolled v window: the last three rows of (window ++ sequence), read
-        // before any write (this workgroup alone owns these channels)
+    // rolled windows: the last three rows of (window ++ sequence) per channel,
+    // each read before its thread writes.  The v channels belong to this
+    // workgroup alone; the q/k channels are shared by the workgroups of the
+    // key head and written by the last of them to arrive, after every other
+    // has consumed its window reads.
+    auto roll = [&](int64_t ch) {
         float vw[3];
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const int t = T - 3 + j;
-            const float xa = to_f32(X[(int64_t)(r0 + (t < 0 ? 0 : t)) * A.x_stride + gv]);
-            const float wa = init ? to_f32(win[(int64_t)(3 + (t < 0 ? t : -1)) * C + gv]) : 0.0f;
+            const float xa = to_f32(X[(int64_t)(r0 + (t < 0 ? 0 : t)) * A.x_stride + ch]);
+            const float wa = init ? to_f32(win[(int64_t)(3 + (t < 0 ? t : -1)) * C + ch]) : 0.0f;
             vw[j] = t >= 0 ? xa : wa;
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) win[(int64_t)j * C + gv] = from_f32<ActT>(vw[j]);
-    }
+        for (int j = 0; j < 3; ++j) win[(int64_t)j * C + ch] = from_f32<ActT>(vw[j]);
+    };
+    if (sh_last) roll(gq);
+    if (has_v) roll(gv);
 }
+
+#undef PHASE_IDS
 
 template <typename ActT, typename StT>
 hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t s) {
