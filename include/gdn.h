@@ -193,10 +193,10 @@ int32_t gdn_recurrent_seq(const gdn_dims* dims, const gdn_params* params,
  * W = T diag(beta e^G) K, U = T diag(beta) V and the chunk-state update,
  * with bf16 matrix-core products accumulated in fp32.  chunk == 64 is
  * compiled.  workspace: device bytes >= gdn_chunked_workspace_bytes (may be
- * NULL when that is 0).  x rows and conv-window rows are read as 16-byte
- * vectors: x and conv.base must be 16-byte aligned and x_stride and
- * conv.page_stride multiples of 16 bytes' worth of elements (8 bf16 or 4
- * fp32), else GDN_ERR_ARG. */
+ * NULL when that is 0).  x rows and conv-window rows are read, and o rows
+ * written, as 16-byte vectors: x, conv.base and o must be 16-byte aligned and
+ * x_stride and conv.page_stride multiples of 16 bytes' worth of elements (8
+ * bf16 or 4 fp32), else GDN_ERR_ARG. */
 int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* params,
                             const void* x, int64_t x_stride,
                             const void* a, const void* b, int64_t ab_stride,

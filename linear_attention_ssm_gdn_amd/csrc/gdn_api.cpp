@@ -176,10 +176,10 @@ GDN_EXPORT int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* p
     if (st != GDN_OK) return st;
     if (chunk <= 0) return GDN_ERR_ARG;
     if (!gdn::chunked_supported(dims->d_k, dims->d_v, chunk)) return GDN_ERR_UNSUPPORTED;
-    // x and conv-window rows are read as 16-byte vectors
+    // x and conv-window rows are read, and o rows written, as 16-byte vectors
     const int64_t vec = dims->act_dtype == GDN_BF16 ? 8 : 4;
     if (batch->n_seqs > 0 && (!aligned(x, 16) || x_stride % vec != 0 || !aligned(conv.base, 16) ||
-                              conv.page_stride % vec != 0))
+                              conv.page_stride % vec != 0 || !aligned(o, 16)))
         return GDN_ERR_ARG;
     size_t need = 0;
     if ((st = gdn_chunked_workspace_bytes(dims, batch->n_seqs, batch->n_rows, chunk, &need)) != GDN_OK) return st;

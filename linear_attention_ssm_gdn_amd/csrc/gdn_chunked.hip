@@ -69,6 +69,8 @@ constexpr int OFF_KLAST = OFF_SC + 8 * CH * 4; // [128] fp32
 constexpr int OFF_WV = OFF_KLAST + DK * 4;       // [64][4] fp32 v-channel conv taps
 constexpr int OFF_WQK = OFF_WV + BVC * 4 * 4;    // [256][4] fp32 q and k channel conv taps
 constexpr int LDS_BYTES = OFF_WQK + 2 * DK * 4 * 4;
+constexpr int LOS = 68;                          // fp32 row stride of the output staging tile (in P's region)
+static_assert(CH * LOS * 4 <= 2 * CH * LT * 2, "output staging fits P");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(CH * LAF * 4 <= SZ_REG && CH * LQK * 2 <= SZ_REG, "region sizes");
 
@@ -100,10 +102,20 @@ __device__ __forceinline__ void split4(const f32x4& v, bf16x4& hi, bf16x4& lo) {
     hi = to_bf4(v);
     lo = to_bf4(v[0] - (float)hi[0], v[1] - (float)hi[1], v[2] - (float)hi[2], v[3] - (float)hi[3]);
 }
-__device__ __forceinline__ float silu_fast(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
-__device__ __forceinline__ uint32_t pack_bf2(__bf16 a, __bf16 b) {
-    const bf16x2 v = {a, b};
+// SiLU through the hardware exponential and reciprocal (about one ulp each,
+// far inside the error of the bf16 products that consume it).
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two floats rounded to bf16 (nearest even) and packed, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    const bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
     return __builtin_bit_cast(uint32_t, v);
+}
+// hi/lo split of a pair: hi = bf16(a, b), lo = bf16 of what hi misses.
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf2(a, b);
+    lo = pack_bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 // K^T [128][LT] is stored with its token columns XOR-swizzled in blocks of 8
@@ -159,6 +171,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     __bf16* LTbg = reinterpret_cast<__bf16*>(lds + OFF_KH + CH * LT * 2);  // after P4
     __bf16* LTb = reinterpret_cast<__bf16*>(lds + OFF_KL);                 // after P4
     __bf16* Wm = reinterpret_cast<__bf16*>(lds + OFF_QL);                  // after P5
+    float* Os = reinterpret_cast<float*>(lds + OFF_PH);                    // from P6's end to the next P3
     float* sc = reinterpret_cast<float*>(lds + OFF_SC);
     float* klast = reinterpret_cast<float*>(lds + OFF_KLAST);
     float* wv4 = reinterpret_cast<float*>(lds + OFF_WV);
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     const float exp_alog = expf(A.a_log[h]);
     const float dtb = A.dt_bias[h];
     bool my_last = false;
-    float* __restrict__ Og = A.o + (int64_t)r0 * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + 16 * wv + lr;
+    float* __restrict__ Og = A.o + (int64_t)r0 * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase;
     const int64_t o_stride = (int64_t)A.h_v * A.d_v;
 
     // ---- conv tiles.  q/k: part (q, then k) = tid >> 7, tokens 8 tgp .. +7,
@@ -283,18 +296,29 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     };
     prefetch(0);
 
-    // A chunk's output tile (wave w: columns 16 w .. +15) is stored during the
-    // next chunk, right after that chunk's prefetch is issued.
+    // A chunk's output tile (wave w: columns 16 w .. +15, in MFMA accumulator
+    // layout) goes to LDS once the chunk's last read of P is done, and to
+    // memory as 16-byte row pieces during the next chunk, right after that
+    // chunk's prefetch is issued.
     f32x4 o_tile[4];
     int o_c0 = 0, o_n = 0;
-    auto store_o = [&]() {
+    auto stage_o = [&]() {
+        PHASE_IDS;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * mt + 4 * lg + j;
-                if (t < o_n) Og[(int64_t)(o_c0 + t) * o_stride] = o_tile[mt][j];
-            }
+            for (int j = 0; j < 4; ++j) Os[(16 * mt + 4 * lg + j) * LOS + 16 * wv + lr] = o_tile[mt][j];
+    };
+    auto store_o = [&]() {
+        const int ft = fresh_tid();
+        const int c4 = ft & 15, r = ft >> 4;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int t = r + 16 * it;
+            if (t < o_n)
+                *reinterpret_cast<f32x4*>(Og + (int64_t)(o_c0 + t) * o_stride + 4 * c4) =
+                    *reinterpret_cast<const f32x4*>(Os + t * LOS + 4 * c4);
+        }
         o_n = 0;
     };
 
@@ -302,61 +326,69 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         const int n = (T - c0 < CH) ? (T - c0) : CH;
         // ================================================================ P1
         {
-            // q/k tile: one channel at a time over the 8 tokens; the token-major
-            // rows are packed as they fill and stored once complete
+            // q/k tile, two channels at a time over the 8 tokens: each pair packs
+            // into one dword of every token-major row.  Outputs of tokens past
+            // the end are left unmasked: their inputs are clamped real rows, so
+            // they are finite, and every product that reads them is scaled by a
+            // zero factor (rq, rk or beta of the padded token).
             const int ft = fresh_tid();
             const int part = ft >> 7, tgp = (ft >> 4) & 7, cgl = ft & 15;
             const int tq4 = ft & 15, vc4 = ft >> 4;
-            __bf16* rowh = (part ? Kh : Qh) + (8 * tgp) * LQK + 8 * cgl;
-            __bf16* rowl = (part ? Kl : Ql) + (8 * tgp) * LQK + 8 * cgl;
             const float* wrow = wqk + 4 * (part * DK + 8 * cgl);
             u32x4 ph[8], pl[8];
             float ss[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss[i] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 4 * e);
-                const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
-                float xv[11];
+            for (int ep = 0; ep < 4; ++ep) {
+                float y[2][8];
 #pragma unroll
-                for (int j = 0; j < 11; ++j) xv[j] = nqk[j].get(e);
-                __bf16 hb[8], lb[8];
+                for (int u = 0; u < 2; ++u) {
+                    const int e = 2 * ep + u;
+                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 4 * e);
+                    const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
+                    float xv[11];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    // rows past the end hold clamped real inputs, so the value is finite and is masked by a select
-                    const float yc = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
-                    const float y = 8 * tgp + i < n ? yc : 0.0f;
-                    ss[i] = fmaf(y, y, ss[i]);
-                    hb[i] = (__bf16)y;
-                    lb[i] = (__bf16)(y - (float)hb[i]);
-                }
+                    for (int j = 0; j < 11; ++j) xv[j] = nqk[j].get(e);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t mh = (uint32_t)__builtin_bit_cast(uint16_t, hb[i]);
-                    const uint32_t ml = (uint32_t)__builtin_bit_cast(uint16_t, lb[i]);
-                    if (e & 1) {
-                        ph[i][e >> 1] |= mh << 16;
-                        pl[i][e >> 1] |= ml << 16;
-                    } else {
-                        ph[i][e >> 1] = mh;
-                        pl[i][e >> 1] = ml;
+                    for (int i = 0; i < 8; ++i) {
+                        y[u][i] = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
+                        ss[i] = fmaf(y[u][i], y[u][i], ss[i]);
                     }
                 }
-                if (part) {  // k also transposed: channel row, 8 tokens
-                    const int c = 8 * cgl + e;
-                    const u32x4 th = {pack_bf2(hb[0], hb[1]), pack_bf2(hb[2], hb[3]), pack_bf2(hb[4], hb[5]),
-                                      pack_bf2(hb[6], hb[7])};
-                    const u32x4 tl = {pack_bf2(lb[0], lb[1]), pack_bf2(lb[2], lb[3]), pack_bf2(lb[4], lb[5]),
-                                      pack_bf2(lb[6], lb[7])};
-                    *reinterpret_cast<u32x4*>(KTh + kt_at(c, 8 * tgp)) = th;
-                    *reinterpret_cast<u32x4*>(KTl + kt_at(c, 8 * tgp)) = tl;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    uint32_t hi, lo;
+                    split_pk(y[0][i], y[1][i], hi, lo);
+                    ph[i][ep] = hi;
+                    pl[i][ep] = lo;
+                }
+                if (part) {  // k also transposed: rows 2 ep (low halves) and 2 ep + 1 (high halves)
+                    u32x4 h0, h1, l0, l1;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint32_t a = ph[2 * m][ep], b = ph[2 * m + 1][ep];
+                        const uint32_t c = pl[2 * m][ep], d = pl[2 * m + 1][ep];
+                        h0[m] = (a & 0xffffu) | (b << 16);
+                        h1[m] = (a >> 16) | (b & 0xffff0000u);
+                        l0[m] = (c & 0xffffu) | (d << 16);
+                        l1[m] = (c >> 16) | (d & 0xffff0000u);
+                    }
+                    const int c = 8 * cgl + 2 * ep;
+                    *reinterpret_cast<u32x4*>(KTh + kt_at(c, 8 * tgp)) = h0;
+                    *reinterpret_cast<u32x4*>(KTh + kt_at(c + 1, 8 * tgp)) = h1;
+                    *reinterpret_cast<u32x4*>(KTl + kt_at(c, 8 * tgp)) = l0;
+                    *reinterpret_cast<u32x4*>(KTl + kt_at(c + 1, 8 * tgp)) = l1;
                 }
             }
+            {
+                __bf16* rowh = (part ? Kh : Qh) + (8 * tgp) * LQK + 8 * cgl;
+                __bf16* rowl = (part ? Kl : Ql) + (8 * tgp) * LQK + 8 * cgl;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                *reinterpret_cast<u32x4*>(rowh + i * LQK) = ph[i];
-                *reinterpret_cast<u32x4*>(rowl + i * LQK) = pl[i];
+                for (int i = 0; i < 8; ++i) {
+                    *reinterpret_cast<u32x4*>(rowh + i * LQK) = ph[i];
+                    *reinterpret_cast<u32x4*>(rowl + i * LQK) = pl[i];
+                }
             }
             // L2-norm factors: lane cgl (< 8) of the row writes token 8 tgp + cgl
             float mine = 0.0f;
@@ -379,16 +411,13 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 float xv[7];
 #pragma unroll
                 for (int j = 0; j < 7; ++j) xv[j] = nvv[j].get(e);
-                __bf16 hb[4], lb[4];
+                float y[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float yc = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
-                    const float y = 4 * tq4 + i < n ? yc : 0.0f;
-                    hb[i] = (__bf16)y;
-                    lb[i] = (__bf16)(y - (float)hb[i]);
-                }
-                const u32x2 th = {pack_bf2(hb[0], hb[1]), pack_bf2(hb[2], hb[3])};
-                const u32x2 tl = {pack_bf2(lb[0], lb[1]), pack_bf2(lb[2], lb[3])};
+                for (int i = 0; i < 4; ++i) y[i] = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
+                uint32_t h0, l0, h1, l1;
+                split_pk(y[0], y[1], h0, l0);
+                split_pk(y[2], y[3], h1, l1);
+                const u32x2 th = {h0, h1}, tl = {l0, l1};
                 *reinterpret_cast<u32x2*>(VTh + col * LT + 4 * tq4) = th;
                 *reinterpret_cast<u32x2*>(VTl + col * LT + 4 * tq4) = tl;
             }
@@ -407,7 +436,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     if (lane >= off) G += o;
                 }
                 const float Glast = __shfl(G, 63, 64);
-                sc[SC_G * CH + t] = G;
+                sc[SC_G * CH + t] = G * 1.44269504088896341f;  // log2(e) G: P3 takes exp2 of differences
                 sc[SC_BETA * CH + t] = beta;
                 sc[SC_GAM * CH + t] = expf(G);
                 sc[SC_WDR * CH + t] = expf(Glast - G);  // rk folded in below
@@ -444,10 +473,12 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     const bf16x8 khm = ld8(Kh, LQK, 16 * mt + lr, col);
                     const bf16x8 khn = ld8(Kh, LQK, 16 * nt + lr, col);
                     const bf16x8 kln = ld8(Kl, LQK, 16 * nt + lr, col);
-                    aq = mma32(qh, khn, aq);
-                    aq = mma32(qh, kln, aq);
-                    aq = mma32(ql, khn, aq);
-                    ak = mma32(khm, khn, ak);
+                    // transposed tiles (rows s, columns t), so that each lane holds
+                    // four consecutive s of one t and writes them as one vector
+                    aq = mma32(khn, qh, aq);
+                    aq = mma32(kln, qh, aq);
+                    aq = mma32(khn, ql, aq);
+                    ak = mma32(khn, khm, ak);
                 }
                 accq[k] = aq; acck[k] = ak;
                 ++cnt;
@@ -466,24 +497,30 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             for (int k = 0; k < 3; ++k) {
                 if (tmt[k] < 0) continue;
                 const int mt = tmt[k], nt = tnt[k];
-                const int sidx = 16 * nt + lr;
-                const float Gs = sc[SC_G * CH + sidx], rks = sc[SC_RK * CH + sidx];
+                const int t = 16 * mt + lr, s0 = 16 * nt + 4 * lg;
+                const float g2t = sc[SC_G * CH + t], rqt = sc[SC_RQ * CH + t];
+                const float rkt = sc[SC_RK * CH + t], bt = sc[SC_BETA * CH + t];
+                const f32x4 g2s = *reinterpret_cast<const f32x4*>(sc + SC_G * CH + s0);
+                const f32x4 rks = *reinterpret_cast<const f32x4*>(sc + SC_RK * CH + s0);
+                float p[4];
+                f32x4 a;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * mt + 4 * lg + j;
-                    float p = 0.0f, a = 0.0f;
-                    if (sidx < t) {
-                        const float e = expf(sc[SC_G * CH + t] - Gs);
-                        const float rkt = sc[SC_RK * CH + t];
-                        p = sc[SC_RQ * CH + t] * rks * accq[k][j] * e;
-                        a = sc[SC_BETA * CH + t] * rkt * rks * acck[k][j] * e;
-                    }
-                    if (sidx == t) sc[SC_KQ * CH + t] = sc[SC_RQ * CH + t] * sc[SC_RK * CH + t] * accq[k][j];
-                    const __bf16 ph = (__bf16)p;
-                    Ph[t * LT + sidx] = ph;
-                    Pl[t * LT + sidx] = (__bf16)(p - (float)ph);
-                    Af[t * LAF + sidx] = a;
+                    // computed for every s and selected: for s >= t the exponential
+                    // may overflow, and is discarded
+                    const float e = __builtin_amdgcn_exp2f(g2t - g2s[j]);
+                    const float pv = rqt * rks[j] * accq[k][j] * e;
+                    const float av = bt * rkt * rks[j] * acck[k][j] * e;
+                    p[j] = s0 + j < t ? pv : 0.0f;
+                    a[j] = s0 + j < t ? av : 0.0f;
+                    if (s0 + j == t) sc[SC_KQ * CH + t] = rqt * rkt * accq[k][j];
                 }
+                uint32_t h0, l0, h1, l1;
+                split_pk(p[0], p[1], h0, l0);
+                split_pk(p[2], p[3], h1, l1);
+                *reinterpret_cast<u32x2*>(Ph + t * LT + s0) = u32x2{h0, h1};
+                *reinterpret_cast<u32x2*>(Pl + t * LT + s0) = u32x2{l0, l1};
+                *reinterpret_cast<f32x4*>(Af + t * LAF + s0) = a;
             }
             (void)cnt;
         }
@@ -540,11 +577,25 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             lds_barrier();
         }
         // LT = T - I (strictly lower), column-scaled by beta and by beta e^G rk
-        for (int e = fresh_tid(); e < CH * CH; e += NTH) {
-            const int t = e >> 6, sidx = e & 63;
-            const float lt = (sidx < t) ? (float)Tm[t * LT + sidx] : 0.0f;
-            LTb[t * LT + sidx] = (__bf16)(lt * sc[SC_BETA * CH + sidx]);
-            LTbg[t * LT + sidx] = (__bf16)(lt * sc[SC_BGR * CH + sidx]);
+        // (8 columns of one row per thread and pass)
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int e = fresh_tid() + NTH * pass;
+            const int t = e >> 3, s0 = 8 * (e & 7);
+            const bf16x8 tv = *reinterpret_cast<const bf16x8*>(Tm + t * LT + s0);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0 + 4);
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + s0);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + s0 + 4);
+            float lt[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) lt[k] = s0 + k < t ? (float)tv[k] : 0.0f;
+            const u32x4 ob = {pack_bf2(lt[0] * b0[0], lt[1] * b0[1]), pack_bf2(lt[2] * b0[2], lt[3] * b0[3]),
+                              pack_bf2(lt[4] * b1[0], lt[5] * b1[1]), pack_bf2(lt[6] * b1[2], lt[7] * b1[3])};
+            const u32x4 og = {pack_bf2(lt[0] * g0[0], lt[1] * g0[1]), pack_bf2(lt[2] * g0[2], lt[3] * g0[3]),
+                              pack_bf2(lt[4] * g1[0], lt[5] * g1[1]), pack_bf2(lt[6] * g1[2], lt[7] * g1[3])};
+            *reinterpret_cast<u32x4*>(LTb + t * LT + s0) = ob;
+            *reinterpret_cast<u32x4*>(LTbg + t * LT + s0) = og;
         }
         lds_barrier();
         // ================================================================ P5
@@ -556,11 +607,12 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             for (int k = 0; k < 8; ++k) {
                 const int idx = wv + 4 * k, mt = idx >> 3, dt = idx & 7;
                 const int d = 16 * dt + lr;
+                const int ko = kt_at(d, 16 * mt + 4 * lg);
+                const bf16x4 kh = *reinterpret_cast<const bf16x4*>(KTh + ko);
+                const bf16x4 kl = *reinterpret_cast<const bf16x4*>(KTl + ko);
+                const f32x4 bg = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + 16 * mt + 4 * lg);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * mt + 4 * lg + j;
-                    wacc[k][j] = sc[SC_BGR * CH + t] * ((float)KTh[kt_at(d, t)] + (float)KTl[kt_at(d, t)]);
-                }
+                for (int j = 0; j < 4; ++j) wacc[k][j] = bg[j] * ((float)kh[j] + (float)kl[j]);
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const bf16x8 aop = ld8(LTbg, LT, 16 * mt + lr, 32 * ks + 8 * lg);
@@ -668,8 +720,10 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             }
         }
         lds_barrier();
+        stage_o();  // P is dead until the next chunk's P3
     }
 
+    lds_barrier();
     store_o();  // the last chunk's outputs
 
     // ---- epilogue: state, then the rolled windows

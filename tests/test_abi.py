@@ -165,10 +165,10 @@ def test_chunked_validation(so, L):
     d = _dims(L)
     a = _seq_args(L, d)
 
-    def call(chunk=64, ws_bytes=0, dims=d, x=a["x"], x_stride=a["x_stride"], conv=a["conv"]):
+    def call(chunk=64, ws_bytes=0, dims=d, x=a["x"], x_stride=a["x_stride"], conv=a["conv"], o=a["o"]):
         return so.gdn_chunked_prefill(ctypes.byref(dims), ctypes.byref(a["params"]), x, x_stride, a["a"],
                                       a["b"], a["ab_stride"], ctypes.byref(a["batch"]), conv, a["state"],
-                                      a["o"], chunk, None, ws_bytes, None, None)
+                                      o, chunk, None, ws_bytes, None, None)
     assert call(chunk=0) == 1
     assert call(chunk=32) == 2
     assert call(dims=_dims(L, d_k=64)) == 2
@@ -178,6 +178,7 @@ def test_chunked_validation(so, L):
     assert call(x_stride=C + 4) == 1
     assert call(conv=L.GdnConvPool(FAKE + 8, 3 * C, 3, 4, FAKE)) == 1
     assert call(conv=L.GdnConvPool(FAKE, 3 * C + 4, 3, 4, FAKE)) == 1
+    assert call(o=FAKE + 4) == 1
     out = ctypes.c_size_t(123)
     assert so.gdn_chunked_workspace_bytes(ctypes.byref(d), 4, 32768, 64, ctypes.byref(out)) == 0
     assert out.value == 0
