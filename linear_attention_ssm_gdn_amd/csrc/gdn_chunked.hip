@@ -98,6 +98,7 @@ __device__ __forceinline__ bf16x4 to_bf4(float a, float b, float c, float d) {
     return r;
 }
 __device__ __forceinline__ bf16x4 to_bf4(const f32x4& v) { return to_bf4(v[0], v[1], v[2], v[3]); }
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
 __device__ __forceinline__ void split4(const f32x4& v, bf16x4& hi, bf16x4& lo) {
     hi = to_bf4(v);
     lo = to_bf4(v[0] - (float)hi[0], v[1] - (float)hi[1], v[2] - (float)hi[2], v[3] - (float)hi[3]);
@@ -105,6 +106,9 @@ __device__ __forceinline__ void split4(const f32x4& v, bf16x4& hi, bf16x4& lo) {
 // SiLU through the hardware exponential and reciprocal (about one ulp each,
 // far inside the error of the bf16 products that consume it).
 __device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+// The same for z given as log2(e) z, returning log2(e) silu(z).
+__device__ __forceinline__ float silu_log2e(float zl) { return zl * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zl)); }
+constexpr float LOG2E = 1.44269504088896341f;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 // Two floats rounded to bf16 (nearest even) and packed, a in the low half.
@@ -222,8 +226,11 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     const bool has_v = tid < BVC;
     const int64_t gv = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + tid;
     float* wqk = reinterpret_cast<float*>(lds + OFF_WQK);
+    // q and k are only ever used through their L2-norm factors, so they are
+    // carried scaled by log2(e) (conv taps scaled here, eps by log2(e)^2 in
+    // the norms), which puts the SiLU's exponential on exp2 directly
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wqk[4 * tid + e] = to_f32(Wc[gq * 4 + e]);
+    for (int e = 0; e < 4; ++e) wqk[4 * tid + e] = LOG2E * to_f32(Wc[gq * 4 + e]);
     if (has_v) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) wv4[4 * tid + e] = to_f32(Wc[gv * 4 + e]);
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     for (int j = 0; j < 11; ++j) xv[j] = nqk[j].get(e);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        y[u][i] = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
+                        y[u][i] = silu_log2e(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
                         ss[i] = fmaf(y[u][i], y[u][i], ss[i]);
                     }
                 }
@@ -399,7 +406,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             }
             if (cgl < 8) {
                 const int t = 8 * tgp + cgl;
-                sc[(part ? SC_RK : SC_RQ) * CH + t] = t < n ? (part ? 1.0f : A.scale) / sqrtf(mine + A.eps) : 0.0f;
+                sc[(part ? SC_RK : SC_RQ) * CH + t] =
+                    t < n ? (part ? 1.0f : A.scale) / sqrtf(mine + (LOG2E * LOG2E) * A.eps) : 0.0f;
             }
 
             // v tile: channel by channel, 4 tokens each, stored transposed
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     if (lane >= off) G += o;
                 }
                 const float Glast = __shfl(G, 63, 64);
-                sc[SC_G * CH + t] = G * 1.44269504088896341f;  // log2(e) G: P3 takes exp2 of differences
+                sc[SC_G * CH + t] = G * LOG2E;  // P3 takes exp2 of differences
                 sc[SC_BETA * CH + t] = beta;
                 sc[SC_GAM * CH + t] = expf(G);
                 sc[SC_WDR * CH + t] = expf(Glast - G);  // rk folded in below
@@ -633,51 +641,70 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         {
             PHASE_IDS;
             const int colv = 16 * wv + lr;  // this lane's column within the block
-            bf16x4 sb[8];
+            // Contractions over d and over tokens run as 16x16x32 products on
+            // accumulator-layout operands: lane group lg supplies K indices
+            // 16 k + 4 lg + (0..3) of two consecutive 16-blocks k, which is a
+            // permutation of the 32 K indices shared by both operands.
+            bf16x8 sb[4];
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) sb[dt] = to_bf4(s[dt]);
+            for (int kk = 0; kk < 4; ++kk) sb[kk] = cat8(to_bf4(s[2 * kk]), to_bf4(s[2 * kk + 1]));
             f32x4 D[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 // U = beta V + LTb V
+                const int t0 = 16 * mt + 4 * lg;
+                const bf16x4 vh = ld4(VTh, LT, colv, t0), vl = ld4(VTl, LT, colv, t0);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + t0);
                 f32x4 u;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * mt + 4 * lg + j;
-                    u[j] = sc[SC_BETA * CH + t] * ((float)VTh[colv * LT + t] + (float)VTl[colv * LT + t]);
-                }
+                for (int j = 0; j < 4; ++j) u[j] = bt[j] * ((float)vh[j] + (float)vl[j]);
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
                     u = mma32(ld8(LTb, LT, 16 * mt + lr, 32 * ks + 8 * lg), ld8(VTh, LT, colv, 32 * ks + 8 * lg), u);
                 // W S
                 f32x4 ws = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int kt = 0; kt < 8; ++kt) ws = mma16(ld4(Wm, LQK, 16 * mt + lr, 16 * kt + 4 * lg), sb[kt], ws);
+                for (int kk = 0; kk < 4; ++kk)
+                    ws = mma32(cat8(ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 4 * lg), ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 16 + 4 * lg)),
+                               sb[kk], ws);
                 D[mt] = u - ws;
             }
             bf16x4 dh[4], dl[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) split4(D[mt], dh[mt], dl[mt]);
-            // O = diag(e^G rq) Q S + diag(k.q) D + P D
+            // O = diag(e^G rq) Q S + diag(k.q) D + P D  (P is lower triangular by
+            // 16-blocks: block pairs below the diagonal, then the diagonal block
+            // alone where it starts a pair)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
+                const int row = 16 * mt + lr;
                 f32x4 qs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int kt = 0; kt < 8; ++kt) qs = mma16(ld4(Qh, LQK, 16 * mt + lr, 16 * kt + 4 * lg), sb[kt], qs);
+                for (int kk = 0; kk < 4; ++kk)
+                    qs = mma32(cat8(ld4(Qh, LQK, row, 32 * kk + 4 * lg), ld4(Qh, LQK, row, 32 * kk + 16 + 4 * lg)), sb[kk], qs);
+                const int t0 = 16 * mt + 4 * lg;
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(sc + SC_GAM * CH + t0);
+                const f32x4 rq = *reinterpret_cast<const f32x4*>(sc + SC_RQ * CH + t0);
+                const f32x4 kq = *reinterpret_cast<const f32x4*>(sc + SC_KQ * CH + t0);
                 f32x4 o;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * mt + 4 * lg + j;
-                    o[j] = sc[SC_GAM * CH + t] * sc[SC_RQ * CH + t] * qs[j] + sc[SC_KQ * CH + t] * D[mt][j];
-                }
+                for (int j = 0; j < 4; ++j) o[j] = gm[j] * rq[j] * qs[j] + kq[j] * D[mt][j];
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    if (kt > mt) continue;
-                    const bf16x4 ph = ld4(Ph, LT, 16 * mt + lr, 16 * kt + 4 * lg);
-                    const bf16x4 pl = ld4(Pl, LT, 16 * mt + lr, 16 * kt + 4 * lg);
-                    o = mma16(ph, dh[kt], o);
-                    o = mma16(ph, dl[kt], o);
-                    o = mma16(pl, dh[kt], o);
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (2 * kk + 1 > mt) continue;
+                    const bf16x8 ph = cat8(ld4(Ph, LT, row, 32 * kk + 4 * lg), ld4(Ph, LT, row, 32 * kk + 16 + 4 * lg));
+                    const bf16x8 pl = cat8(ld4(Pl, LT, row, 32 * kk + 4 * lg), ld4(Pl, LT, row, 32 * kk + 16 + 4 * lg));
+                    const bf16x8 bh = cat8(dh[2 * kk], dh[2 * kk + 1]), bl = cat8(dl[2 * kk], dl[2 * kk + 1]);
+                    o = mma32(ph, bh, o);
+                    o = mma32(ph, bl, o);
+                    o = mma32(pl, bh, o);
+                }
+                if ((mt & 1) == 0) {
+                    const bf16x4 ph = ld4(Ph, LT, row, 16 * mt + 4 * lg);
+                    const bf16x4 pl = ld4(Pl, LT, row, 16 * mt + 4 * lg);
+                    o = mma16(ph, dh[mt], o);
+                    o = mma16(ph, dl[mt], o);
+                    o = mma16(pl, dh[mt], o);
                 }
                 o_tile[mt] = o;
             }
@@ -687,10 +714,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             bf16x4 wh[4], wl[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                f32x4 dw;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dw[j] = D[kt][j] * sc[SC_WDR * CH + 16 * kt + 4 * lg + j];
-                split4(dw, wh[kt], wl[kt]);
+                const f32x4 wd = *reinterpret_cast<const f32x4*>(sc + SC_WDR * CH + 16 * kt + 4 * lg);
+                split4(D[kt] * wd, wh[kt], wl[kt]);
             }
             const int tl = n - 1;
             float dsel = 0.0f;
@@ -702,20 +727,28 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             // the lane of group (tl % 16) / 4 holds D[tl][colv]
             const float dlast = __shfl(dsel, ((tl & 15) >> 2) * 16 + lr, 64);
             const float glast = sc[SC_GAM * CH + tl];
+            bf16x8 wh2[2], wl2[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                wh2[kk] = cat8(wh[2 * kk], wh[2 * kk + 1]);
+                wl2[kk] = cat8(wl[2 * kk], wl[2 * kk + 1]);
+            }
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
+                const int row = 16 * dt + lr;
                 f32x4 acc = s[dt] * glast;
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const int ko = kt_at(16 * dt + lr, 16 * kt + 4 * lg);
-                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(KTh + ko);
-                    const bf16x4 kl = *reinterpret_cast<const bf16x4*>(KTl + ko);
-                    acc = mma16(kh, wh[kt], acc);
-                    acc = mma16(kh, wl[kt], acc);
-                    acc = mma16(kl, wh[kt], acc);
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int k0 = kt_at(row, 32 * kk + 4 * lg), k1 = kt_at(row, 32 * kk + 16 + 4 * lg);
+                    const bf16x8 kh = cat8(*reinterpret_cast<const bf16x4*>(KTh + k0), *reinterpret_cast<const bf16x4*>(KTh + k1));
+                    const bf16x8 kl = cat8(*reinterpret_cast<const bf16x4*>(KTl + k0), *reinterpret_cast<const bf16x4*>(KTl + k1));
+                    acc = mma32(kh, wh2[kk], acc);
+                    acc = mma32(kh, wl2[kk], acc);
+                    acc = mma32(kl, wh2[kk], acc);
                 }
+                const f32x4 kv = *reinterpret_cast<const f32x4*>(klast + 16 * dt + 4 * lg);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = fmaf(klast[16 * dt + 4 * lg + j], dlast, acc[j]);
+                for (int j = 0; j < 4; ++j) acc[j] = fmaf(kv[j], dlast, acc[j]);
                 s[dt] = acc;
             }
         }
