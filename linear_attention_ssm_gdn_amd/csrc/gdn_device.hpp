@@ -36,6 +36,11 @@ template <typename T> __device__ __forceinline__ float round_as(float v) { retur
 // ------------------------------------------------------------- gating (b)
 // SiLU(z) = z / (1 + e^{-z}).
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// The fused kernels' SiLU: the hardware exponential and reciprocal (about one
+// ulp each, so a few ulp overall).  Every token-by-token kernel (sequence,
+// streaming decode, verify) uses this one, which keeps them bit-identical to
+// each other.
+__device__ __forceinline__ float silu_hw(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // softplus(u) = log(1 + e^u); for u > 20 it equals u to within 2e-9 relative.
 __device__ __forceinline__ float softplus(float u) { return u > 20.0f ? u : log1pf(expf(u)); }

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
             for (int tt = 0; tt < TT; ++tt) {
                 if (tt < nt) {
                     const float x0 = xp[tt];
-                    ydst[tt * yld] = silu(conv4(w, xm3, xm2, xm1, x0));
+                    ydst[tt * yld] = silu_hw(conv4(w, xm3, xm2, xm1, x0));
                     xm3 = xm2;
                     xm2 = xm1;
                     xm1 = x0;
@@ -166,13 +166,20 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
         }
         __syncthreads();
         if (t0 + TT < T) prefetch(t0 + TT);
-        // B: the recurrence
-        for (int tt = 0; tt < nt; ++tt) {
-            float k[R], q[R], v[CPL], o[CPL];
-            lds_rows<R>(sk + tt * DK, tid, k);
-            lds_rows<R>(sq + tt * DK, tid, q);
-            lds_cols<CPL>(sv + tt * BV, tid, v);
-            delta_step<R, CPL>(s, k, q, v, ssc[tt * 4 + 0], ssc[tt * 4 + 1], ssc[tt * 4 + 2], o);
+        // B: the recurrence, two tokens per trip with two operand sets, each
+        // set's LDS reads issued one token ahead of its use
+        struct Opnd { float k[R], q[R], v[CPL], eg, beta, kq; };
+        auto operands = [&](Opnd& p, int tt) {
+            lds_rows<R>(sk + tt * DK, tid, p.k);
+            lds_rows<R>(sq + tt * DK, tid, p.q);
+            lds_cols<CPL>(sv + tt * BV, tid, p.v);
+            p.eg = ssc[tt * 4 + 0];
+            p.beta = ssc[tt * 4 + 1];
+            p.kq = ssc[tt * 4 + 2];
+        };
+        auto step = [&](const Opnd& p, int tt) {
+            float o[CPL];
+            delta_step<R, CPL>(s, p.k, p.q, p.v, p.eg, p.beta, p.kq, o);
             if (writer) {
                 float* dst = O + (int64_t)(t0 + tt) * o_stride;
                 if constexpr (CPL == 4) {
@@ -181,6 +188,16 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) dst[c] = o[c];
                 }
+            }
+        };
+        Opnd pa_, pb_;
+        operands(pa_, 0);
+        for (int tt = 0; tt < nt; tt += 2) {
+            operands(pb_, tt + 1 < nt ? tt + 1 : tt);
+            step(pa_, tt);
+            if (tt + 1 < nt) {
+                operands(pa_, tt + 2 < nt ? tt + 2 : tt + 1);
+                step(pb_, tt + 1);
             }
         }
         __syncthreads();
@@ -406,7 +423,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
                     }
                 }
                 if (has_ch) {
-                    *ydst = silu(conv4(w, xm3, xm2, xm1, x0));
+                    *ydst = silu_hw(conv4(w, xm3, xm2, xm1, x0));
                     xm3 = xm2;
                     xm2 = xm1;
                     xm1 = x0;

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
             for (int tt = 0; tt < TT; ++tt) {
                 if (tt < nc) {
                     const float x0 = xp[tt];
-                    const float y = silu(conv4(w, x3, x2, x1, x0));
+                    const float y = silu_hw(conv4(w, x3, x2, x1, x0));
                     ydst[tt * yld] = y;
                     if (rec_this) reinterpret_cast<float*>(recw + tt * row_bytes)[gc] = y;
                     x3 = x2; x2 = x1; x1 = x0;
