@@ -135,6 +135,10 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
     const int64_t o_stride = (int64_t)A.h_v * A.d_v;
     bool my_last = false;
 
+    // The barriers in the chunk loop order LDS only: a full workgroup barrier
+    // would also wait for every outstanding global store and for the next
+    // chunk's prefetch.  Each thread's own loads are waited for where their
+    // registers are used.
     for (int t0 = 0; t0 < T; t0 += TT) {
         const int nt = (T - t0 < TT) ? (T - t0) : TT;
         // A1: conv + SiLU into LDS
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (t0 == 0 && tid == 0)  // every window read of this workgroup has been consumed
             my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
         // A2: gating, one 16-lane row per token
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
                 ssc[gtok * 4 + 2] = kq;
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (t0 + TT < T) prefetch(t0 + TT);
         // B: the recurrence, two tokens per trip with two operand sets, each
         // set's LDS reads issued one token ahead of its use
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
                 step(pb_, tt + 1);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- epilogue: state, then the rolled windows
