@@ -44,7 +44,34 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
     const int blk = bid % nblk;
     bid /= nblk;
     const int h = bid % A.h_v;
-    const int seq = bid / A.h_v;
+    // Dispatch order: workgroups are handed out in index order, so when the
+    // grid exceeds what stays resident, index v is mapped to the v-th longest
+    // sequence (ties by position) and the longest sequences, which set the
+    // kernel's critical path, start first.  Every workgroup ranks the lengths
+    // itself (batches of up to one sequence per thread; larger batches keep
+    // their order).
+    int seq = bid / A.h_v;
+    if (A.n_seqs > 1 && A.n_seqs <= BLOCK_THREADS) {
+        int* len = reinterpret_cast<int*>(sq);  // free until the first conv
+        __shared__ int sh_seq;
+        const int n = A.n_seqs;
+        int my = 0;
+        if (tid < n) {
+            my = A.cu[tid + 1] - A.cu[tid];
+            len[tid] = my;
+        }
+        __syncthreads();
+        if (tid < n) {
+            int rank = 0;
+            for (int j = 0; j < n; ++j) {
+                const int lj = len[j];
+                rank += (lj > my || (lj == my && j < tid)) ? 1 : 0;
+            }
+            if (rank == seq) sh_seq = tid;
+        }
+        __syncthreads();
+        seq = sh_seq;
+    }
     const int rr = A.h_v / A.h_k;
     const int ki = h / rr;
     const int colbase = blk * BV;
