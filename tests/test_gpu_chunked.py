@@ -39,6 +39,15 @@ def test_chunked_parity_ragged(ora, lens):
     _check(ora, wl, wk.make_sequence_inputs(wl))
 
 
+def test_chunked_fp32_activations_short_sequences(ora):
+    """fp32 activations (rows read as 16-byte vectors of 4 channels) and
+    sequences shorter than the conv window, with and without an initial
+    state: the first chunk's halo rows come from the window or are zero."""
+    wl = _small((1, 2, 3, 66, 129), seed=45, act_dtype=wk.F32)
+    inp = wk.make_sequence_inputs(wl)
+    _check(ora, wl, inp, has_init=np.array([0, 1, 0, 1, 0], np.uint8))
+
+
 def test_chunked_bf16_state_and_has_init(ora):
     wl = _small((150, 70), seed=42)
     inp = wk.make_sequence_inputs(wl)
