@@ -108,19 +108,30 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
     }
     float* ydst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
     const int yld = lc < 2 * DK ? DK : BV;
-    const float exp_alog = expf(A.a_log[h]);
-    const float dtb = A.dt_bias[h];
+    float exp_alog_v = expf(A.a_log[h]);
+    float dtb = A.dt_bias[h];
+    asm volatile("" : "+v"(dtb));
+    const float& exp_alog = exp_alog_v;
 
-    // ---- candidate inputs (loaded early; consumed after the replay)
+    // ---- LDS rows: when both the replayed rows and the candidates fit in
+    // half of the TT token rows ("split"), the replayed rows take rows
+    // 0 .. TT/2-1 and the candidates rows TT/2 .. TT-1, so the candidates'
+    // conv and every gate run while the state is still in flight; otherwise
+    // both start at row 0 and the candidates follow the replay.
+    const bool split = (nc <= TT / 2) && (n_replay <= TT / 2);
+    const int crow = split ? TT / 2 : 0;       // first candidate row
+    const int gtok = (wv << 2) + (lane >> 4);  // the token row of this thread's 16-lane row
+    const int cidx = gtok - crow;              // the candidate of that row (if any)
+
+    // ---- small inputs first, then the state: loads complete in order, so
+    // everything above the state is usable while the state is in flight
     float xp[TT];
-    float pa = 0.0f, pb = 0.0f;   // gate inputs of this row's token (tt = 4 wv + lane/16)
-    const int gtok = (wv << 2) + (lane >> 4);
+    float pa = 0.0f, pb = 0.0f;   // gate inputs of candidate cidx
     const int64_t row_bytes = A.record_row_bytes;
     const int64_t rows_per_slot = A.n_spec + 1;
-    // gate inputs of this row's replayed record row, with the other small loads
-    float ra = 0.0f, rb = 0.0f;
+    float ra = 0.0f, rb = 0.0f;   // gate inputs of replayed row gtok
+    const uint8_t* rec = pg + A.record_off + (int64_t)L * rows_per_slot * row_bytes;
     if (n_replay > 0) {
-        const uint8_t* rec = pg + A.record_off + (int64_t)L * rows_per_slot * row_bytes;
         const float* rrow = reinterpret_cast<const float*>(rec + (gtok < n_replay ? gtok : 0) * row_bytes);
         ra = rrow[C + h];
         rb = rrow[C + A.h_v + h];
@@ -138,8 +149,8 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
                 xp[tt] = (gc >= 0 && tt < nc) ? xv : 0.0f;
             }
             {
-                const bool ok = gtok < nc;
-                const int64_t row = ((int64_t)req * nc + (ok ? gtok : nc - 1)) * A.ab_stride + h;
+                const bool ok = cidx >= 0 && cidx < nc;
+                const int64_t row = ((int64_t)req * nc + (ok ? cidx : nc - 1)) * A.ab_stride + h;
                 const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
                 const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
                 pa = ok ? av : 0.0f;
@@ -150,46 +161,123 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
             for (int tt = 0; tt < TT; ++tt) xp[tt] = 0.0f;
         }
     }
+    // One-page: the replayed rows go straight into the LDS rows 0 .. n_replay-1,
+    // all in flight at once: lane l of a wave lands at base + 4 l, and each
+    // region's base is chosen so that lane lc writes its own channel's slot.
+    if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
+        const int wbase = tid & ~63;
+        for (int i = 0; i < n_replay; ++i) {
+            const float* row = reinterpret_cast<const float*>(rec + i * row_bytes);
+            if (lc < DK)
+                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
+            else if (lc < 2 * DK)
+                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
+            else if (lc < NLC)
+                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sv + i * BV + wbase - 2 * DK));
+        }
+    }
+    // Every small input is taken (waited for) here, before the state's loads
+    // are issued: a use after them would make the compiler wait for the
+    // whole state, since it cannot count through the replay loop above.
+    {
+        float exp_pin = exp_alog;
+        asm volatile("" : "+v"(exp_pin), "+v"(pa), "+v"(pb), "+v"(ra), "+v"(rb), "+v"(xw0), "+v"(xw1), "+v"(xw2));
+        asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) asm volatile("" : "+v"(xp[tt]));
+        exp_alog_v = exp_pin;
+    }
+    asm volatile("" ::: "memory");  // the state's loads are issued after all of the above
 
-    // the state last: loads complete in order, so the candidates' conv inputs
-    // above are usable while the state is still in flight
     float s[CPL][R];
     load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
 
-    // ---- one-page: replay rows 0..acc of the live record, store the checkpoint
-    if (LAYOUT == GDN_SPEC_ONEPAGE) {
-        if (n_replay > 0) {
-            // The replayed rows go straight into the LDS rows, all in flight at
-            // once: lane l of a wave lands at base + 4 l, and each region's base
-            // is chosen so that lane lc writes its own channel's slot.
-            const uint8_t* rec = pg + A.record_off + (int64_t)L * rows_per_slot * row_bytes;
-            const int wbase = tid & ~63;
-            for (int i = 0; i < n_replay; ++i) {
-                const float* row = reinterpret_cast<const float*>(rec + i * row_bytes);
-                if (lc < DK)
-                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
-                else if (lc < 2 * DK)
-                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
-                else if (lc < NLC)
-                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sv + i * BV + wbase - 2 * DK));
+    // ---- candidates: conv (+ record) into rows crow.., then gating
+    const bool qk_writer = (h == ki * rr) && (blk == 0);
+    uint8_t* recw = pg + A.record_off + (int64_t)(1 - L) * rows_per_slot * row_bytes;
+    auto cand_conv = [&]() {
+        if (gc >= 0) {
+            if (nc > 0) {
+                const bool rec_this = (LAYOUT == GDN_SPEC_ONEPAGE) && (lc >= 2 * DK || qk_writer);
+                float x3 = xw0, x2 = xw1, x1 = xw2;
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) {
+                    if (tt < nc) {
+                        const float x0 = xp[tt];
+                        const float y = silu_hw(conv4(w, x3, x2, x1, x0));
+                        ydst[(crow + tt) * yld] = y;
+                        if (rec_this) reinterpret_cast<float*>(recw + tt * row_bytes)[gc] = y;
+                        x3 = x2; x2 = x1; x1 = x0;
+                    }
+                }
+            } else {
+                // commit only: consume the window loads before arriving
+                ydst[crow * yld] = xw0 + xw1 + xw2;
             }
-            wait_vmem();
-            lds_barrier();
-            if (gtok < n_replay) {
-                (void)gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
-                float eg, beta;
-                gate_scalars(ra, rb, exp_alog, dtb, eg, beta);
-                if ((lane & 15) == 0) {
-                    ssc[gtok * 4 + 0] = eg;
-                    ssc[gtok * 4 + 1] = beta;
+        }
+    };
+    // the gates of this thread's token row: a replayed row or a candidate
+    auto gates = [&](bool replay_rows, bool cand_rows) {
+        if (replay_rows && gtok < n_replay) {
+            (void)gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
+            float eg, beta;
+            gate_scalars(ra, rb, exp_alog, dtb, eg, beta);
+            if ((lane & 15) == 0) {
+                ssc[gtok * 4 + 0] = eg;
+                ssc[gtok * 4 + 1] = beta;
+            }
+        }
+        if (cand_rows && cidx >= 0 && cidx < nc) {
+            const float kq = gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
+            float eg, beta;
+            gate_scalars(pa, pb, exp_alog, dtb, eg, beta);
+            if ((lane & 15) == 0) {
+                ssc[gtok * 4 + 0] = eg;
+                ssc[gtok * 4 + 1] = beta;
+                ssc[gtok * 4 + 2] = kq;
+                if (LAYOUT == GDN_SPEC_ONEPAGE && blk == 0) {
+                    float* rrow = reinterpret_cast<float*>(recw + cidx * row_bytes);
+                    rrow[C + h] = pa;
+                    rrow[C + A.h_v + h] = pb;
                 }
             }
-            lds_barrier();
-            for (int tt = 0; tt < n_replay; ++tt) {
-                float k[R], v[CPL];
-                lds_rows<R>(sk + tt * DK, tid, k);
-                lds_cols<CPL>(sv + tt * BV, tid, v);
-                delta_update<R, CPL>(s, k, v, ssc[tt * 4 + 0], ssc[tt * 4 + 1]);
+        }
+    };
+    if (split) {
+        // Everything but the state has arrived once at most the state's R
+        // loads (one per row, issued last) are outstanding; the candidates'
+        // record stores come after this wait.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(R) : "memory");
+        cand_conv();
+        lds_barrier();
+        gates(true, nc > 0);
+        lds_barrier();
+    } else if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
+        wait_vmem();
+        lds_barrier();
+        gates(true, false);
+        lds_barrier();
+    }
+
+    // ---- one-page: replay rows 0..acc of the live record, store the checkpoint
+    if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
+        // two rows per trip with two operand sets, each set's LDS reads
+        // issued one row ahead of its use
+        struct ROpnd { float k[R], v[CPL], eg, beta; };
+        auto roperands = [&](ROpnd& p, int tt) {
+            lds_rows<R>(sk + tt * DK, tid, p.k);
+            lds_cols<CPL>(sv + tt * BV, tid, p.v);
+            p.eg = ssc[tt * 4 + 0];
+            p.beta = ssc[tt * 4 + 1];
+        };
+        ROpnd r0, r1;
+        roperands(r0, 0);
+        for (int tt = 0; tt < n_replay; tt += 2) {
+            roperands(r1, tt + 1 < n_replay ? tt + 1 : tt);
+            delta_update<R, CPL>(s, r0.k, r0.v, r0.eg, r0.beta);
+            if (tt + 1 < n_replay) {
+                roperands(r0, tt + 2 < n_replay ? tt + 2 : tt + 1);
+                delta_update<R, CPL>(s, r1.k, r1.v, r1.eg, r1.beta);
             }
         }
     }
@@ -214,56 +302,32 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
             for (int m = 0; m < R; ++m) s[c][m] = round_as<StT>(s[c][m]);
     }
 
-    // ---- candidates: conv (+ record), gating, recurrence
-    const bool qk_writer = (h == ki * rr) && (blk == 0);
-    uint8_t* recw = pg + A.record_off + (int64_t)(1 - L) * rows_per_slot * row_bytes;
-    if (gc >= 0) {
-        if (nc > 0) {
-            const bool rec_this = (LAYOUT == GDN_SPEC_ONEPAGE) && (lc >= 2 * DK || qk_writer);
-            float x3 = xw0, x2 = xw1, x1 = xw2;
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                if (tt < nc) {
-                    const float x0 = xp[tt];
-                    const float y = silu_hw(conv4(w, x3, x2, x1, x0));
-                    ydst[tt * yld] = y;
-                    if (rec_this) reinterpret_cast<float*>(recw + tt * row_bytes)[gc] = y;
-                    x3 = x2; x2 = x1; x1 = x0;
-                }
-            }
-        } else {
-            // commit only: consume the window loads before arriving
-            ydst[0] = xw0 + xw1 + xw2;
-        }
-    }
-    lds_barrier();
-    if (nc > 0) {
-        if (gtok < nc) {
-            const float kq = gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
-            float eg, beta;
-            gate_scalars(pa, pb, exp_alog, dtb, eg, beta);
-            if ((lane & 15) == 0) {
-                ssc[gtok * 4 + 0] = eg;
-                ssc[gtok * 4 + 1] = beta;
-                ssc[gtok * 4 + 2] = kq;
-                if (LAYOUT == GDN_SPEC_ONEPAGE && blk == 0) {
-                    float* rrow = reinterpret_cast<float*>(recw + gtok * row_bytes);
-                    rrow[C + h] = pa;
-                    rrow[C + A.h_v + h] = pb;
-                }
-            }
-        }
+    if (!split) {
+        cand_conv();
         lds_barrier();
+        if (nc > 0) gates(false, true);
+        lds_barrier();
+    }
+    if (nc > 0) {
         const int cg = lane_colgroup(tid);
         const bool writer = lane_rowgroup(tid) == 0;
         float* __restrict__ O = A.o + (int64_t)req * nc * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + cg * CPL;
         const int64_t o_stride = (int64_t)A.h_v * A.d_v;
-        for (int tt = 0; tt < nc; ++tt) {
-            float k[R], q[R], v[CPL], o[CPL];
-            lds_rows<R>(sk + tt * DK, tid, k);
-            lds_rows<R>(sq + tt * DK, tid, q);
-            lds_cols<CPL>(sv + tt * BV, tid, v);
-            delta_step<R, CPL>(s, k, q, v, ssc[tt * 4 + 0], ssc[tt * 4 + 1], ssc[tt * 4 + 2], o);
+        // two tokens per trip with two operand sets, each set's LDS reads
+        // issued one token ahead of its use
+        struct Opnd { float k[R], q[R], v[CPL], eg, beta, kq; };
+        auto operands = [&](Opnd& p, int tt) {
+            const int r = crow + tt;
+            lds_rows<R>(sk + r * DK, tid, p.k);
+            lds_rows<R>(sq + r * DK, tid, p.q);
+            lds_cols<CPL>(sv + r * BV, tid, p.v);
+            p.eg = ssc[r * 4 + 0];
+            p.beta = ssc[r * 4 + 1];
+            p.kq = ssc[r * 4 + 2];
+        };
+        auto step = [&](const Opnd& p, int tt) {
+            float o[CPL];
+            delta_step<R, CPL>(s, p.k, p.q, p.v, p.eg, p.beta, p.kq, o);
             if (writer) {
                 float* dst = O + (int64_t)tt * o_stride;
                 if constexpr (CPL == 4) {
@@ -276,6 +340,16 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A
             if (LAYOUT == GDN_SPEC_SLOTS)
                 store_state<StT, DK, CPL>(st_base + ((int64_t)tt * A.h_v + h) * head_elems + colbase, A.d_v, s,
                                           tid);
+        };
+        Opnd p0, p1;
+        operands(p0, 0);
+        for (int tt = 0; tt < nc; tt += 2) {
+            operands(p1, tt + 1 < nc ? tt + 1 : tt);
+            step(p0, tt);
+            if (tt + 1 < nc) {
+                operands(p0, tt + 2 < nc ? tt + 2 : tt + 1);
+                step(p1, tt + 1);
+            }
         }
     } else if (LAYOUT == GDN_SPEC_SLOTS) {
         store_state<StT, DK, CPL>(st_base + (int64_t)h * head_elems + colbase, A.d_v, s, tid);
