@@ -118,8 +118,12 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
 
     // ---- chunk inputs, loaded one chunk ahead
     float xp[TT];
-    float pa = 0.0f, pb = 0.0f;   // gate inputs of this row's token (tt = 4 wv + lane/16)
-    const int gtok = (wv << 2) + (lane >> 4);
+    // Threads NLC .. NLC+TT-1 hold no conv channel; thread NLC + tt takes the
+    // gate inputs of token tt and computes its gate scalars during the conv.
+    static_assert(NLC + TT <= BLOCK_THREADS, "a gate thread per token of a chunk");
+    float pa = 0.0f, pb = 0.0f;
+    const int gsel = tid - NLC;                // the token of this gate thread, if in 0..TT-1
+    const int gtok = (wv << 2) + (lane >> 4);  // the token row of this thread's 16-lane row
     // Loads are unconditional (row and channel clamped into range) so all of
     // them stay in flight together; values past the sequence are zeroed.
     const int64_t gcl = gc >= 0 ? gc : 0;
@@ -130,8 +134,8 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
             const float xv = to_f32(X[(int64_t)(r0 + t) * A.x_stride + gcl]);
             xp[tt] = (gc >= 0 && t0 + tt < T) ? xv : 0.0f;
         }
-        const bool ok = gtok < TT && t0 + gtok < T;
-        const int t = ok ? t0 + gtok : T - 1;
+        const bool ok = gsel >= 0 && gsel < TT && t0 + gsel < T;
+        const int t = ok ? t0 + gsel : T - 1;
         const int64_t row = (int64_t)(r0 + t) * A.ab_stride + h;
         const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
         const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
@@ -180,6 +184,11 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
                     xm1 = x0;
                 }
             }
+        } else if (gsel >= 0 && gsel < nt) {
+            float eg, beta;
+            gate_scalars(pa, pb, exp_alog, dtb, eg, beta);
+            ssc[gsel * 4 + 0] = eg;
+            ssc[gsel * 4 + 1] = beta;
         }
         lds_barrier();
         if (t0 == 0 && tid == 0)  // every window read of this workgroup has been consumed
@@ -187,13 +196,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
         // A2: gating, one 16-lane row per token
         if (gtok < nt) {
             const float kq = gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
-            float eg, beta;
-            gate_scalars(pa, pb, exp_alog, dtb, eg, beta);
-            if ((lane & 15) == 0) {
-                ssc[gtok * 4 + 0] = eg;
-                ssc[gtok * 4 + 1] = beta;
-                ssc[gtok * 4 + 2] = kq;
-            }
+            if ((lane & 15) == 0) ssc[gtok * 4 + 2] = kq;
         }
         lds_barrier();
         if (t0 + TT < T) prefetch(t0 + TT);
@@ -274,6 +277,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
     constexpr int SL = LDS_ELEM_SLOT;      // bytes per lane slot of a staged element
     using Stage = StateStage<StT, DK, CPL>;
     static_assert(NLC <= BLOCK_THREADS && NLC % 64 == 0, "whole waves of conv channels");
+    static_assert(NLC <= 7 * 64, "wave 7 holds no conv channel: it takes the gate scalars");
     // Staged small inputs: fields of NLC slots (taps 0..3, window rows 0..2,
     // x), then 64 slots each of a and b for wave 0.
     constexpr int F_TAP = 0, F_WIN = 4, F_X = 7, N_CH_FIELDS = 8;
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
                 }
                 x0 = staged(F_X);
             }
-            if (wv == 0) {
+            if (wv == 7) {  // the gate scalars' wave (it holds no conv channel)
                 pa = to_f32(*reinterpret_cast<const ActT*>(sin + AB_OFF + lane * SL));
                 pb = to_f32(*reinterpret_cast<const ActT*>(sin + AB_OFF + (64 + lane) * SL));
             }
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
                 if (t > 0) {  // later tokens of a longer item: plain loads
                     const int64_t row = (int64_t)(cur.r0 + t);
                     if (has_ch) x0 = to_f32(X[row * A.x_stride + gc]);
-                    if (wv == 0) {
+                    if (wv == 7) {
                         pa = to_f32(Ag[row * A.ab_stride + cur.h]);
                         pb = to_f32(Bg[row * A.ab_stride + cur.h]);
                     }
@@ -459,18 +463,20 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
                     xm2 = xm1;
                     xm1 = x0;
                 }
+                if (wv == 7) {  // the gate scalars alongside the conv
+                    float eg, beta;
+                    gate_scalars(pa, pb, exp_alog, cur.dt_bias, eg, beta);
+                    if (lane == 0) {
+                        ssc[0] = eg;
+                        ssc[1] = beta;
+                    }
+                }
                 lds_barrier();
                 if (t == 0 && tid == 0)  // every window read of this item has been consumed
                     arrived_before = arrive(sync);
                 if (tid < 16) {
                     const float kq = gate_qk<DK>(sq, sk, A.scale, A.eps, tid);
-                    float eg, beta;
-                    gate_scalars(pa, pb, exp_alog, cur.dt_bias, eg, beta);
-                    if (tid == 0) {
-                        ssc[0] = eg;
-                        ssc[1] = beta;
-                        ssc[2] = kq;
-                    }
+                    if (tid == 0) ssc[2] = kq;
                 }
                 lds_barrier();
                 {
