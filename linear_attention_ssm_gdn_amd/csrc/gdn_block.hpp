@@ -246,8 +246,8 @@ __device__ __forceinline__ float gate_qk(float* qrow, float* krow, float scale, 
     }
     sq = reduce16(sq);
     sk = reduce16(sk);
-    const float rq = scale / sqrtf(sq + eps);
-    const float rk = 1.0f / sqrtf(sk + eps);
+    const float rq = scale * __builtin_amdgcn_rsqf(sq + eps);  // hardware 1/sqrt, about one ulp
+    const float rk = __builtin_amdgcn_rsqf(sk + eps);
     float kq = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {

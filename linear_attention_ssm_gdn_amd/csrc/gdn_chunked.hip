@@ -187,7 +187,32 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     const int blk = bid % nblk;
     bid /= nblk;
     const int h = bid % A.h_v;
-    const int seq = bid / A.h_v;
+    // Dispatch order: with more workgroups than stay resident (one per CU),
+    // index v takes the v-th longest sequence (ties by position), so the
+    // longest sequences start first.  Batches of up to one sequence per
+    // thread are ranked; larger ones keep their order.
+    int seq = bid / A.h_v;
+    if (A.n_seqs > 1 && A.n_seqs <= NTH) {
+        int* len = reinterpret_cast<int*>(lds + OFF_SC);  // free until the first chunk's gates
+        const int n = A.n_seqs, tid0 = threadIdx.x;
+        int my = 0;
+        if (tid0 < n) {
+            my = A.cu[tid0 + 1] - A.cu[tid0];
+            len[tid0] = my;
+        }
+        __syncthreads();
+        if (tid0 < n) {
+            int rank = 0;
+            for (int j = 0; j < n; ++j) {
+                const int lj = len[j];
+                rank += (lj > my || (lj == my && j < tid0)) ? 1 : 0;
+            }
+            if (rank == seq) sh_last = tid0;
+        }
+        __syncthreads();
+        seq = sh_last;
+        __syncthreads();  // sh_last is reused at the end
+    }
     const int rr = A.h_v / A.h_k;
     const int ki = h / rr;
     const int colbase = blk * BVC;
