@@ -194,20 +194,20 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     int seq = bid / A.h_v;
     if (A.n_seqs > 1 && A.n_seqs <= NTH) {
         int* len = reinterpret_cast<int*>(lds + OFF_SC);  // free until the first chunk's gates
-        const int n = A.n_seqs, tid0 = threadIdx.x;
+        const int n = A.n_seqs;
         int my = 0;
-        if (tid0 < n) {
-            my = A.cu[tid0 + 1] - A.cu[tid0];
-            len[tid0] = my;
+        if (tid < n) {
+            my = A.cu[tid + 1] - A.cu[tid];
+            len[tid] = my;
         }
         __syncthreads();
-        if (tid0 < n) {
+        if (tid < n) {
             int rank = 0;
             for (int j = 0; j < n; ++j) {
                 const int lj = len[j];
-                rank += (lj > my || (lj == my && j < tid0)) ? 1 : 0;
+                rank += (lj > my || (lj == my && j < tid)) ? 1 : 0;
             }
-            if (rank == seq) sh_last = tid0;
+            if (rank == seq) sh_last = tid;
         }
         __syncthreads();
         seq = sh_last;
