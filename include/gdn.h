@@ -37,9 +37,12 @@
  *   into *err when err is not NULL.
  * - conv-window sync words: sequences whose workgroups share conv channels
  *   hand the rolled window to the last workgroup to finish reading it, which
- *   counts arrivals in gdn_conv_pool.sync.  The words must be zero before the
- *   first call and every call leaves them zero when its kernels complete;
- *   a call aborted midway must be followed by re-zeroing them.
+ *   counts arrivals in gdn_conv_pool.sync.  One more word after the
+ *   n_pages * h_k arrival counters is the work counter from which the
+ *   short-sequence (decode) kernel of gdn_recurrent_seq hands out items.
+ *   The words must be zero before the first call and every call leaves them
+ *   zero when its kernels complete; a call aborted midway must be followed
+ *   by re-zeroing them.
  * - Calls that touch the same pages must be ordered (same stream, or events).
  */
 #ifndef GDN_H
@@ -109,7 +112,7 @@ typedef struct gdn_conv_pool {
     int64_t page_stride;   /* elements, >= rows * C_conv */
     int32_t rows;          /* >= conv_w - 1 (verify: >= conv_w - 1 + n_spec) */
     int32_t n_pages;
-    uint32_t* sync;        /* [n_pages][h_k] arrival counters, zero between calls */
+    uint32_t* sync;        /* [n_pages][h_k] arrival counters + 1 work counter, zero between calls */
 } gdn_conv_pool;
 
 /* Recurrent states: page p, head h at base + p*page_stride + h*d_k*d_v

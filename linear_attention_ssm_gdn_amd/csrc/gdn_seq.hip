@@ -393,10 +393,20 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
 
     // In the iteration that processes item i the workgroup also issues item
     // i+1's loads and resolves item i+2's metadata, under the wait for those
-    // loads.
+    // loads.  Workgroup b takes items b, b+g and b+2g; when there are more,
+    // the rest are handed out from the work counter that follows the
+    // arrival counters: a workgroup claims item i+3 in the iteration of item
+    // i (the claim returns under the same wait), so workgroups whose loads
+    // are served faster take more items.  Each workgroup makes exactly one
+    // claim past the end; the maker of the last claim of all returns the
+    // counter to zero.
     const int g = gridDim.x;
     auto clamp_item = [&](int64_t j) -> int { return j < n_items ? (int)j : n_items; };
+    const bool dyn = (int64_t)n_items > 3 * (int64_t)g;
+    uint32_t* work = A.sync + (int64_t)A.conv_n_pages * A.h_k;
+    __shared__ int sh_claim;
     int cur_j = blockIdx.x, nxt_j = clamp_item((int64_t)blockIdx.x + g);
+    int nn_j = clamp_item((int64_t)blockIdx.x + 2 * (int64_t)g);
     Item cur{}, nxt{};
     bool cur_ok = cur_j < n_items && resolve(cur_j, cur);
     if (cur_ok) fetch(cur);
@@ -439,6 +449,11 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
             fetch(nxt);
         }
         pending = nxt_ok;
+        // ---- claim the item after item i+2 (issued after the loads above, so
+        // the wait for them covers its result)
+        const bool claiming = dyn && nn_j < n_items;
+        uint32_t claimed = 0;
+        if (claiming && tid == 0) claimed = fetch_add_late(work, 1u);
 
         // ---- the current item, one token at a time
         const int64_t gc = channel(cur);
@@ -494,16 +509,28 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
         }
 
         // ---- item i+2's metadata, under the wait for item i+1's loads
-        const int nn_j = clamp_item((int64_t)nxt_j + g);
         Item nn{};
         const bool nn_ok = nn_j < n_items && resolve(nn_j, nn);
 
-        if (cur_ok) {
-            // This wave's staged loads of the next item (and the arrival) have
-            // landed once this returns; the barrier below makes that true for
-            // every wave.
+        if (cur_ok || claiming) {
+            // This wave's staged loads of the next item (and the arrival and
+            // the claim) have landed once this returns; the barrier below
+            // makes that true for every wave.
             wait_vmem();
             pending = false;
+        }
+        if (tid == 0) {
+            int nnn_j = clamp_item((int64_t)nn_j + g);
+            if (dyn) {
+                nnn_j = n_items;
+                if (claiming) {
+                    asm volatile("" : "+v"(claimed) : : "memory");
+                    nnn_j = clamp_item(3 * (int64_t)g + claimed);
+                    if ((int64_t)claimed == (int64_t)n_items - 2 * (int64_t)g - 1)  // the last claim of all
+                        __hip_atomic_store(work, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            sh_claim = nnn_j;
         }
         // The arrival's result is taken here, on every path and before the
         // state stores are issued, so no wait covers the stores' acknowledgements.
@@ -528,6 +555,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
         nxt_j = nn_j;
         nxt = nn;
         nxt_ok = nn_ok;
+        nn_j = sh_claim;  // written before the barrier above; rewritten only after the next one
     }
 }
 

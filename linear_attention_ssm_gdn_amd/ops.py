@@ -92,12 +92,12 @@ class Batch:
 @dataclasses.dataclass
 class ConvPool:
     buf: torch.Tensor    # [n_pages][rows][C_conv], act dtype
-    sync: torch.Tensor   # [n_pages][h_k] int32, zero between calls
+    sync: torch.Tensor   # [n_pages * h_k + 1] int32: arrival counters, then the work counter; zero between calls
 
     @staticmethod
     def alloc(dims: Dims, n_pages: int, rows: int, device) -> "ConvPool":
         return ConvPool(torch.zeros((n_pages, rows, dims.c_conv), dtype=dims.act_torch, device=device),
-                        torch.zeros((n_pages, dims.h_k), dtype=torch.int32, device=device))
+                        torch.zeros((n_pages * dims.h_k + 1,), dtype=torch.int32, device=device))
 
     def c(self) -> L.GdnConvPool:
         n, rows, C = self.buf.shape

@@ -38,6 +38,41 @@ def test_decode_parity(ora):
     _check(ora, wl, wk.make_sequence_inputs(wl))
 
 
+def test_decode_work_counter_repeated_steps(ora):
+    """The decode kernel hands out the items past each workgroup's first
+    three from the work counter that follows the conv pool's arrival words.
+    Three steps in a row on the same pools: each equals the oracle's step
+    from the previous step's device state and window, and every sync word,
+    the work counter included, is zero after each call.  Outputs are
+    compared normwise per head over the batch: a single token's 128-value
+    output slice can be thousands of times smaller than the head's typical
+    output (q nearly orthogonal to k under strong decay, where o is about
+    (k.q) beta v and k.q is itself a cancelling sum), and there a relative
+    error per slice measures fp32 rounding of the terms, not the kernel.
+    States are compared per (sequence, head) slice as everywhere else."""
+    g = gdn()
+    wl = wk.DECODE
+    base = wk.make_sequence_inputs(wl)
+    n = len(wl.seqlens)
+    dims, conv, state = seq_pools(wl, base, list(range(n)), n)
+    params = params_of(base, wl)
+    batch = make_batch(base["cu_seqlens"], list(range(n)), base["x"].shape[0])
+    for step in range(3):
+        fresh = wk.make_sequence_inputs(wl.replace(seed=wl.seed + 100 + step))
+        ref_inp = dict(base, x=fresh["x"], a=fresh["a"], b=fresh["b"],
+                       window0=host(conv.buf)[:, :wl.conv_w - 1], S0=host(state.buf))
+        x, a, b = (dev(fresh[k], dims.act_torch) for k in ("x", "a", "b"))
+        o = torch.full((x.shape[0], wl.h_v, wl.d_v), float("nan"), device=DEV)
+        g.gdn_recurrent_seq(dims, params, x, a, b, batch, conv, state, o=o)
+        torch.cuda.synchronize()
+        o_ref, win_ref, S_ref = oracle_seq(ora, wl, ref_inp)
+        oh = host(o)
+        assert max(rel(oh[:, h], o_ref[:, h]) for h in range(wl.h_v)) <= TOL, step
+        assert max_slice_rel_S(host(state.buf), S_ref) <= TOL, step
+        np.testing.assert_array_equal(host(conv.buf), win_ref)
+        assert int(conv.sync.abs().sum()) == 0, step
+
+
 def test_short_prefill_parity(ora):
     wl = wk.SHORT_PREFILL
     _check(ora, wl, wk.make_sequence_inputs(wl))
