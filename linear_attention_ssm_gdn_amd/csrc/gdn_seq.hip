@@ -118,11 +118,12 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
 
     // ---- chunk inputs, loaded one chunk ahead
     float xp[TT];
-    // Threads NLC .. NLC+TT-1 hold no conv channel; thread NLC + tt takes the
+    // The last wave holds no conv channel; its thread 64*7 + tt takes the
     // gate inputs of token tt and computes its gate scalars during the conv.
-    static_assert(NLC + TT <= BLOCK_THREADS, "a gate thread per token of a chunk");
+    constexpr int GATE0 = BLOCK_THREADS - 64;
+    static_assert(NLC <= GATE0 && TT <= 64, "a gate thread per token of a chunk, in a wave without conv channels");
     float pa = 0.0f, pb = 0.0f;
-    const int gsel = tid - NLC;                // the token of this gate thread, if in 0..TT-1
+    const int gsel = tid - GATE0;              // the token of this gate thread, if in 0..TT-1
     const int gtok = (wv << 2) + (lane >> 4);  // the token row of this thread's 16-lane row
     // Loads are unconditional (row and channel clamped into range) so all of
     // them stay in flight together; values past the sequence are zeroed.
