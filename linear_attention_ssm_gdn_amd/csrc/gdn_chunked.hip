@@ -77,6 +77,24 @@ static_assert(CH * LAF * 4 <= SZ_REG && CH * LQK * 2 <= SZ_REG, "region sizes");
 // scalar rows in the SC block
 enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
 
+// A vector instruction that reads a matrix-core result must not issue
+// within the product's write-back.  The compiler schedules such reads (or the
+// copies out of the accumulator registers) 8 wait states after a 16x16x32
+// product, and on this part those reads have returned stale values now and
+// then: outputs of identical launches differed in the first two accumulator
+// registers of some lanes, and 16 more wait states made every launch
+// bit-identical.  Every product chain whose result vector instructions read
+// ends with settle(): 16 wait states that take the accumulators as
+// accumulator-register operands, so they follow the last product that writes
+// them and precede every read or copy of them.
+#define GDN_SETTLE_NOPS "s_nop 7\n\ts_nop 7"
+__device__ __forceinline__ void settle(f32x4& a) { asm volatile(GDN_SETTLE_NOPS : "+a"(a)); }
+__device__ __forceinline__ void settle(f32x4& a, f32x4& b) { asm volatile(GDN_SETTLE_NOPS : "+a"(a), "+a"(b)); }
+__device__ __forceinline__ void settle8(f32x4 (&a)[8]) {
+    asm volatile(GDN_SETTLE_NOPS : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]),
+                 "+a"(a[6]), "+a"(a[7]));
+}
+
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
@@ -513,6 +531,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     aq = mma32(khn, ql, aq);
                     ak = mma32(khn, khm, ak);
                 }
+                settle(aq, ak);
                 accq[k] = aq; acck[k] = ak;
                 ++cnt;
             }
@@ -576,10 +595,12 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             f32x4 R = eye - nB;                    // running product, starts at I - N
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                const f32x4 Yn = mma16(to_bf4(Z), to_bf4(Y), zero);  // Y <- Y Y (A operand = layout of Y^T = Z)
-                const f32x4 Zn = mma16(to_bf4(Y), to_bf4(Z), zero);  // Z <- Z Z
+                f32x4 Yn = mma16(to_bf4(Z), to_bf4(Y), zero);  // Y <- Y Y (A operand = layout of Y^T = Z)
+                f32x4 Zn = mma16(to_bf4(Y), to_bf4(Z), zero);  // Z <- Z Z
+                settle(Yn, Zn);
                 Y = Yn; Z = Zn;
                 R = mma16(to_bf4(eye + Z), to_bf4(R), zero);         // R <- (I + Y) R
+                settle(R);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * b + lr] = (__bf16)R[j];
@@ -602,8 +623,10 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                                         Tm[(16 * d + 4 * lg + 3) * LT + 16 * c + lr]};
                     Xacc = mma16(aop, bop, Xacc);
                 }
+                settle(Xacc);
                 const bf16x4 tbb = ld4(Tm, LT, 16 * b + lr, 16 * b + 4 * lg);
-                const f32x4 Yv = mma16(tbb, to_bf4(Xacc), zero);
+                f32x4 Yv = mma16(tbb, to_bf4(Xacc), zero);
+                settle(Yv);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * c + lr] = (__bf16)(-Yv[j]);
             }
@@ -653,6 +676,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     wacc[k] = mma32(aop, bop, wacc[k]);
                 }
             }
+            settle8(wacc);
             // A (in the same region) is dead since the LT pass; W takes its place
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -692,6 +716,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 for (int kk = 0; kk < 4; ++kk)
                     ws = mma32(cat8(ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 4 * lg), ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 16 + 4 * lg)),
                                sb[kk], ws);
+                settle(u, ws);
                 D[mt] = u - ws;
             }
             bf16x4 dh[4], dl[4];
@@ -707,6 +732,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
                     qs = mma32(cat8(ld4(Qh, LQK, row, 32 * kk + 4 * lg), ld4(Qh, LQK, row, 32 * kk + 16 + 4 * lg)), sb[kk], qs);
+                settle(qs);
                 const int t0 = 16 * mt + 4 * lg;
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(sc + SC_GAM * CH + t0);
                 const f32x4 rq = *reinterpret_cast<const f32x4*>(sc + SC_RQ * CH + t0);
@@ -771,10 +797,14 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     acc = mma32(kh, wl2[kk], acc);
                     acc = mma32(kl, wh2[kk], acc);
                 }
+                s[dt] = acc;
+            }
+            settle8(s);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
                 const f32x4 kv = *reinterpret_cast<const f32x4*>(klast + 16 * dt + 4 * lg);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = fmaf(kv[j], dlast, acc[j]);
-                s[dt] = acc;
+                for (int j = 0; j < 4; ++j) s[dt][j] = fmaf(kv[j], dlast, s[dt][j]);
             }
         }
         lds_barrier();
