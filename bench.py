@@ -262,6 +262,81 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"repeated {n} times in {budget_s:.0f} s"}
 
 
+# ------------------------------------------------------ dispatch sweep
+SWEEP_SEQS = (1, 2, 4, 8, 16, 32)
+SWEEP_LENS = (16, 32, 64, 96, 128, 192, 256, 384, 512, 768, 1024, 2048, 4096, 8192)
+SWEEP_MAX_TOKENS = 32768
+
+
+class UniformBatch:
+    """n sequences of T tokens each, cut from one draw of the long-prefill
+    inputs (same shapes and value distributions); POOLS state/window copies."""
+
+    def __init__(self, g, torch, base, n, T):
+        self.g, self.torch = g, torch
+        d, x, a, b, S0, W0 = base
+        self.dims = d
+        N = n * T
+        cu = torch.arange(0, N + 1, T, dtype=torch.int32, device="cuda")
+        self.batch = g.Batch(cu, torch.arange(n, dtype=torch.int32, device="cuda"), None, T, N)
+        self.x, self.a, self.b = x[:N], a[:N], b[:N]
+        reps = (n + S0.shape[0] - 1) // S0.shape[0]
+        s0 = S0.repeat(reps, 1, 1, 1)[:n]
+        w0 = W0.repeat(reps, 1, 1)[:n]
+        self.sets = []
+        for _ in range(POOLS):
+            conv = g.ConvPool.alloc(d, n, 3, "cuda")
+            conv.buf.copy_(w0)
+            self.sets.append((conv, g.StatePool(s0.clone()),
+                              torch.empty((N, d.h_v, d.d_v), device="cuda")))
+        self.i = 0
+        self.chunk = 0
+
+    def launch(self):
+        conv, state, o = self.sets[self.i % POOLS]
+        self.i += 1
+        if self.chunk:
+            self.g.gdn_chunked_prefill(self.dims, self.params, self.x, self.a, self.b, self.batch, conv, state,
+                                       chunk=self.chunk, o=o)
+        else:
+            self.g.gdn_recurrent_seq(self.dims, self.params, self.x, self.a, self.b, self.batch, conv, state, o=o)
+
+
+def sweep_dispatch(g, torch, steps):
+    """Kernel time of the token-by-token and chunked paths over uniform
+    batches (n sequences x T tokens, n T <= SWEEP_MAX_TOKENS): one JSON line
+    per point, then the shortest length at which the chunked path wins for
+    each n."""
+    wl = wk.LONG_PREFILL
+    inp = wk.make_sequence_inputs(wl)
+    d = g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.conv_w, 0, wl.act_dtype, wl.state_dtype, wl.scale, wl.l2_eps)
+    params = g.Params(_upload(torch, inp["conv_w"], d.act_torch), _upload(torch, inp["a_log"], torch.float32),
+                      _upload(torch, inp["dt_bias"], torch.float32))
+    base = (d, _upload(torch, inp["x"], d.act_torch), _upload(torch, inp["a"], d.act_torch),
+            _upload(torch, inp["b"], d.act_torch), _upload(torch, inp["S0"], d.state_torch),
+            _upload(torch, inp["window0"], d.act_torch))
+    cross = {}
+    for n in SWEEP_SEQS:
+        for T in SWEEP_LENS:
+            if n * T > SWEEP_MAX_TOKENS:
+                continue
+            ub = UniformBatch(g, torch, base, n, T)
+            ub.params = params
+            ub.chunk = 0
+            seq_ms, _ = measure(torch, ub, steps, 3)
+            ub.chunk = wl.chunk
+            chk_ms, _ = measure(torch, ub, steps, 3)
+            line = {"n_seqs": n, "seqlen": T, "tokens": n * T, "us_token_by_token": round(seq_ms * 1e3, 2),
+                    "us_chunked": round(chk_ms * 1e3, 2), "faster": "chunked" if chk_ms < seq_ms else "token_by_token"}
+            print(json.dumps(line), flush=True)
+            if chk_ms < seq_ms and n not in cross:
+                cross[n] = T
+            del ub
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "dispatch", "chunk": wl.chunk,
+                      "first_length_where_chunked_wins": {str(k): v for k, v in cross.items()}}), flush=True)
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -270,6 +345,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="decode,short_prefill,long_prefill,spec_verify")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep-dispatch", action="store_true",
+                    help="time token-by-token vs chunked prefill over uniform batches instead of the benchmark")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run a plain 1 GiB device copy (the byte-counter calibration kernel)")
     args = ap.parse_args()
@@ -280,6 +357,9 @@ def main():
     import torch
     import linear_attention_ssm_gdn_amd as g
     g.load()
+    if args.sweep_dispatch:
+        sweep_dispatch(g, torch, max(args.steps // 20, 5))
+        return
     only = set(args.only.split(","))
     result = {"metric": METRIC}
     if args.copy_calib:

@@ -207,6 +207,43 @@ int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* params,
                             float* o, int32_t chunk, void* workspace, size_t ws_bytes,
                             int32_t* err, void* stream);
 
+/* ------------------------------------------- prefill path selection */
+
+/* Which of the two sequence paths a prefill batch takes ("r9700-stack
+ * v0.2.3", section "1. Time to first token": below a measured break-even
+ * the layer core runs token by token, above it in the chunked form). */
+#define GDN_PATH_TOKEN 0       /* gdn_recurrent_seq */
+#define GDN_PATH_CHUNKED 1     /* gdn_chunked_prefill, chunk 64 */
+#define GDN_PREFILL_MAX_DEFAULT (-1)
+
+/* The path gdn_prefill takes for this batch shape (host-only, nothing is
+ * launched).  Token by token while the longest sequence has at most
+ * `token_max` rows, chunked above.  token_max < 0 takes the library's
+ * default, the kernel-time break-even measured on MI355X over uniform
+ * batches at d_k = d_v = 128: 32 rows for batches of one or two sequences,
+ * 16 rows for more (past that the chunked form is faster at every length
+ * and batch size measured, 32 to 8192 rows and 1 to 32 sequences).  A large
+ * token_max keeps every batch on the token-by-token path (relative error
+ * 1e-4 against the exact recurrence, against 3e-3 for the bf16 matrix-core
+ * chunked form); 0 sends every non-empty batch to the chunked path.  The
+ * longest length is batch->max_seqlen, or batch->n_rows when that is 0.
+ * Head dims the chunked path is not compiled for always take the token path.
+ * *path (host) receives GDN_PATH_TOKEN or GDN_PATH_CHUNKED. */
+int32_t gdn_prefill_path(const gdn_dims* dims, const gdn_batch* batch, int32_t token_max, int32_t* path);
+
+/* Run the layer core over a prefill batch on the path gdn_prefill_path
+ * selects; the result is that of gdn_recurrent_seq or gdn_chunked_prefill
+ * (chunk 64) for the same arguments, bit for bit.  Arguments, layouts,
+ * ownership and errors are those of the selected entry point (the chunked
+ * path's 16-byte alignment rules apply only when it is selected); path
+ * (host, may be NULL) receives the path taken. */
+int32_t gdn_prefill(const gdn_dims* dims, const gdn_params* params,
+                    const void* x, int64_t x_stride,
+                    const void* a, const void* b, int64_t ab_stride,
+                    const gdn_batch* batch, gdn_conv_pool conv, gdn_state_pool state,
+                    float* o, int32_t token_max, void* workspace, size_t ws_bytes,
+                    int32_t* path, int32_t* err, void* stream);
+
 /* --------------------------------------------------- (d) spec verify */
 
 /* One speculative verify step over n_req requests ("r9700-stack v0.2.4",

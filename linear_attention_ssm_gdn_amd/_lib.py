@@ -18,9 +18,12 @@ GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_SPEC_ONEPAGE, GDN_SPEC_SLOTS = 0, 1
 GDN_DEVERR_PAGE, GDN_DEVERR_BATCH, GDN_DEVERR_ACCEPTED, GDN_DEVERR_PARITY = 1, 2, 4, 8
+GDN_PATH_TOKEN, GDN_PATH_CHUNKED = 0, 1
+GDN_PREFILL_MAX_DEFAULT = -1
 
 SYMBOLS = ("gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout", "gdn_chunked_workspace_bytes",
-           "gdn_conv_update", "gdn_recurrent_seq", "gdn_chunked_prefill", "gdn_spec_verify")
+           "gdn_conv_update", "gdn_recurrent_seq", "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill",
+           "gdn_spec_verify")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -92,6 +95,13 @@ def load() -> ctypes.CDLL:
     L.gdn_chunked_prefill.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _vp, _i64, _vp, _vp,
                                       _i64, ctypes.POINTER(GdnBatch), GdnConvPool, GdnStatePool, _vp, _i32,
                                       _vp, ctypes.c_size_t, _vp, _vp]
+    L.gdn_prefill_path.restype = _i32
+    L.gdn_prefill_path.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnBatch), _i32,
+                                   ctypes.POINTER(_i32)]
+    L.gdn_prefill.restype = _i32
+    L.gdn_prefill.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _vp, _i64, _vp, _vp, _i64,
+                              ctypes.POINTER(GdnBatch), GdnConvPool, GdnStatePool, _vp, _i32, _vp,
+                              ctypes.c_size_t, ctypes.POINTER(_i32), _vp, _vp]
     L.gdn_spec_verify.restype = _i32
     L.gdn_spec_verify.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _i32, _vp, _i64, _vp,
                                   _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, GdnConvPool, _vp,

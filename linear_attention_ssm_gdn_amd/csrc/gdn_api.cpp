@@ -197,6 +197,43 @@ GDN_EXPORT int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* p
     return from_hip(gdn::launch_chunked(A, dims->d_k, dims->act_dtype, dims->state_dtype, (hipStream_t)stream));
 }
 
+namespace {
+// Kernel-time break-even of the two sequence paths on MI355X (uniform
+// batches, d_k = d_v = 128, bf16 activations, fp32 state): token by token is
+// faster up to 16 rows per sequence, and up to 32 for one or two sequences,
+// where it ties; the chunked form is faster everywhere past that.
+constexpr int32_t kTokenMaxFew = 32;   // batches of 1-2 sequences
+constexpr int32_t kTokenMaxMany = 16;  // larger batches
+constexpr int32_t kPrefillChunk = 64;
+}  // namespace
+
+GDN_EXPORT int32_t gdn_prefill_path(const gdn_dims* dims, const gdn_batch* batch, int32_t token_max,
+                                    int32_t* path) {
+    int32_t st;
+    if ((st = check_dims(dims)) != GDN_OK) return st;
+    if ((st = check_batch(batch)) != GDN_OK) return st;
+    if (!path) return GDN_ERR_ARG;
+    const int64_t longest = batch->max_seqlen > 0 ? batch->max_seqlen : batch->n_rows;
+    const int64_t limit = token_max >= 0 ? token_max : (batch->n_seqs <= 2 ? kTokenMaxFew : kTokenMaxMany);
+    const bool chunked_ok = gdn::chunked_supported(dims->d_k, dims->d_v, kPrefillChunk);
+    *path = (chunked_ok && longest > limit) ? GDN_PATH_CHUNKED : GDN_PATH_TOKEN;
+    return GDN_OK;
+}
+
+GDN_EXPORT int32_t gdn_prefill(const gdn_dims* dims, const gdn_params* params, const void* x, int64_t x_stride,
+                               const void* a, const void* b, int64_t ab_stride, const gdn_batch* batch,
+                               gdn_conv_pool conv, gdn_state_pool state, float* o, int32_t token_max,
+                               void* workspace, size_t ws_bytes, int32_t* path, int32_t* err, void* stream) {
+    int32_t which = GDN_PATH_TOKEN;
+    const int32_t st = gdn_prefill_path(dims, batch, token_max, &which);
+    if (st != GDN_OK) return st;
+    if (path) *path = which;
+    if (which == GDN_PATH_CHUNKED)
+        return gdn_chunked_prefill(dims, params, x, x_stride, a, b, ab_stride, batch, conv, state, o, kPrefillChunk,
+                                   workspace, ws_bytes, err, stream);
+    return gdn_recurrent_seq(dims, params, x, x_stride, a, b, ab_stride, batch, conv, state, o, err, stream);
+}
+
 GDN_EXPORT int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* params, int32_t layout, const void* x,
                                    int64_t x_stride, const void* a, const void* b, int64_t ab_stride, int32_t n_req,
                                    int32_t n_cand, const int32_t* req_page, const int32_t* num_accepted,

@@ -198,6 +198,37 @@ def gdn_chunked_prefill(dims: Dims, params: Params, x: torch.Tensor, a: torch.Te
     return o
 
 
+def gdn_prefill_path(dims: Dims, batch: Batch, token_max: int = L.GDN_PREFILL_MAX_DEFAULT) -> int:
+    out = ctypes.c_int32(-1)
+    d, bt = dims.c(), batch.c()
+    _check("gdn_prefill_path", L.load().gdn_prefill_path(ctypes.byref(d), ctypes.byref(bt), token_max,
+                                                         ctypes.byref(out)))
+    return int(out.value)
+
+
+def gdn_prefill(dims: Dims, params: Params, x: torch.Tensor, a: torch.Tensor, b: torch.Tensor, batch: Batch,
+                conv: ConvPool, state: StatePool, token_max: int = L.GDN_PREFILL_MAX_DEFAULT,
+                o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                err: Optional[torch.Tensor] = None):
+    """Returns (o, path): path is GDN_PATH_TOKEN or GDN_PATH_CHUNKED."""
+    if o is None:
+        o = torch.empty((batch.n_rows, dims.h_v, dims.d_v), dtype=torch.float32, device=x.device)
+    if a.stride() != b.stride():
+        raise ValueError("a and b must share their row stride")
+    if workspace is None:
+        need = gdn_chunked_workspace_bytes(dims, batch.n_seqs, batch.n_rows, 64)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    path = ctypes.c_int32(-1)
+    d, p, bt = dims.c(), params.c(), batch.c()
+    st = L.load().gdn_prefill(ctypes.byref(d), ctypes.byref(p), x.data_ptr(), _rows(x, "x"), a.data_ptr(),
+                              b.data_ptr(), _rows(a, "a"), ctypes.byref(bt), conv.c(), state.c(), o.data_ptr(),
+                              token_max, _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                              ctypes.byref(path), _ptr(err), _stream(x))
+    _check("gdn_prefill", st)
+    return o, int(path.value)
+
+
 @dataclasses.dataclass
 class SpecPages:
     """Speculative pages: raw bytes [n_pages][page_bytes] laid out by

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
     assert set(names) == {"gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout",
                           "gdn_chunked_workspace_bytes", "gdn_conv_update", "gdn_recurrent_seq",
-                          "gdn_chunked_prefill", "gdn_spec_verify"}
+                          "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill", "gdn_spec_verify"}
     for n in names:
         assert hasattr(so, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "linear_attention_ssm_gdn_amd",
@@ -182,6 +182,60 @@ def test_chunked_validation(so, L):
     out = ctypes.c_size_t(123)
     assert so.gdn_chunked_workspace_bytes(ctypes.byref(d), 4, 32768, 64, ctypes.byref(out)) == 0
     assert out.value == 0
+
+
+def test_prefill_path_selection(so, L):
+    """Host-side choice between the token-by-token and chunked paths: the
+    measured default break-even (32 rows for one or two sequences, 16 for
+    more), an explicit token_max, max_seqlen unknown (n_rows stands in), and
+    head dims the chunked kernel is not compiled for."""
+    def path(dims, n_seqs, max_seqlen, token_max=-1, n_rows=None):
+        b = L.GdnBatch(FAKE, FAKE, None, n_seqs, max_seqlen, n_rows if n_rows is not None else n_seqs * max_seqlen)
+        out = ctypes.c_int32(-7)
+        assert so.gdn_prefill_path(ctypes.byref(dims), ctypes.byref(b), token_max, ctypes.byref(out)) == 0
+        return out.value
+    d = _dims(L)
+    T, K = L.GDN_PATH_TOKEN, L.GDN_PATH_CHUNKED
+    for n in (1, 2):
+        assert path(d, n, 1) == T and path(d, n, 32) == T and path(d, n, 33) == K
+    for n in (3, 8, 64):
+        assert path(d, n, 16) == T and path(d, n, 17) == K and path(d, n, 8192) == K
+    assert path(d, 8, 4096, token_max=2 ** 31 - 1) == T
+    assert path(d, 1, 1, token_max=0) == K
+    assert path(d, 1, 100, token_max=100) == T and path(d, 1, 101, token_max=100) == K
+    assert path(d, 4, 0, n_rows=40) == K and path(d, 4, 0, n_rows=16) == T
+    assert path(d, 0, 0, n_rows=0) == T
+    assert path(_dims(L, d_k=64), 1, 4096) == T        # no chunked kernel for d_k = 64
+    assert path(_dims(L, d_v=96), 1, 4096) == T        # nor for d_v % 64 != 0
+    b = L.GdnBatch(FAKE, FAKE, None, 1, 8, 8)
+    assert so.gdn_prefill_path(ctypes.byref(d), ctypes.byref(b), -1, None) == 1
+    assert so.gdn_prefill_path(ctypes.byref(_dims(L, conv_w=3)), ctypes.byref(b), -1,
+                               ctypes.byref(ctypes.c_int32())) == 2
+
+
+def test_prefill_validation(so, L):
+    """gdn_prefill validates as the path it selects: the chunked path's
+    16-byte alignment applies only to batches that take it."""
+    d = _dims(L)
+    a = _seq_args(L, d)
+
+    def call(max_seqlen, x=a["x"], token_max=-1, params=a["params"]):
+        b = L.GdnBatch(FAKE, FAKE, None, 2, max_seqlen, 2 * max_seqlen)
+        p = ctypes.c_int32(-7)
+        st = so.gdn_prefill(ctypes.byref(d), ctypes.byref(params) if params is not None else None, x,
+                            a["x_stride"], a["a"], a["b"], a["ab_stride"], ctypes.byref(b), a["conv"], a["state"],
+                            a["o"], token_max, None, 0, ctypes.byref(p), None, None)
+        return st, p.value
+    assert call(4096, x=FAKE + 2)[0] == 1                     # chunked: x must be 16-byte aligned
+    assert call(4096, x=None)[0] == 1
+    assert call(8, params=None)[0] == 1
+    assert call(4096, x=None, token_max=2 ** 31 - 1)[0] == 1       # token path: its own checks
+    b0 = L.GdnBatch(None, None, None, 0, 0, 0)
+    p = ctypes.c_int32(-7)
+    assert so.gdn_prefill(ctypes.byref(d), ctypes.byref(a["params"]), None, a["x_stride"], None, None,
+                          a["ab_stride"], ctypes.byref(b0), a["conv"], a["state"], None, -1, None, 0,
+                          ctypes.byref(p), None, None) == 0
+    assert p.value == L.GDN_PATH_TOKEN
 
 
 def test_verify_validation(so, L):
