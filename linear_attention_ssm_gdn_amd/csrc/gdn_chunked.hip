@@ -90,6 +90,9 @@ enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
 #define GDN_SETTLE_NOPS "s_nop 7\n\ts_nop 7"
 __device__ __forceinline__ void settle(f32x4& a) { asm volatile(GDN_SETTLE_NOPS : "+a"(a)); }
 __device__ __forceinline__ void settle(f32x4& a, f32x4& b) { asm volatile(GDN_SETTLE_NOPS : "+a"(a), "+a"(b)); }
+__device__ __forceinline__ void settle4(f32x4 (&a)[4]) {
+    asm volatile(GDN_SETTLE_NOPS : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+}
 __device__ __forceinline__ void settle8(f32x4 (&a)[8]) {
     asm volatile(GDN_SETTLE_NOPS : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]),
                  "+a"(a[6]), "+a"(a[7]));
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     __bf16* Tm = reinterpret_cast<__bf16*>(lds + OFF_KH);                  // after P3
     __bf16* LTbg = reinterpret_cast<__bf16*>(lds + OFF_KH + CH * LT * 2);  // after P4
     __bf16* LTb = reinterpret_cast<__bf16*>(lds + OFF_KL);                 // after P4
-    __bf16* Wm = reinterpret_cast<__bf16*>(lds + OFF_QL);                  // after P5
+    __bf16* Wm = reinterpret_cast<__bf16*>(lds + OFF_QL);                  // -W, after P5
     float* Os = reinterpret_cast<float*>(lds + OFF_PH);                    // from P6's end to the next P3
     float* sc = reinterpret_cast<float*>(lds + OFF_SC);
     float* klast = reinterpret_cast<float*>(lds + OFF_KLAST);
@@ -682,7 +685,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             for (int k = 0; k < 8; ++k) {
                 const int idx = wv + 4 * k, mt = idx >> 3, dt = idx & 7;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Wm[(16 * mt + 4 * lg + j) * LQK + 16 * dt + lr] = (__bf16)wacc[k][j];
+                for (int j = 0; j < 4; ++j) Wm[(16 * mt + 4 * lg + j) * LQK + 16 * dt + lr] = (__bf16)(-wacc[k][j]);
             }
         }
         lds_barrier();
@@ -700,7 +703,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             f32x4 D[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                // U = beta V + LTb V
+                // D = U - W S = beta V + LTb V + (-W) S, one accumulator chain
                 const int t0 = 16 * mt + 4 * lg;
                 const bf16x4 vh = ld4(VTh, LT, colv, t0), vl = ld4(VTl, LT, colv, t0);
                 const f32x4 bt = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + t0);
@@ -710,36 +713,40 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
                     u = mma32(ld8(LTb, LT, 16 * mt + lr, 32 * ks + 8 * lg), ld8(VTh, LT, colv, 32 * ks + 8 * lg), u);
-                // W S
-                f32x4 ws = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    ws = mma32(cat8(ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 4 * lg), ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 16 + 4 * lg)),
-                               sb[kk], ws);
-                settle(u, ws);
-                D[mt] = u - ws;
+                    u = mma32(cat8(ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 4 * lg), ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 16 + 4 * lg)),
+                              sb[kk], u);
+                D[mt] = u;
             }
+            settle4(D);
             bf16x4 dh[4], dl[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) split4(D[mt], dh[mt], dl[mt]);
             // O = diag(e^G rq) Q S + diag(k.q) D + P D  (P is lower triangular by
             // 16-blocks: block pairs below the diagonal, then the diagonal block
             // alone where it starts a pair)
+            f32x4 qs[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const int row = 16 * mt + lr;
-                f32x4 qs = {0.0f, 0.0f, 0.0f, 0.0f};
+                qs[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    qs = mma32(cat8(ld4(Qh, LQK, row, 32 * kk + 4 * lg), ld4(Qh, LQK, row, 32 * kk + 16 + 4 * lg)), sb[kk], qs);
-                settle(qs);
+                    qs[mt] = mma32(cat8(ld4(Qh, LQK, row, 32 * kk + 4 * lg), ld4(Qh, LQK, row, 32 * kk + 16 + 4 * lg)),
+                                   sb[kk], qs[mt]);
+            }
+            settle4(qs);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int row = 16 * mt + lr;
                 const int t0 = 16 * mt + 4 * lg;
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(sc + SC_GAM * CH + t0);
                 const f32x4 rq = *reinterpret_cast<const f32x4*>(sc + SC_RQ * CH + t0);
                 const f32x4 kq = *reinterpret_cast<const f32x4*>(sc + SC_KQ * CH + t0);
                 f32x4 o;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) o[j] = gm[j] * rq[j] * qs[j] + kq[j] * D[mt][j];
+                for (int j = 0; j < 4; ++j) o[j] = gm[j] * rq[j] * qs[mt][j] + kq[j] * D[mt][j];
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (2 * kk + 1 > mt) continue;
