@@ -83,11 +83,14 @@ enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
 // product, and on this part those reads have returned stale values now and
 // then: outputs of identical launches differed in the first two accumulator
 // registers of some lanes, and 16 more wait states made every launch
-// bit-identical.  Every product chain whose result vector instructions read
-// ends with settle(): 16 wait states that take the accumulators as
-// accumulator-register operands, so they follow the last product that writes
-// them and precede every read or copy of them.
-#define GDN_SETTLE_NOPS "s_nop 7\n\ts_nop 7"
+// bit-identical, while a rarer mismatch remained (about one launch in a
+// few hundred); the wait is 32 wait states.  Every product chain whose result
+// vector instructions read ends with settle(): the wait states take the
+// accumulators as accumulator-register operands, so they follow the last
+// product that writes them and precede every read or copy of them.  The one
+// chain that feeds a 16x16x32 result into 16x16x16 products (different pass
+// counts) settles in between as well.
+#define GDN_SETTLE_NOPS "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
 __device__ __forceinline__ void settle(f32x4& a) { asm volatile(GDN_SETTLE_NOPS : "+a"(a)); }
 __device__ __forceinline__ void settle(f32x4& a, f32x4& b) { asm volatile(GDN_SETTLE_NOPS : "+a"(a), "+a"(b)); }
 __device__ __forceinline__ void settle4(f32x4 (&a)[4]) {
@@ -758,6 +761,7 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                     o = mma32(pl, bh, o);
                 }
                 if ((mt & 1) == 0) {
+                    if (mt > 0) settle(o);
                     const bf16x4 ph = ld4(Ph, LT, row, 16 * mt + 4 * lg);
                     const bf16x4 pl = ld4(Pl, LT, row, 16 * mt + 4 * lg);
                     o = mma16(ph, dh[mt], o);
