@@ -12,7 +12,7 @@ the timed region starts.  State/input pools rotate every step so that the
 working set (>= 512 MiB) cannot sit in the 256 MB last-level cache.  Kernel
 time is taken with HIP events on the stream the kernels are launched on.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,...]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,...] [--sweep-dispatch]
 """
 from __future__ import annotations
 
@@ -202,6 +202,41 @@ class VerifyWorkload:
         st[3] = n + 1
 
 
+class MixedWorkload:
+    """A serving step mixing the short ragged prefill batch with the verify
+    batch (32 requests x 8 candidates, fp32 state): one gdn_mixed_step launch
+    (fused) or gdn_recurrent_seq then gdn_spec_verify (separate).  Both
+    parts use the verify workload's parameters, so the two forms compute the
+    same step."""
+
+    def __init__(self, g, torch, seq_wl=wk.SHORT_PREFILL, ver_wl=wk.SPEC_VERIFY):
+        self.g = g
+        self.seq = SeqWorkload(g, torch, seq_wl)
+        self.ver = VerifyWorkload(g, torch, ver_wl, wk.F32)
+        self.fused = True
+
+    def launch(self):
+        g, sw, vw = self.g, self.seq, self.ver
+        x, a, b, conv, state, o = sw.sets[sw.i % POOLS]
+        sw.i += 1
+        st = vw.sets[vw.i % POOLS]
+        vw.i += 1
+        pages, vconv, vo, n = st
+        s = n % vw.wl.n_steps
+        acc = vw.acc[(n - 1) % vw.wl.n_steps] if n > 0 else vw.acc[0] * 0
+        par = vw.par[(n + 1) & 1]
+        if self.fused:
+            g.gdn_mixed_step(vw.dims, vw.params, seq=dict(x=x, a=a, b=b, batch=sw.batch, conv=conv, state=state, o=o),
+                             verify=dict(pages=pages, x=vw.x[s], a=vw.a[s], b=vw.b[s], n_req=vw.wl.n_req,
+                                         n_cand=vw.wl.n_cand, req_page=vw.rp, num_accepted=acc, step_parity=par,
+                                         conv=vconv, o=vo))
+        else:
+            g.gdn_recurrent_seq(vw.dims, vw.params, x, a, b, sw.batch, conv, state, o=o)
+            g.gdn_spec_verify(vw.dims, vw.params, pages, vw.x[s], vw.a[s], vw.b[s], vw.wl.n_req, vw.wl.n_cand,
+                              vw.rp, acc, par, vconv, o=vo)
+        st[3] = n + 1
+
+
 def measure(torch, wload, steps, warmup):
     for _ in range(warmup):
         wload.launch()
@@ -343,7 +378,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="decode,short_prefill,long_prefill,spec_verify")
+    ap.add_argument("--only", default="decode,short_prefill,long_prefill,spec_verify,mixed_step")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep-dispatch", action="store_true",
                     help="time token-by-token vs chunked prefill over uniform batches instead of the benchmark")
@@ -464,6 +499,29 @@ def main():
         other["spec_verify"] = {"state_f32": res[wk.F32], "state_bf16": res[wk.BF16],
                                 "page_bytes_onepage_f32": lay1, "page_bytes_slots_f32": lay8,
                                 "config": {"n_req": wl.n_req, "n_cand": wl.n_cand}}
+
+    # ---- mixed steps: a prefill batch + a verify batch, one launch vs two
+    if "mixed_step" in only:
+        res = {}
+        small_seq = wk.SHORT_PREFILL.replace(name="small_prefill", seqlens=(45, 17, 9, 3))
+        small_ver = wk.SPEC_VERIFY.replace(name="small_verify", n_req=8)
+        for name, sw, vw in (("short_prefill_plus_verify", wk.SHORT_PREFILL, wk.SPEC_VERIFY),
+                             ("small_prefill_plus_verify", small_seq, small_ver)):
+            log(f"mixed_step {name}")
+            w = MixedWorkload(g, torch, sw, vw)
+            n = max(args.steps // 4, 10)
+            w.fused = True
+            f_ms, _ = measure(torch, w, n, 5)
+            w.fused = False
+            s_ms, _ = measure(torch, w, n, 5)
+            res[name] = {"value": round(f_ms * 1e3, 1), "unit": "us/step", "us_separate_launches": round(s_ms * 1e3, 1),
+                         "speedup_vs_separate": round(s_ms / f_ms, 3),
+                         "config": {"prefill_seqlens": list(sw.seqlens), "verify_n_req": vw.n_req,
+                                    "verify_n_cand": vw.n_cand, "state_dtype": "f32"}}
+            log(f"mixed_step {name}: {f_ms * 1e3:.1f} us fused, {s_ms * 1e3:.1f} us as two launches")
+            del w
+            torch.cuda.empty_cache()
+        other["mixed_step"] = res
 
     result["other_workloads"] = other
     if not args.no_cpu:

@@ -276,6 +276,57 @@ int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* params, int32_t 
                         void* pages, int64_t page_bytes, int32_t n_pages,
                         gdn_conv_pool conv, float* o, int32_t* err, void* stream);
 
+/* ------------------------------------------------------- mixed step */
+
+/* The token-by-token part of a mixed step: the arguments of
+ * gdn_recurrent_seq.  batch is a host pointer. */
+typedef struct gdn_seq_part {
+    const void* x;
+    int64_t x_stride;
+    const void* a;
+    const void* b;
+    int64_t ab_stride;
+    const gdn_batch* batch;
+    gdn_conv_pool conv;
+    gdn_state_pool state;
+    float* o;
+} gdn_seq_part;
+
+/* The verify part of a mixed step: the arguments of gdn_spec_verify. */
+typedef struct gdn_verify_part {
+    int32_t layout;
+    const void* x;
+    int64_t x_stride;
+    const void* a;
+    const void* b;
+    int64_t ab_stride;
+    int32_t n_req;
+    int32_t n_cand;
+    const int32_t* req_page;
+    const int32_t* num_accepted;
+    const uint8_t* step_parity;
+    void* pages;
+    int64_t page_bytes;
+    int32_t n_pages;
+    gdn_conv_pool conv;
+    float* o;
+} gdn_verify_part;
+
+/* One serving step that mixes token-by-token sequences (prefill or decode
+ * rows of a ragged batch) with speculative verify requests, in ONE launch
+ * ("r9700-stack v0.2.3", section "1. Time to first token": both kernels
+ * address the batch's own rows, so a step that mixes prefills with running
+ * spec-decode sequences needs no gather).  The result is that of
+ * gdn_recurrent_seq on `seq` followed by gdn_spec_verify on `verify`, bit
+ * for bit; the sequence workgroups come first in the grid (longest sequence
+ * first), and the verify workgroups fill the slots shorter sequences free.
+ * seq and verify are host pointers; either may be NULL or empty (n_seqs or
+ * n_req 0).  The two parts must touch distinct pages; their conv pools may
+ * be one pool.  Each part is validated as its stand-alone entry point is;
+ * err collects the device-side errors of both. */
+int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,
+                       const gdn_verify_part* verify, int32_t* err, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,4 +9,5 @@ from ._lib import (GDN_BF16, GDN_DEVERR_ACCEPTED, GDN_DEVERR_BATCH, GDN_DEVERR_P
                    GDN_SPEC_ONEPAGE, GDN_SPEC_SLOTS, load)
 from .ops import (Batch, ConvPool, Dims, GdnError, Params, SpecPages, StatePool,  # noqa: F401
                   gdn_abi_version, gdn_chunked_prefill, gdn_chunked_workspace_bytes, gdn_conv_update,
-                  gdn_prefill, gdn_prefill_path, gdn_recurrent_seq, gdn_spec_page_layout, gdn_spec_verify)
+                  gdn_mixed_step, gdn_prefill, gdn_prefill_path, gdn_recurrent_seq, gdn_spec_page_layout,
+                  gdn_spec_verify)

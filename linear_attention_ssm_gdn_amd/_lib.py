@@ -23,7 +23,7 @@ GDN_PREFILL_MAX_DEFAULT = -1
 
 SYMBOLS = ("gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout", "gdn_chunked_workspace_bytes",
            "gdn_conv_update", "gdn_recurrent_seq", "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill",
-           "gdn_spec_verify")
+           "gdn_spec_verify", "gdn_mixed_step")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -57,6 +57,18 @@ class GdnSpecLayout(ctypes.Structure):
     _fields_ = [("page_bytes", ctypes.c_size_t), ("header_off", ctypes.c_size_t),
                 ("state_off", ctypes.c_size_t), ("record_off", ctypes.c_size_t),
                 ("record_row_bytes", ctypes.c_size_t)]
+
+
+class GdnSeqPart(ctypes.Structure):
+    _fields_ = [("x", _vp), ("x_stride", _i64), ("a", _vp), ("b", _vp), ("ab_stride", _i64),
+                ("batch", ctypes.POINTER(GdnBatch)), ("conv", GdnConvPool), ("state", GdnStatePool), ("o", _vp)]
+
+
+class GdnVerifyPart(ctypes.Structure):
+    _fields_ = [("layout", _i32), ("x", _vp), ("x_stride", _i64), ("a", _vp), ("b", _vp), ("ab_stride", _i64),
+                ("n_req", _i32), ("n_cand", _i32), ("req_page", _vp), ("num_accepted", _vp),
+                ("step_parity", _vp), ("pages", _vp), ("page_bytes", _i64), ("n_pages", _i32),
+                ("conv", GdnConvPool), ("o", _vp)]
 
 
 _lib = None
@@ -106,5 +118,8 @@ def load() -> ctypes.CDLL:
     L.gdn_spec_verify.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _i32, _vp, _i64, _vp,
                                   _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, GdnConvPool, _vp,
                                   _vp, _vp]
+    L.gdn_mixed_step.restype = _i32
+    L.gdn_mixed_step.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), ctypes.POINTER(GdnSeqPart),
+                                 ctypes.POINTER(GdnVerifyPart), _vp, _vp]
     _lib = L
     return L

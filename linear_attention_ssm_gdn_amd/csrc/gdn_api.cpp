@@ -83,6 +83,46 @@ int32_t check_sequence_call(const gdn_dims* dims, const gdn_params* params, cons
     return GDN_OK;
 }
 
+gdn::SeqArgs seq_args(const gdn_dims* dims, const gdn_params* params, const void* x, int64_t x_stride,
+                      const void* a, const void* b, int64_t ab_stride, const gdn_batch* batch,
+                      const gdn_conv_pool& conv, const gdn_state_pool& state, float* o, int32_t* err) {
+    gdn::SeqArgs A{};
+    A.x = x; A.x_stride = x_stride; A.a = a; A.b = b; A.ab_stride = ab_stride; A.n_rows = batch->n_rows;
+    A.cu = batch->cu_seqlens; A.page_idx = batch->page_idx; A.has_init = batch->has_init; A.n_seqs = batch->n_seqs;
+    A.conv_w = params->conv_w; A.a_log = params->a_log; A.dt_bias = params->dt_bias;
+    A.conv_base = conv.base; A.conv_page_stride = conv.page_stride; A.conv_n_pages = conv.n_pages; A.sync = conv.sync;
+    A.state = state.base; A.state_page_stride = state.page_stride; A.state_n_pages = state.n_pages;
+    A.o = o; A.err = err; A.h_k = dims->h_k; A.h_v = dims->h_v; A.d_v = dims->d_v;
+    A.scale = dims->scale; A.eps = dims->l2_eps;
+    return A;
+}
+
+// Validation of a verify call (dims and params already checked); fills *L.
+int32_t check_verify_call(const gdn_dims* dims, int32_t layout, const void* x, int64_t x_stride, const void* a,
+                          const void* b, int64_t ab_stride, int32_t n_req, int32_t n_cand, const int32_t* req_page,
+                          const int32_t* num_accepted, const uint8_t* step_parity, const void* pages,
+                          int64_t page_bytes, int32_t n_pages, const gdn_conv_pool& conv, const float* o,
+                          gdn_spec_layout* L);
+
+gdn::VerifyArgs verify_args(const gdn_dims* dims, const gdn_params* params, const gdn_spec_layout& L, const void* x,
+                            int64_t x_stride, const void* a, const void* b, int64_t ab_stride, int32_t n_req,
+                            int32_t n_cand, const int32_t* req_page, const int32_t* num_accepted,
+                            const uint8_t* step_parity, void* pages, int64_t page_bytes, int32_t n_pages,
+                            const gdn_conv_pool& conv, float* o, int32_t* err) {
+    gdn::VerifyArgs A{};
+    A.x = x; A.x_stride = x_stride; A.a = a; A.b = b; A.ab_stride = ab_stride;
+    A.n_req = n_req; A.n_cand = n_cand;
+    A.req_page = req_page; A.num_accepted = num_accepted; A.step_parity = step_parity;
+    A.pages = static_cast<uint8_t*>(pages); A.page_bytes = page_bytes; A.n_pages = n_pages;
+    A.header_off = (int64_t)L.header_off; A.state_off = (int64_t)L.state_off;
+    A.record_off = (int64_t)L.record_off; A.record_row_bytes = (int64_t)L.record_row_bytes;
+    A.conv_w = params->conv_w; A.a_log = params->a_log; A.dt_bias = params->dt_bias;
+    A.conv_base = conv.base; A.conv_page_stride = conv.page_stride; A.conv_n_pages = conv.n_pages; A.sync = conv.sync;
+    A.o = o; A.err = err; A.h_k = dims->h_k; A.h_v = dims->h_v; A.d_v = dims->d_v; A.n_spec = dims->n_spec;
+    A.scale = dims->scale; A.eps = dims->l2_eps;
+    return A;
+}
+
 }  // namespace
 
 GDN_EXPORT int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
@@ -155,14 +195,7 @@ GDN_EXPORT int32_t gdn_recurrent_seq(const gdn_dims* dims, const gdn_params* par
                                      int32_t* err, void* stream) {
     int32_t st = check_sequence_call(dims, params, x, x_stride, a, b, ab_stride, batch, conv, state, o);
     if (st != GDN_OK || batch->n_seqs == 0) return st;
-    gdn::SeqArgs A{};
-    A.x = x; A.x_stride = x_stride; A.a = a; A.b = b; A.ab_stride = ab_stride; A.n_rows = batch->n_rows;
-    A.cu = batch->cu_seqlens; A.page_idx = batch->page_idx; A.has_init = batch->has_init; A.n_seqs = batch->n_seqs;
-    A.conv_w = params->conv_w; A.a_log = params->a_log; A.dt_bias = params->dt_bias;
-    A.conv_base = conv.base; A.conv_page_stride = conv.page_stride; A.conv_n_pages = conv.n_pages; A.sync = conv.sync;
-    A.state = state.base; A.state_page_stride = state.page_stride; A.state_n_pages = state.n_pages;
-    A.o = o; A.err = err; A.h_k = dims->h_k; A.h_v = dims->h_v; A.d_v = dims->d_v;
-    A.scale = dims->scale; A.eps = dims->l2_eps;
+    const gdn::SeqArgs A = seq_args(dims, params, x, x_stride, a, b, ab_stride, batch, conv, state, o, err);
     return from_hip(gdn::launch_seq(A, dims->d_k, dims->act_dtype, dims->state_dtype, batch->max_seqlen,
                                     (hipStream_t)stream));
 }
@@ -243,25 +276,64 @@ GDN_EXPORT int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* param
     if ((st = check_dims(dims)) != GDN_OK) return st;
     if ((st = check_params(params)) != GDN_OK) return st;
     gdn_spec_layout L{};
-    if ((st = gdn_spec_page_layout(dims, layout, &L)) != GDN_OK) return st;
+    if ((st = check_verify_call(dims, layout, x, x_stride, a, b, ab_stride, n_req, n_cand, req_page, num_accepted,
+                                step_parity, pages, page_bytes, n_pages, conv, o, &L)) != GDN_OK)
+        return st;
+    if (n_req == 0) return GDN_OK;
+    const gdn::VerifyArgs A = verify_args(dims, params, L, x, x_stride, a, b, ab_stride, n_req, n_cand, req_page,
+                                          num_accepted, step_parity, pages, page_bytes, n_pages, conv, o, err);
+    return from_hip(gdn::launch_verify(A, dims->d_k, dims->act_dtype, dims->state_dtype, layout,
+                                       (hipStream_t)stream));
+}
+
+namespace {
+int32_t check_verify_call(const gdn_dims* dims, int32_t layout, const void* x, int64_t x_stride, const void* a,
+                          const void* b, int64_t ab_stride, int32_t n_req, int32_t n_cand, const int32_t* req_page,
+                          const int32_t* num_accepted, const uint8_t* step_parity, const void* pages,
+                          int64_t page_bytes, int32_t n_pages, const gdn_conv_pool& conv, const float* o,
+                          gdn_spec_layout* L) {
+    int32_t st;
+    if ((st = gdn_spec_page_layout(dims, layout, L)) != GDN_OK) return st;
     if (n_req < 0 || n_cand < 0 || n_cand > dims->n_spec + 1) return GDN_ERR_ARG;
     if (n_req == 0) return GDN_OK;
     if (!req_page || !num_accepted || !step_parity || !pages || n_pages < 0) return GDN_ERR_ARG;
-    if (page_bytes < (int64_t)L.page_bytes || page_bytes % 256 != 0 || !aligned(pages, 256)) return GDN_ERR_ARG;
+    if (page_bytes < (int64_t)L->page_bytes || page_bytes % 256 != 0 || !aligned(pages, 256)) return GDN_ERR_ARG;
     if ((st = check_conv_pool(dims, conv, dims->conv_w - 1 + dims->n_spec, true)) != GDN_OK) return st;
     if (n_cand > 0 && (!x || !a || !b || !o)) return GDN_ERR_ARG;
     if (n_cand > 0 && (x_stride < c_conv(dims) || ab_stride < dims->h_v)) return GDN_ERR_ARG;
-    gdn::VerifyArgs A{};
-    A.x = x; A.x_stride = x_stride; A.a = a; A.b = b; A.ab_stride = ab_stride;
-    A.n_req = n_req; A.n_cand = n_cand;
-    A.req_page = req_page; A.num_accepted = num_accepted; A.step_parity = step_parity;
-    A.pages = static_cast<uint8_t*>(pages); A.page_bytes = page_bytes; A.n_pages = n_pages;
-    A.header_off = (int64_t)L.header_off; A.state_off = (int64_t)L.state_off;
-    A.record_off = (int64_t)L.record_off; A.record_row_bytes = (int64_t)L.record_row_bytes;
-    A.conv_w = params->conv_w; A.a_log = params->a_log; A.dt_bias = params->dt_bias;
-    A.conv_base = conv.base; A.conv_page_stride = conv.page_stride; A.conv_n_pages = conv.n_pages; A.sync = conv.sync;
-    A.o = o; A.err = err; A.h_k = dims->h_k; A.h_v = dims->h_v; A.d_v = dims->d_v; A.n_spec = dims->n_spec;
-    A.scale = dims->scale; A.eps = dims->l2_eps;
-    return from_hip(gdn::launch_verify(A, dims->d_k, dims->act_dtype, dims->state_dtype, layout,
-                                       (hipStream_t)stream));
+    return GDN_OK;
+}
+}  // namespace
+
+GDN_EXPORT int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,
+                                  const gdn_verify_part* verify, int32_t* err, void* stream) {
+    int32_t st;
+    if ((st = check_dims(dims)) != GDN_OK) return st;
+    if ((st = check_params(params)) != GDN_OK) return st;
+    gdn::SeqArgs S{};
+    gdn::VerifyArgs V{};
+    int32_t layout = GDN_SPEC_ONEPAGE;
+    if (seq) {
+        if ((st = check_sequence_call(dims, params, seq->x, seq->x_stride, seq->a, seq->b, seq->ab_stride,
+                                      seq->batch, seq->conv, seq->state, seq->o)) != GDN_OK)
+            return st;
+        if (seq->batch->n_seqs > 0)
+            S = seq_args(dims, params, seq->x, seq->x_stride, seq->a, seq->b, seq->ab_stride, seq->batch, seq->conv,
+                         seq->state, seq->o, err);
+    }
+    if (verify) {
+        gdn_spec_layout L{};
+        const gdn_verify_part& v = *verify;
+        if ((st = check_verify_call(dims, v.layout, v.x, v.x_stride, v.a, v.b, v.ab_stride, v.n_req, v.n_cand,
+                                    v.req_page, v.num_accepted, v.step_parity, v.pages, v.page_bytes, v.n_pages,
+                                    v.conv, v.o, &L)) != GDN_OK)
+            return st;
+        layout = v.layout;
+        if (v.n_req > 0)
+            V = verify_args(dims, params, L, v.x, v.x_stride, v.a, v.b, v.ab_stride, v.n_req, v.n_cand, v.req_page,
+                            v.num_accepted, v.step_parity, v.pages, v.page_bytes, v.n_pages, v.conv, v.o, err);
+    }
+    if (S.n_seqs == 0 && V.n_req == 0) return GDN_OK;
+    return from_hip(gdn::launch_mixed(S, V, dims->d_k, dims->act_dtype, dims->state_dtype, layout,
+                                      (hipStream_t)stream));
 }

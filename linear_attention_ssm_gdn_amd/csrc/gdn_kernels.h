@@ -68,6 +68,10 @@ hipError_t launch_conv(const ConvArgs& a, int act_dtype, int y_dtype, int max_se
 hipError_t launch_verify(const VerifyArgs& a, int d_k, int act_dtype, int state_dtype, int layout,
                          hipStream_t s);
 hipError_t launch_chunked(const ChunkArgs& a, int d_k, int act_dtype, int state_dtype, hipStream_t s);
+// One launch running the token-by-token workgroups of `s` and the verify
+// workgroups of `v` (either part may be empty: n_seqs or n_req == 0).
+hipError_t launch_mixed(const SeqArgs& s, const VerifyArgs& v, int d_k, int act_dtype, int state_dtype, int layout,
+                        hipStream_t st);
 
 // Which (d_k, d_v) the kernels are compiled for.
 bool seq_supported(int d_k, int d_v);

@@ -1,391 +1,12 @@
-// gdn_verify.hip -- one speculative verify step (Gated DeltaNet part (d)).
-//
-// The one-page design of "r9700-stack v0.2.4: one GDN state page per
-// request" (section "What it does"): each request keeps one state
-// checkpoint plus a record of the previous step's candidate rows (post-conv
-// q|k|v and the a/b gate inputs) in two slots and a flag word (live slot,
-// parity, done counter).  A step replays the accepted rows of the live slot
-// into the checkpoint, stores it, then runs the new candidates from the
-// stored value and records them in the other slot.  The comparison design
-// keeps one state page per candidate instead.  Both designs run through this
-// one kernel template and the same per-token functions, which is what makes
-// them bit-identical.
-//
-// Grid: one workgroup per (request, value head, block of 32*CPL value
-// columns), the lane layout of gdn_block.hpp.  Candidates per step <= 16.
-#include "gdn_block.hpp"
-#include "gdn_kernels.h"
-#include "../../include/gdn.h"
+// gdn_verify.hip -- one speculative verify step (Gated DeltaNet part (d)):
+// the launcher of the workgroup in gdn_verify_block.hpp.
+#include "gdn_verify_block.hpp"
 
 namespace gdn {
 
-constexpr int VER_TT = 16;
-
 template <typename ActT, typename StT, int DK, int CPL, int LAYOUT>
 __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_verify(const VerifyArgs A) {
-    constexpr int TT = VER_TT;
-    constexpr int R = DK / 16;
-    constexpr int BV = 32 * CPL;
-    constexpr int NLC = 2 * DK + BV;
-    static_assert(TT <= 32, "one 16-lane row per token of a chunk");
-    static_assert(NLC <= BLOCK_THREADS, "one conv channel per thread");
-    __shared__ __attribute__((aligned(16))) float sq[TT * DK];
-    __shared__ __attribute__((aligned(16))) float sk[TT * DK];
-    __shared__ __attribute__((aligned(16))) float sv[TT * BV];
-    __shared__ float ssc[TT * 4];
-    __shared__ int sh_last;
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int nblk = A.d_v / BV;
-    int bid = blockIdx.x;
-    const int blk = bid % nblk;
-    bid /= nblk;
-    const int h = bid % A.h_v;
-    const int req = bid / A.h_v;
-    const int rr = A.h_v / A.h_k;
-    const int ki = h / rr;
-    const int colbase = blk * BV;
-    const int64_t C = 2 * (int64_t)A.h_k * DK + (int64_t)A.h_v * A.d_v;
-    const bool reporter = (h == 0 && blk == 0 && tid == 0);
-
-    const int page = A.req_page[req];
-    if (page < 0) return;
-    if (page >= A.n_pages || page >= A.conv_n_pages) {
-        if (reporter) set_err(A.err, GDN_DEVERR_PAGE);
-        return;
-    }
-    uint8_t* pg = A.pages + (int64_t)page * A.page_bytes;
-    gdn_spec_header* hdr = reinterpret_cast<gdn_spec_header*>(pg + A.header_off);
-    const uint32_t flag = hdr->flag;
-    const int L = (int)(flag & 1u);
-    const int P = (int)((flag >> 1) & 1u);
-    const int nr = (int)hdr->n_rows[L];
-    const int par = A.step_parity[req] & 1;
-    if (par == P) {
-        if (reporter) set_err(A.err, GDN_DEVERR_PARITY);
-        return;
-    }
-    int acc = 0;
-    if (nr > 0) {
-        acc = A.num_accepted[req];
-        if (acc < 0 || acc >= nr || nr > A.n_spec + 1) {
-            if (reporter) set_err(A.err, GDN_DEVERR_ACCEPTED);
-            return;
-        }
-    }
-    const int n_replay = (LAYOUT == GDN_SPEC_ONEPAGE && nr > 0) ? acc + 1 : 0;
-    const int nc = A.n_cand;
-
-    // ---- done counter: the last workgroup of the request to get here flips the
-    // flag at the end.  The counter stands for "this workgroup has read the
-    // header", which is true now, so it is counted now; its result is read
-    // once the state has arrived (issued before it, so already back).
-    uint32_t done_before = 0;
-    if (tid == 0) done_before = fetch_add_late(&hdr->flag, 256u);
-
-    // ---- starting state: the checkpoint, or slot[acc]
-    const int64_t head_elems = (int64_t)DK * A.d_v;
-    StT* __restrict__ st_base = reinterpret_cast<StT*>(pg + A.state_off);
-    StT* __restrict__ Sload = (LAYOUT == GDN_SPEC_ONEPAGE)
-                                  ? st_base + (int64_t)h * head_elems + colbase
-                                  : st_base + ((int64_t)acc * A.h_v + h) * head_elems + colbase;
-
-    // ---- this thread's conv channel: weights, window rows acc..acc+2 of the conv buffer
-    ActT* __restrict__ cbuf = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
-    const int lc = tid;
-    int64_t gc = -1;
-    float w[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xw0 = 0.0f, xw1 = 0.0f, xw2 = 0.0f;
-    if (lc < NLC) {
-        gc = lc < DK ? (int64_t)ki * DK + lc
-           : lc < 2 * DK ? (int64_t)A.h_k * DK + (int64_t)ki * DK + (lc - DK)
-           : 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + (lc - 2 * DK);
-        const ActT* Wc = static_cast<const ActT*>(A.conv_w) + gc * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = to_f32(Wc[e]);
-        xw0 = to_f32(cbuf[(int64_t)(acc + 0) * C + gc]);
-        xw1 = to_f32(cbuf[(int64_t)(acc + 1) * C + gc]);
-        xw2 = to_f32(cbuf[(int64_t)(acc + 2) * C + gc]);
-    }
-    float* ydst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
-    const int yld = lc < 2 * DK ? DK : BV;
-    float exp_alog_v = expf(A.a_log[h]);
-    float dtb = A.dt_bias[h];
-    asm volatile("" : "+v"(dtb));
-    const float& exp_alog = exp_alog_v;
-
-    // ---- LDS rows: when both the replayed rows and the candidates fit in
-    // half of the TT token rows ("split"), the replayed rows take rows
-    // 0 .. TT/2-1 and the candidates rows TT/2 .. TT-1, so the candidates'
-    // conv and every gate run while the state is still in flight; otherwise
-    // both start at row 0 and the candidates follow the replay.
-    const bool split = (nc <= TT / 2) && (n_replay <= TT / 2);
-    const int crow = split ? TT / 2 : 0;       // first candidate row
-    const int gtok = (wv << 2) + (lane >> 4);  // the token row of this thread's 16-lane row
-    const int cidx = gtok - crow;              // the candidate of that row (if any)
-
-    // ---- small inputs first, then the state: loads complete in order, so
-    // everything above the state is usable while the state is in flight
-    float xp[TT];
-    float pa = 0.0f, pb = 0.0f;   // gate inputs of candidate cidx
-    const int64_t row_bytes = A.record_row_bytes;
-    const int64_t rows_per_slot = A.n_spec + 1;
-    float ra = 0.0f, rb = 0.0f;   // gate inputs of replayed row gtok
-    const uint8_t* rec = pg + A.record_off + (int64_t)L * rows_per_slot * row_bytes;
-    if (n_replay > 0) {
-        const float* rrow = reinterpret_cast<const float*>(rec + (gtok < n_replay ? gtok : 0) * row_bytes);
-        ra = rrow[C + h];
-        rb = rrow[C + A.h_v + h];
-    }
-    {
-        // unconditional loads (row and channel clamped into range) stay in flight
-        // together; values past the candidates are zeroed
-        const ActT* X = static_cast<const ActT*>(A.x);
-        const int64_t gcl = gc >= 0 ? gc : 0;
-        if (nc > 0) {
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                const int t = tt < nc ? tt : nc - 1;
-                const float xv = to_f32(X[((int64_t)req * nc + t) * A.x_stride + gcl]);
-                xp[tt] = (gc >= 0 && tt < nc) ? xv : 0.0f;
-            }
-            {
-                const bool ok = cidx >= 0 && cidx < nc;
-                const int64_t row = ((int64_t)req * nc + (ok ? cidx : nc - 1)) * A.ab_stride + h;
-                const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
-                const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
-                pa = ok ? av : 0.0f;
-                pb = ok ? bv : 0.0f;
-            }
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) xp[tt] = 0.0f;
-        }
-    }
-    // One-page: the replayed rows go straight into the LDS rows 0 .. n_replay-1,
-    // all in flight at once: lane l of a wave lands at base + 4 l, and each
-    // region's base is chosen so that lane lc writes its own channel's slot.
-    if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
-        const int wbase = tid & ~63;
-        for (int i = 0; i < n_replay; ++i) {
-            const float* row = reinterpret_cast<const float*>(rec + i * row_bytes);
-            if (lc < DK)
-                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
-            else if (lc < 2 * DK)
-                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
-            else if (lc < NLC)
-                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sv + i * BV + wbase - 2 * DK));
-        }
-    }
-    // Every small input is taken (waited for) here, before the state's loads
-    // are issued: a use after them would make the compiler wait for the
-    // whole state, since it cannot count through the replay loop above.
-    {
-        float exp_pin = exp_alog;
-        asm volatile("" : "+v"(exp_pin), "+v"(pa), "+v"(pb), "+v"(ra), "+v"(rb), "+v"(xw0), "+v"(xw1), "+v"(xw2));
-        asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) asm volatile("" : "+v"(xp[tt]));
-        exp_alog_v = exp_pin;
-    }
-    asm volatile("" ::: "memory");  // the state's loads are issued after all of the above
-
-    float s[CPL][R];
-    load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
-
-    // ---- candidates: conv (+ record) into rows crow.., then gating
-    const bool qk_writer = (h == ki * rr) && (blk == 0);
-    uint8_t* recw = pg + A.record_off + (int64_t)(1 - L) * rows_per_slot * row_bytes;
-    auto cand_conv = [&]() {
-        if (gc >= 0) {
-            if (nc > 0) {
-                const bool rec_this = (LAYOUT == GDN_SPEC_ONEPAGE) && (lc >= 2 * DK || qk_writer);
-                float x3 = xw0, x2 = xw1, x1 = xw2;
-#pragma unroll
-                for (int tt = 0; tt < TT; ++tt) {
-                    if (tt < nc) {
-                        const float x0 = xp[tt];
-                        const float y = silu_hw(conv4(w, x3, x2, x1, x0));
-                        ydst[(crow + tt) * yld] = y;
-                        if (rec_this) reinterpret_cast<float*>(recw + tt * row_bytes)[gc] = y;
-                        x3 = x2; x2 = x1; x1 = x0;
-                    }
-                }
-            } else {
-                // commit only: consume the window loads before arriving
-                ydst[crow * yld] = xw0 + xw1 + xw2;
-            }
-        }
-    };
-    // the gates of this thread's token row: a replayed row or a candidate
-    auto gates = [&](bool replay_rows, bool cand_rows) {
-        if (replay_rows && gtok < n_replay) {
-            (void)gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
-            float eg, beta;
-            gate_scalars(ra, rb, exp_alog, dtb, eg, beta);
-            if ((lane & 15) == 0) {
-                ssc[gtok * 4 + 0] = eg;
-                ssc[gtok * 4 + 1] = beta;
-            }
-        }
-        if (cand_rows && cidx >= 0 && cidx < nc) {
-            const float kq = gate_qk<DK>(sq + gtok * DK, sk + gtok * DK, A.scale, A.eps, lane & 15);
-            float eg, beta;
-            gate_scalars(pa, pb, exp_alog, dtb, eg, beta);
-            if ((lane & 15) == 0) {
-                ssc[gtok * 4 + 0] = eg;
-                ssc[gtok * 4 + 1] = beta;
-                ssc[gtok * 4 + 2] = kq;
-                if (LAYOUT == GDN_SPEC_ONEPAGE && blk == 0) {
-                    float* rrow = reinterpret_cast<float*>(recw + cidx * row_bytes);
-                    rrow[C + h] = pa;
-                    rrow[C + A.h_v + h] = pb;
-                }
-            }
-        }
-    };
-    if (split) {
-        // Everything but the state has arrived once at most the state's R
-        // loads (one per row, issued last) are outstanding; the candidates'
-        // record stores come after this wait.
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(R) : "memory");
-        cand_conv();
-        lds_barrier();
-        gates(true, nc > 0);
-        lds_barrier();
-    } else if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
-        wait_vmem();
-        lds_barrier();
-        gates(true, false);
-        lds_barrier();
-    }
-
-    // ---- one-page: replay rows 0..acc of the live record, store the checkpoint
-    if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
-        // two rows per trip with two operand sets, each set's LDS reads
-        // issued one row ahead of its use
-        struct ROpnd { float k[R], v[CPL], eg, beta; };
-        auto roperands = [&](ROpnd& p, int tt) {
-            lds_rows<R>(sk + tt * DK, tid, p.k);
-            lds_cols<CPL>(sv + tt * BV, tid, p.v);
-            p.eg = ssc[tt * 4 + 0];
-            p.beta = ssc[tt * 4 + 1];
-        };
-        ROpnd r0, r1;
-        roperands(r0, 0);
-        for (int tt = 0; tt < n_replay; tt += 2) {
-            roperands(r1, tt + 1 < n_replay ? tt + 1 : tt);
-            delta_update<R, CPL>(s, r0.k, r0.v, r0.eg, r0.beta);
-            if (tt + 1 < n_replay) {
-                roperands(r0, tt + 2 < n_replay ? tt + 2 : tt + 1);
-                delta_update<R, CPL>(s, r1.k, r1.v, r1.eg, r1.beta);
-            }
-        }
-    }
-
-    // ---- window arrival, before any store: the window values are in registers
-    // (their loads were issued before the state's, which has been consumed),
-    // and the barrier also separates the replay's LDS reads from the
-    // candidates' writes.  The atomic's result is read at the end: reading it
-    // is a wait on the in-order vector-memory counter, and by then the stores
-    // issued after it no longer stand in anyone's way.
-    asm volatile("" : "+v"(xw0), "+v"(xw1), "+v"(xw2), "+v"(done_before));
-    lds_barrier();
-    uint32_t arrived_before = 0;
-    if (tid == 0) arrived_before = arrive(A.sync + (int64_t)page * A.h_k + ki);
-
-    if (LAYOUT == GDN_SPEC_ONEPAGE) {
-        // the checkpoint; continue from its stored (rounded) value
-        store_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-#pragma unroll
-            for (int m = 0; m < R; ++m) s[c][m] = round_as<StT>(s[c][m]);
-    }
-
-    if (!split) {
-        cand_conv();
-        lds_barrier();
-        if (nc > 0) gates(false, true);
-        lds_barrier();
-    }
-    if (nc > 0) {
-        const int cg = lane_colgroup(tid);
-        const bool writer = lane_rowgroup(tid) == 0;
-        float* __restrict__ O = A.o + (int64_t)req * nc * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase + cg * CPL;
-        const int64_t o_stride = (int64_t)A.h_v * A.d_v;
-        // two tokens per trip with two operand sets, each set's LDS reads
-        // issued one token ahead of its use
-        struct Opnd { float k[R], q[R], v[CPL], eg, beta, kq; };
-        auto operands = [&](Opnd& p, int tt) {
-            const int r = crow + tt;
-            lds_rows<R>(sk + r * DK, tid, p.k);
-            lds_rows<R>(sq + r * DK, tid, p.q);
-            lds_cols<CPL>(sv + r * BV, tid, p.v);
-            p.eg = ssc[r * 4 + 0];
-            p.beta = ssc[r * 4 + 1];
-            p.kq = ssc[r * 4 + 2];
-        };
-        auto step = [&](const Opnd& p, int tt) {
-            float o[CPL];
-            delta_step<R, CPL>(s, p.k, p.q, p.v, p.eg, p.beta, p.kq, o);
-            if (writer) {
-                float* dst = O + (int64_t)tt * o_stride;
-                if constexpr (CPL == 4) {
-                    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-                } else {
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) dst[c] = o[c];
-                }
-            }
-            if (LAYOUT == GDN_SPEC_SLOTS)
-                store_state<StT, DK, CPL>(st_base + ((int64_t)tt * A.h_v + h) * head_elems + colbase, A.d_v, s,
-                                          tid);
-        };
-        Opnd p0, p1;
-        operands(p0, 0);
-        for (int tt = 0; tt < nc; tt += 2) {
-            operands(p1, tt + 1 < nc ? tt + 1 : tt);
-            step(p0, tt);
-            if (tt + 1 < nc) {
-                operands(p0, tt + 2 < nc ? tt + 2 : tt + 1);
-                step(p1, tt + 1);
-            }
-        }
-    } else if (LAYOUT == GDN_SPEC_SLOTS) {
-        store_state<StT, DK, CPL>(st_base + (int64_t)h * head_elems + colbase, A.d_v, s, tid);
-    }
-    asm volatile("" : "+v"(arrived_before));  // keep the read of the result here, not at the atomic
-    if (tid == 0)
-        sh_last = arrived_last(A.sync + (int64_t)page * A.h_k + ki, arrived_before, (uint32_t)(rr * nblk)) ? 1 : 0;
-    lds_barrier();
-
-    // ---- conv buffer: [a'+1, a'+2, candidates] or [a', a'+1, a'+2]
-    if (gc >= 0 && (lc >= 2 * DK || sh_last)) {
-        if (nc > 0) {
-            cbuf[0 * C + gc] = from_f32<ActT>(xw1);
-            cbuf[1 * C + gc] = from_f32<ActT>(xw2);
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                if (tt < nc) cbuf[(int64_t)(2 + tt) * C + gc] = from_f32<ActT>(xp[tt]);
-        } else {
-            cbuf[0 * C + gc] = from_f32<ActT>(xw0);
-            cbuf[1 * C + gc] = from_f32<ActT>(xw1);
-            cbuf[2 * C + gc] = from_f32<ActT>(xw2);
-        }
-    }
-
-    // ---- the last workgroup of the request to count itself flips the flag.
-    // Every workgroup of the request read the header before counting, so the
-    // last one may rewrite it; relaxed for the reason given at arrive_last.
-    if (tid == 0) {
-        const uint32_t total = (uint32_t)(A.h_v * nblk);
-        if ((done_before >> 8) + 1u == total) {
-            hdr->n_rows[1 - L] = (uint32_t)nc;
-            hdr->accepted = (uint32_t)acc;
-            __hip_atomic_store(&hdr->flag, (uint32_t)((1 - L) | (par << 1)), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    verify_block<ActT, StT, DK, CPL, LAYOUT>(A, blockIdx.x);
 }
 
 template <typename ActT, typename StT, int DK, int CPL>

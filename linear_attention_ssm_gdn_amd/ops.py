@@ -280,3 +280,42 @@ def gdn_spec_verify(dims: Dims, params: Params, pages: SpecPages, x: Optional[to
                                   torch.cuda.current_stream(dev).cuda_stream)
     _check("gdn_spec_verify", st)
     return o
+
+
+def gdn_mixed_step(dims: Dims, params: Params, seq: Optional[dict] = None, verify: Optional[dict] = None,
+                   err: Optional[torch.Tensor] = None) -> None:
+    """One launch for a step mixing token-by-token sequences and verify requests.
+
+    seq:    dict(x, a, b, batch, conv, state, o) -- the arguments of gdn_recurrent_seq
+    verify: dict(pages, x, a, b, n_req, n_cand, req_page, num_accepted, step_parity, conv, o)
+            -- the arguments of gdn_spec_verify (pages: SpecPages)
+    Outputs are written into the o tensors given."""
+    d, p = dims.c(), params.c()
+    sp = vp = None
+    keep = []
+    stream_of = None
+    if seq is not None:
+        if seq["a"].stride() != seq["b"].stride():
+            raise ValueError("a and b must share their row stride")
+        bt = seq["batch"].c()
+        keep.append(bt)
+        sp = L.GdnSeqPart(seq["x"].data_ptr(), _rows(seq["x"], "x"), seq["a"].data_ptr(), seq["b"].data_ptr(),
+                          _rows(seq["a"], "a"), ctypes.pointer(bt), seq["conv"].c(), seq["state"].c(),
+                          seq["o"].data_ptr())
+        stream_of = seq["x"]
+    if verify is not None:
+        v = verify
+        pages = v["pages"]
+        x, a, b = v.get("x"), v.get("a"), v.get("b")
+        vp = L.GdnVerifyPart(pages.layout, _ptr(x), _rows(x, "x") if x is not None else 0, _ptr(a), _ptr(b),
+                             _rows(a, "a") if a is not None else 0, v["n_req"], v["n_cand"],
+                             v["req_page"].data_ptr(), v["num_accepted"].data_ptr(), v["step_parity"].data_ptr(),
+                             pages.buf.data_ptr(), pages.buf.stride(0), pages.buf.shape[0], v["conv"].c(),
+                             _ptr(v.get("o")))
+        stream_of = stream_of if stream_of is not None else v["req_page"]
+    if stream_of is None:
+        return
+    st = L.load().gdn_mixed_step(ctypes.byref(d), ctypes.byref(p), ctypes.byref(sp) if sp is not None else None,
+                                 ctypes.byref(vp) if vp is not None else None, _ptr(err),
+                                 torch.cuda.current_stream(stream_of.device).cuda_stream)
+    _check("gdn_mixed_step", st)

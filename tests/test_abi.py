@@ -48,7 +48,8 @@ def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
     assert set(names) == {"gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout",
                           "gdn_chunked_workspace_bytes", "gdn_conv_update", "gdn_recurrent_seq",
-                          "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill", "gdn_spec_verify"}
+                          "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill", "gdn_spec_verify",
+                          "gdn_mixed_step"}
     for n in names:
         assert hasattr(so, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "linear_attention_ssm_gdn_amd",
@@ -61,7 +62,8 @@ def test_every_declared_symbol_is_exported(so):
 def test_struct_layouts_match_c(L, tmp_path):
     structs = {"gdn_dims": L.GdnDims, "gdn_params": L.GdnParams, "gdn_batch": L.GdnBatch,
                "gdn_conv_pool": L.GdnConvPool, "gdn_state_pool": L.GdnStatePool,
-               "gdn_spec_layout": L.GdnSpecLayout}
+               "gdn_spec_layout": L.GdnSpecLayout, "gdn_seq_part": L.GdnSeqPart,
+               "gdn_verify_part": L.GdnVerifyPart}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gdn.h"', 'int main(void) {']
     for cname, py in structs.items():
         lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
@@ -257,6 +259,42 @@ def test_verify_validation(so, L):
     assert call(layout=3) == 1
     assert call(x=None) == 1
     assert call(n_req=0) == 0                        # nothing to do
+
+
+def test_mixed_step_validation(so, L):
+    """Each part of a mixed step is validated as its stand-alone entry point;
+    absent or empty parts are allowed and an empty step launches nothing."""
+    d = _dims(L)
+    C = 2 * 16 * 128 + 32 * 128
+    lay = L.GdnSpecLayout()
+    assert so.gdn_spec_page_layout(ctypes.byref(d), 0, ctypes.byref(lay)) == 0
+    params = L.GdnParams(FAKE, FAKE, FAKE)
+    sa = _seq_args(L, d)
+
+    def seq_part(x=FAKE, batch=None, rows=3):
+        b = batch or L.GdnBatch(FAKE, FAKE, None, 2, 8, 16)
+        return L.GdnSeqPart(x, C, FAKE, FAKE, 32, ctypes.pointer(b), L.GdnConvPool(FAKE, rows * C, rows, 4, FAKE),
+                            sa["state"], FAKE)
+
+    def ver_part(n_req=2, n_cand=8, layout=0, rows=10, pages=FAKE):
+        return L.GdnVerifyPart(layout, FAKE, C, FAKE, FAKE, 32, n_req, n_cand, FAKE, FAKE, FAKE, pages,
+                               lay.page_bytes, 4, L.GdnConvPool(FAKE, rows * C, rows, 4, FAKE), FAKE)
+
+    def call(seq=None, ver=None, p=params, dims=d):
+        return so.gdn_mixed_step(ctypes.byref(dims), ctypes.byref(p) if p is not None else None,
+                                 ctypes.byref(seq) if seq is not None else None,
+                                 ctypes.byref(ver) if ver is not None else None, None, None)
+    assert call() == 0                                           # nothing to do
+    empty = L.GdnBatch(None, None, None, 0, 0, 0)
+    assert call(seq=seq_part(batch=empty), ver=ver_part(n_req=0)) == 0
+    assert call(seq=seq_part(), p=None) == 1
+    assert call(seq=seq_part(x=None), ver=ver_part(n_req=0)) == 1
+    assert call(seq=seq_part(rows=2), ver=ver_part(n_req=0)) == 1   # window narrower than W-1 rows
+    assert call(seq=seq_part(batch=empty), ver=ver_part(rows=9)) == 1  # buffer narrower than W-1+n_spec
+    assert call(seq=seq_part(batch=empty), ver=ver_part(n_cand=9)) == 1
+    assert call(seq=seq_part(batch=empty), ver=ver_part(layout=2)) == 1
+    assert call(ver=ver_part(pages=FAKE + 16)) == 1
+    assert call(seq=seq_part(), dims=_dims(L, d_k=96)) == 2
 
 
 def test_conv_update_validation(so, L):
