@@ -279,7 +279,15 @@ int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* params, int32_t 
 /* ------------------------------------------------------- mixed step */
 
 /* The token-by-token part of a mixed step: the arguments of
- * gdn_recurrent_seq.  batch is a host pointer. */
+ * gdn_recurrent_seq (batch is a host pointer), and optionally the
+ * speculative pages the sequences go on to verify from.  With spec_pages
+ * set, each sequence also leaves the header of its page (page_idx) fresh:
+ * all zero, no record rows.  Alias the state pool onto the pages'
+ * checkpoints (state.base = spec_pages + state_off, state.page_stride =
+ * spec_page_bytes / state element size; gdn_spec_page_layout) and give the
+ * sequences a conv pool wide enough for verify: the step then leaves a
+ * prefilled request ready for its first verify step, the prefill's state in
+ * the checkpoint and its window in conv rows 0..W-2, with nothing copied. */
 typedef struct gdn_seq_part {
     const void* x;
     int64_t x_stride;
@@ -290,6 +298,9 @@ typedef struct gdn_seq_part {
     gdn_conv_pool conv;
     gdn_state_pool state;
     float* o;
+    void* spec_pages;          /* or NULL; 256-byte aligned */
+    int64_t spec_page_bytes;   /* multiple of 256 */
+    int32_t spec_n_pages;      /* a page index >= spec_n_pages is a device error (GDN_DEVERR_PAGE) */
 } gdn_seq_part;
 
 /* The verify part of a mixed step: the arguments of gdn_spec_verify. */

@@ -61,7 +61,8 @@ class GdnSpecLayout(ctypes.Structure):
 
 class GdnSeqPart(ctypes.Structure):
     _fields_ = [("x", _vp), ("x_stride", _i64), ("a", _vp), ("b", _vp), ("ab_stride", _i64),
-                ("batch", ctypes.POINTER(GdnBatch)), ("conv", GdnConvPool), ("state", GdnStatePool), ("o", _vp)]
+                ("batch", ctypes.POINTER(GdnBatch)), ("conv", GdnConvPool), ("state", GdnStatePool), ("o", _vp),
+                ("spec_pages", _vp), ("spec_page_bytes", _i64), ("spec_n_pages", _i32)]
 
 
 class GdnVerifyPart(ctypes.Structure):

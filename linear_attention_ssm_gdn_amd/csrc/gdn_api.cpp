@@ -317,9 +317,16 @@ GDN_EXPORT int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params
         if ((st = check_sequence_call(dims, params, seq->x, seq->x_stride, seq->a, seq->b, seq->ab_stride,
                                       seq->batch, seq->conv, seq->state, seq->o)) != GDN_OK)
             return st;
-        if (seq->batch->n_seqs > 0)
+        if (seq->spec_pages && (seq->spec_page_bytes < 256 || seq->spec_page_bytes % 256 != 0 ||
+                                !aligned(seq->spec_pages, 256) || seq->spec_n_pages < 0))
+            return GDN_ERR_ARG;
+        if (seq->batch->n_seqs > 0) {
             S = seq_args(dims, params, seq->x, seq->x_stride, seq->a, seq->b, seq->ab_stride, seq->batch, seq->conv,
                          seq->state, seq->o, err);
+            S.spec_pages = static_cast<uint8_t*>(seq->spec_pages);
+            S.spec_page_bytes = seq->spec_page_bytes;
+            S.spec_n_pages = seq->spec_n_pages;
+        }
     }
     if (verify) {
         gdn_spec_layout L{};

@@ -19,6 +19,8 @@ struct SeqArgs {
     int32_t* err;
     int32_t h_k, h_v, d_v;
     float scale, eps;
+    // optional: speculative pages whose header each sequence leaves fresh
+    uint8_t* spec_pages; int64_t spec_page_bytes; int32_t spec_n_pages;
 };
 
 struct ConvArgs {

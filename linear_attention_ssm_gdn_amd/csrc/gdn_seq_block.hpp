@@ -84,9 +84,15 @@ __device__ __forceinline__ void seq_block(const SeqArgs& A, const int block) {
     const int page = A.page_idx[seq];
     const int r0 = A.cu[seq], r1 = A.cu[seq + 1];
     if (page < 0) return;
-    if (page >= A.conv_n_pages || page >= A.state_n_pages) {
+    if (page >= A.conv_n_pages || page >= A.state_n_pages || (A.spec_pages && page >= A.spec_n_pages)) {
         if (tid == 0 && h == 0 && blk == 0) set_err(A.err, GDN_DEVERR_PAGE);
         return;
+    }
+    // The sequence's speculative page, if any, is left fresh (all-zero
+    // header fields: live slot 0 with no record rows, parity 0).
+    if (A.spec_pages && tid == 0 && h == 0 && blk == 0) {
+        uint32_t* hw = reinterpret_cast<uint32_t*>(A.spec_pages + (int64_t)page * A.spec_page_bytes);
+        hw[0] = 0u; hw[1] = 0u; hw[2] = 0u; hw[3] = 0u;
     }
     if (r0 < 0 || r1 < r0 || (int64_t)r1 > A.n_rows) {
         if (tid == 0 && h == 0 && blk == 0) set_err(A.err, GDN_DEVERR_BATCH);

@@ -252,6 +252,11 @@ class SpecPages:
         """[n_pages][64] uint32 view of every page header."""
         return self.buf[:, self.lay["header_off"]:self.lay["header_off"] + 256].view(torch.int32)
 
+    def checkpoint_pool(self) -> "StatePool":
+        """A state pool aliased onto the pages' checkpoints (slot 0): a
+        sequence call through it writes its final states into the pages."""
+        return StatePool(self.states()[:, 0])
+
     def states(self) -> torch.Tensor:
         """[n_pages][n_slots][h_v][d_k][d_v] view of the state region."""
         d = self.dims
@@ -286,7 +291,8 @@ def gdn_mixed_step(dims: Dims, params: Params, seq: Optional[dict] = None, verif
                    err: Optional[torch.Tensor] = None) -> None:
     """One launch for a step mixing token-by-token sequences and verify requests.
 
-    seq:    dict(x, a, b, batch, conv, state, o) -- the arguments of gdn_recurrent_seq
+    seq:    dict(x, a, b, batch, conv, state, o) -- the arguments of gdn_recurrent_seq, and
+            optionally spec_pages (SpecPages) whose headers the sequences leave fresh
     verify: dict(pages, x, a, b, n_req, n_cand, req_page, num_accepted, step_parity, conv, o)
             -- the arguments of gdn_spec_verify (pages: SpecPages)
     Outputs are written into the o tensors given."""
@@ -299,9 +305,11 @@ def gdn_mixed_step(dims: Dims, params: Params, seq: Optional[dict] = None, verif
             raise ValueError("a and b must share their row stride")
         bt = seq["batch"].c()
         keep.append(bt)
+        spg = seq.get("spec_pages")
         sp = L.GdnSeqPart(seq["x"].data_ptr(), _rows(seq["x"], "x"), seq["a"].data_ptr(), seq["b"].data_ptr(),
                           _rows(seq["a"], "a"), ctypes.pointer(bt), seq["conv"].c(), seq["state"].c(),
-                          seq["o"].data_ptr())
+                          seq["o"].data_ptr(), spg.buf.data_ptr() if spg is not None else None,
+                          spg.buf.stride(0) if spg is not None else 0, spg.buf.shape[0] if spg is not None else 0)
         stream_of = seq["x"]
     if verify is not None:
         v = verify

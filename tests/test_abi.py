@@ -295,6 +295,12 @@ def test_mixed_step_validation(so, L):
     assert call(seq=seq_part(batch=empty), ver=ver_part(layout=2)) == 1
     assert call(ver=ver_part(pages=FAKE + 16)) == 1
     assert call(seq=seq_part(), dims=_dims(L, d_k=96)) == 2
+    sp = seq_part(batch=empty)
+    for pages, nbytes in ((FAKE + 64, 1024), (FAKE, 1000), (FAKE, 0)):
+        sp.spec_pages, sp.spec_page_bytes, sp.spec_n_pages = pages, nbytes, 4
+        assert call(seq=sp) == 1, (pages, nbytes)
+    sp.spec_pages, sp.spec_page_bytes = FAKE, lay.page_bytes
+    assert call(seq=sp) == 0                                     # empty batch: validated, nothing launched
 
 
 def test_conv_update_validation(so, L):

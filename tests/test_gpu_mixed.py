@@ -139,3 +139,92 @@ def test_mixed_step_slots_layout():
                 assert torch.equal(got, ref)
         for got, ref in zip(snap_f, snap_s):
             assert torch.equal(got, ref)
+
+
+def _prefill_then_verify(state_dtype, via_spec_pages):
+    """Prefill four sequences, then run verify steps on their pages.  Either
+    the prefill writes straight into the speculative pages (state pool
+    aliased onto the checkpoints, spec_pages set, headers left fresh), or it
+    runs on a separate state pool whose states are copied into the pages and
+    whose headers are zeroed by hand."""
+    g = gdn()
+    ws, wv = _workloads(state_dtype, seed=73)
+    wv = wv.replace(n_req=4)
+    si = wk.make_sequence_inputs(ws)
+    vi = wk.make_verify_inputs(wv)
+    dims = dims_of(ws, n_spec=wv.n_cand - 1)
+    n = len(ws.seqlens)
+    conv = g.ConvPool.alloc(dims, n, 3 + dims.n_spec, DEV)
+    pages = g.SpecPages.alloc(dims, 0, n, DEV)
+    pages.header()[:, :4] = torch.tensor([0x301, 5, 7, 3], dtype=torch.int32, device=DEV)  # a stale record
+    for s in range(n):
+        conv.buf[s, :3] = dev(si["window0"][s], dims.act_torch)
+    params = params_of(si, ws)
+    x, a, b = dev(si["x"], dims.act_torch), dev(si["a"], dims.act_torch), dev(si["b"], dims.act_torch)
+    batch = make_batch(si["cu_seqlens"], list(range(n)), x.shape[0])
+    o_pref = torch.full((x.shape[0], ws.h_v, ws.d_v), float("nan"), device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    if via_spec_pages:
+        state = pages.checkpoint_pool()
+        state.buf.copy_(dev(si["S0"], dims.state_torch))
+        g.gdn_mixed_step(dims, params, seq=dict(x=x, a=a, b=b, batch=batch, conv=conv, state=state, o=o_pref,
+                                                spec_pages=pages), err=err)
+    else:
+        state = g.StatePool(dev(si["S0"], dims.state_torch))
+        g.gdn_recurrent_seq(dims, params, x, a, b, batch, conv, state, o=o_pref, err=err)
+        pages.states()[:, 0] = state.buf
+        pages.header().zero_()
+    outs = [o_pref.clone()]
+    rp = torch.arange(n, dtype=torch.int32, device=DEV)
+    R, K, C = n, wv.n_cand, ws.c_conv
+    for step in range(wv.n_steps):
+        acc = torch.tensor(np.asarray(vi["accepted"][step - 1] if step else np.zeros(R), np.int32), device=DEV)
+        o = torch.full((R * K, ws.h_v, ws.d_v), float("nan"), device=DEV)
+        g.gdn_spec_verify(dims, params, pages, dev(vi["x"][step].reshape(R * K, C), dims.act_torch),
+                          dev(vi["a"][step].reshape(R * K, ws.h_v), dims.act_torch),
+                          dev(vi["b"][step].reshape(R * K, ws.h_v), dims.act_torch), R, K, rp, acc,
+                          torch.full((R,), (step + 1) & 1, dtype=torch.uint8, device=DEV), conv, o=o, err=err)
+        outs.append(o.view(R, K, ws.h_v, ws.d_v).clone())
+    g.gdn_spec_verify(dims, params, pages, None, None, None, R, 0, rp,
+                      torch.tensor(np.asarray(vi["accepted"][wv.n_steps - 1], np.int32), device=DEV),
+                      torch.full((R,), (wv.n_steps + 1) & 1, dtype=torch.uint8, device=DEV), conv, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    return outs, pages, conv, (ws, wv, si, vi)
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
+def test_prefill_into_spec_pages_equals_copy_and_zero(state_dtype):
+    got, pages_a, conv_a, _ = _prefill_then_verify(state_dtype, True)
+    ref, pages_b, conv_b, _ = _prefill_then_verify(state_dtype, False)
+    for g_, r_ in zip(got, ref):
+        assert not torch.isnan(g_).any()
+        assert torch.equal(g_, r_)
+    assert torch.equal(pages_a.buf, pages_b.buf)
+    assert torch.equal(conv_a.buf, conv_b.buf)
+
+
+def test_prefill_into_spec_pages_oracle_parity(ora):
+    """Prefill through the mixed step into the pages, then verify steps:
+    against the oracle's layer on the prefill followed by its verify
+    semantics from the prefill's final state and window (1e-4)."""
+    outs, pages, conv, (ws, wv, si, vi) = _prefill_then_verify(wk.F32, True)
+    dm = ora.dims_of(ws)
+    o_ref, win, S = ora.layer(dm, si["conv_w"], si["a_log"], si["dt_bias"], si["x"], si["a"], si["b"],
+                              si["cu_seqlens"], si["window0"], si["S0"])
+    vo_ref, win2, S2 = ora.verify(dm, vi["conv_w"], vi["a_log"], vi["dt_bias"], vi["x"], vi["a"], vi["b"],
+                                  vi["accepted"], win, S)
+    from gpu_util import host, max_slice_rel_o
+    assert max_slice_rel_o(host(outs[0]), o_ref, si["cu_seqlens"]) <= 1e-4
+    got = np.stack([host(t) for t in outs[1:]])       # [steps][req][cand][h_v][d_v]
+    worst = 0.0
+    for r in range(wv.n_req):
+        for h in range(ws.h_v):
+            ref = vo_ref[:, r, :, h]
+            worst = max(worst, np.abs(got[:, r, :, h] - ref).max() / np.abs(ref).max())
+    assert worst <= 1e-4, worst
+    St = host(pages.states()[:, 0])
+    for r in range(wv.n_req):
+        for h in range(ws.h_v):
+            assert np.abs(St[r, h] - S2[r, h]).max() / np.abs(S2[r, h]).max() <= 1e-4
+    np.testing.assert_array_equal(host(conv.buf[:, :3]), win2)
