@@ -217,3 +217,35 @@ def test_padding_requests_are_skipped():
     o = run.step(0, np.zeros(4, np.int32))
     assert torch.isnan(o[1]).all() and not torch.isnan(o[0]).any()
     assert torch.equal(run.pages.buf[1], before[1]) and torch.equal(run.pages.buf[4], before[4])
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
+def test_prefix_snapshot_after_commit_continues_bit_identically(state_dtype):
+    """One page per request with a prefix cache ("r9700-stack v0.2.4" leaves
+    prefix caching to the stock pages): after a commit-only step the
+    checkpoint and conv rows 0..2 hold the committed prefix and the record is
+    empty, so a cached copy of them, restored into fresh pages (all-zero
+    header), continues exactly as the original request does."""
+    wl = _small(n_steps=8)
+    inp = _inputs(wl, state_dtype)
+    zero = np.zeros(wl.n_req, np.int32)
+    A = VerifyRun(wl, inp, ONEPAGE, state_dtype)
+    for s in range(4):
+        A.step(s, inp["accepted"][s - 1] if s else zero)
+    A.step(0, inp["accepted"][3], n_cand=0)              # commit: the prefix cache point
+    cached_S = A.committed_state().clone()
+    cached_W = A.committed_window().clone()
+    hdr = A.pages.header()[A.req_page]
+    assert int(hdr[:, 1 + (int(hdr[0, 0]) & 1)].abs().sum()) == 0   # the live record holds no rows
+    B = VerifyRun(wl, inp, ONEPAGE, state_dtype)
+    B.pages.states()[B.req_page, 0] = cached_S
+    B.conv.buf[B.req_page, :3] = cached_W
+    for s in range(4, 8):
+        prev = inp["accepted"][s - 1] if s > 4 else zero
+        oa, ob = A.step(s, prev), B.step(s, prev)
+        assert torch.equal(oa, ob), s
+    A.step(0, inp["accepted"][7], n_cand=0)
+    B.step(0, inp["accepted"][7], n_cand=0)
+    assert torch.equal(A.committed_state(), B.committed_state())
+    assert torch.equal(A.committed_window(), B.committed_window())
+    assert int(A.err.item()) == 0 and int(B.err.item()) == 0
