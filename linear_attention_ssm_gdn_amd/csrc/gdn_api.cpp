@@ -102,7 +102,18 @@ int32_t check_verify_call(const gdn_dims* dims, int32_t layout, const void* x, i
                           const void* b, int64_t ab_stride, int32_t n_req, int32_t n_cand, const int32_t* req_page,
                           const int32_t* num_accepted, const uint8_t* step_parity, const void* pages,
                           int64_t page_bytes, int32_t n_pages, const gdn_conv_pool& conv, const float* o,
-                          gdn_spec_layout* L);
+                          gdn_spec_layout* L) {
+    int32_t st;
+    if ((st = gdn_spec_page_layout(dims, layout, L)) != GDN_OK) return st;
+    if (n_req < 0 || n_cand < 0 || n_cand > dims->n_spec + 1) return GDN_ERR_ARG;
+    if (n_req == 0) return GDN_OK;
+    if (!req_page || !num_accepted || !step_parity || !pages || n_pages < 0) return GDN_ERR_ARG;
+    if (page_bytes < (int64_t)L->page_bytes || page_bytes % 256 != 0 || !aligned(pages, 256)) return GDN_ERR_ARG;
+    if ((st = check_conv_pool(dims, conv, dims->conv_w - 1 + dims->n_spec, true)) != GDN_OK) return st;
+    if (n_cand > 0 && (!x || !a || !b || !o)) return GDN_ERR_ARG;
+    if (n_cand > 0 && (x_stride < c_conv(dims) || ab_stride < dims->h_v)) return GDN_ERR_ARG;
+    return GDN_OK;
+}
 
 gdn::VerifyArgs verify_args(const gdn_dims* dims, const gdn_params* params, const gdn_spec_layout& L, const void* x,
                             int64_t x_stride, const void* a, const void* b, int64_t ab_stride, int32_t n_req,
@@ -285,25 +296,6 @@ GDN_EXPORT int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* param
     return from_hip(gdn::launch_verify(A, dims->d_k, dims->act_dtype, dims->state_dtype, layout,
                                        (hipStream_t)stream));
 }
-
-namespace {
-int32_t check_verify_call(const gdn_dims* dims, int32_t layout, const void* x, int64_t x_stride, const void* a,
-                          const void* b, int64_t ab_stride, int32_t n_req, int32_t n_cand, const int32_t* req_page,
-                          const int32_t* num_accepted, const uint8_t* step_parity, const void* pages,
-                          int64_t page_bytes, int32_t n_pages, const gdn_conv_pool& conv, const float* o,
-                          gdn_spec_layout* L) {
-    int32_t st;
-    if ((st = gdn_spec_page_layout(dims, layout, L)) != GDN_OK) return st;
-    if (n_req < 0 || n_cand < 0 || n_cand > dims->n_spec + 1) return GDN_ERR_ARG;
-    if (n_req == 0) return GDN_OK;
-    if (!req_page || !num_accepted || !step_parity || !pages || n_pages < 0) return GDN_ERR_ARG;
-    if (page_bytes < (int64_t)L->page_bytes || page_bytes % 256 != 0 || !aligned(pages, 256)) return GDN_ERR_ARG;
-    if ((st = check_conv_pool(dims, conv, dims->conv_w - 1 + dims->n_spec, true)) != GDN_OK) return st;
-    if (n_cand > 0 && (!x || !a || !b || !o)) return GDN_ERR_ARG;
-    if (n_cand > 0 && (x_stride < c_conv(dims) || ab_stride < dims->h_v)) return GDN_ERR_ARG;
-    return GDN_OK;
-}
-}  // namespace
 
 GDN_EXPORT int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,
                                   const gdn_verify_part* verify, int32_t* err, void* stream) {
