@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix cores
 FP32_VALU_PEAK_TFLOPS = 157.3    # fp32 vector (256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz)
 POOLS = 4
+LAST_PERCENTILES = {}  # per-launch kernel time percentiles (us) of the last measure()
 
 
 def log(msg):
@@ -116,6 +117,11 @@ class Timer:
 
     def mean_ms(self):
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+
+    def percentiles_us(self):
+        t = np.array([s.elapsed_time(e) for s, e in self.pairs]) * 1e3
+        return {"p10": round(float(np.percentile(t, 10)), 2), "p50": round(float(np.percentile(t, 50)), 2),
+                "p90": round(float(np.percentile(t, 90)), 2)}
 
 
 def _upload(torch, arr, dt):
@@ -247,6 +253,8 @@ def measure(torch, wload, steps, warmup):
         timer.time(wload.launch)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    LAST_PERCENTILES.clear()
+    LAST_PERCENTILES.update(timer.percentiles_us())
     return timer.mean_ms(), wall * 1e3
 
 
@@ -424,7 +432,7 @@ def main():
         "config": {"workload": "decode", "n_seqs": len(wl.seqlens), "tokens_per_seq": 1, "h_k": wl.h_k,
                    "h_v": wl.h_v, "d_k": wl.d_k, "d_v": wl.d_v, "conv_w": wl.conv_w, "act_dtype": wl.act_dtype,
                    "state_dtype": wl.state_dtype, "tokens_per_s_per_layer": round(len(wl.seqlens) / (k_ms * 1e-3)),
-                   "state_pools_rotated": POOLS},
+                   "state_pools_rotated": POOLS, "us_per_step_percentiles": dict(LAST_PERCENTILES)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "k_gdn_seq_stream", "algorithmic_bytes": nbytes},
@@ -443,6 +451,7 @@ def main():
         other["short_prefill"] = {
             "value": round(wl.n_tokens / (k_ms * 1e-3)), "unit": "tokens/s/layer", "us_per_call": round(k_ms * 1e3, 2),
             "us_per_token_critical_path": round(k_ms * 1e3 / max(wl.seqlens), 4),
+            "us_per_call_percentiles": dict(LAST_PERCENTILES),
             "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": read_traffic("k_gdn_seq", "short_prefill"),
                          "kernel": "k_gdn_seq", "algorithmic_flops": fl},
@@ -464,6 +473,7 @@ def main():
             tf = fl / (k_ms * 1e-3) / 1e12
             other["long_prefill"] = {
                 "value": round(wl.n_tokens / (k_ms * 1e-3)), "unit": "tokens/s/layer", "us_per_call": round(k_ms * 1e3, 1),
+                "us_per_call_percentiles": dict(LAST_PERCENTILES),
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                              "traffic": read_traffic("k_gdn_chunk", "long_prefill"), "kernel": "k_gdn_chunk",
@@ -486,7 +496,7 @@ def main():
             k_ms, wall_ms = measure(torch, w, max(args.steps // 2, 10), 10)
             nb = verify_bytes(wl, sd, w.mean_replay)
             gbs = nb / (k_ms * 1e-3) / 1e9
-            res[sd] = {"value": round(k_ms * 1e3, 2), "unit": "us/step",
+            res[sd] = {"value": round(k_ms * 1e3, 2), "unit": "us/step", "us_per_step_percentiles": dict(LAST_PERCENTILES),
                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(gbs / HBM_PEAK_GBS, 4),
                                     "traffic": read_traffic("k_gdn_verify", "spec_verify_" + sd),
