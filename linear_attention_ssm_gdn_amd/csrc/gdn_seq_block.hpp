@@ -88,12 +88,6 @@ __device__ __forceinline__ void seq_block(const SeqArgs& A, const int block) {
         if (tid == 0 && h == 0 && blk == 0) set_err(A.err, GDN_DEVERR_PAGE);
         return;
     }
-    // The sequence's speculative page, if any, is left fresh (all-zero
-    // header fields: live slot 0 with no record rows, parity 0).
-    if (A.spec_pages && tid == 0 && h == 0 && blk == 0) {
-        uint32_t* hw = reinterpret_cast<uint32_t*>(A.spec_pages + (int64_t)page * A.spec_page_bytes);
-        hw[0] = 0u; hw[1] = 0u; hw[2] = 0u; hw[3] = 0u;
-    }
     if (r0 < 0 || r1 < r0 || (int64_t)r1 > A.n_rows) {
         if (tid == 0 && h == 0 && blk == 0) set_err(A.err, GDN_DEVERR_BATCH);
         return;
@@ -101,6 +95,12 @@ __device__ __forceinline__ void seq_block(const SeqArgs& A, const int block) {
     const int T = r1 - r0;
     if (T == 0) return;
     const bool init = A.has_init ? (A.has_init[seq] != 0) : true;
+    // The sequence's speculative page, if any, is left fresh (all-zero
+    // header fields: live slot 0 with no record rows, parity 0).
+    if (A.spec_pages && tid == 0 && h == 0 && blk == 0) {
+        uint32_t* hw = reinterpret_cast<uint32_t*>(A.spec_pages + (int64_t)page * A.spec_page_bytes);
+        hw[0] = 0u; hw[1] = 0u; hw[2] = 0u; hw[3] = 0u;
+    }
 
     // ---- this thread's conv channel
     const ActT* __restrict__ X = static_cast<const ActT*>(A.x);

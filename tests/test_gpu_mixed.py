@@ -228,3 +228,32 @@ def test_prefill_into_spec_pages_oracle_parity(ora):
         for h in range(ws.h_v):
             assert np.abs(St[r, h] - S2[r, h]).max() / np.abs(S2[r, h]).max() <= 1e-4
     np.testing.assert_array_equal(host(conv.buf[:, :3]), win2)
+
+
+def test_spec_pages_empty_sequence_keeps_its_header():
+    """A sequence of length 0 is a no-op: its page keeps its header (and its
+    record) while the other sequences' pages are left fresh."""
+    g = gdn()
+    ws, _ = _workloads(wk.F32, seed=74)
+    ws = ws.replace(seqlens=(20, 0, 5))
+    si = wk.make_sequence_inputs(ws)
+    dims = dims_of(ws, n_spec=7)
+    n = 3
+    conv = g.ConvPool.alloc(dims, n, 3 + dims.n_spec, DEV)
+    pages = g.SpecPages.alloc(dims, 0, n, DEV)
+    stale = torch.tensor([0x301, 5, 7, 3], dtype=torch.int32, device=DEV)
+    pages.header()[:, :4] = stale
+    state = pages.checkpoint_pool()
+    state.buf.copy_(dev(si["S0"], dims.state_torch))
+    before = pages.buf[1].clone()
+    x, a, b = dev(si["x"], dims.act_torch), dev(si["a"], dims.act_torch), dev(si["b"], dims.act_torch)
+    batch = make_batch(si["cu_seqlens"], list(range(n)), x.shape[0])
+    o = torch.full((x.shape[0], ws.h_v, ws.d_v), float("nan"), device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    g.gdn_mixed_step(dims, params_of(si, ws), seq=dict(x=x, a=a, b=b, batch=batch, conv=conv, state=state, o=o,
+                                                       spec_pages=pages), err=err)
+    torch.cuda.synchronize()
+    h = pages.header()
+    assert int(h[0, :4].abs().sum()) == 0 and int(h[2, :4].abs().sum()) == 0
+    assert torch.equal(pages.buf[1], before)
+    assert int(err.item()) == 0 and not torch.isnan(o).any()
