@@ -89,7 +89,10 @@ enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
 // accumulators as accumulator-register operands, so they follow the last
 // product that writes them and precede every read or copy of them.  The one
 // chain that feeds a 16x16x32 result into 16x16x16 products (different pass
-// counts) settles in between as well.
+// counts) settles in between as well.  Results of 16x16x16 products (the UT
+// solve's diagonal blocks and sub-diagonals) are read at the compiler's 8
+// wait states: while 16x16x32 reads failed in nearly every launch, the
+// states, which depend on every UT solve, never differed.
 #define GDN_SETTLE_NOPS "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
 __device__ __forceinline__ void settle(f32x4& a) { asm volatile(GDN_SETTLE_NOPS : "+a"(a)); }
 __device__ __forceinline__ void settle(f32x4& a, f32x4& b) { asm volatile(GDN_SETTLE_NOPS : "+a"(a), "+a"(b)); }
@@ -603,10 +606,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             for (int k = 0; k < 3; ++k) {
                 f32x4 Yn = mma16(to_bf4(Z), to_bf4(Y), zero);  // Y <- Y Y (A operand = layout of Y^T = Z)
                 f32x4 Zn = mma16(to_bf4(Y), to_bf4(Z), zero);  // Z <- Z Z
-                settle(Yn, Zn);
                 Y = Yn; Z = Zn;
                 R = mma16(to_bf4(eye + Z), to_bf4(R), zero);         // R <- (I + Y) R
-                settle(R);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * b + lr] = (__bf16)R[j];
@@ -629,10 +630,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                                         Tm[(16 * d + 4 * lg + 3) * LT + 16 * c + lr]};
                     Xacc = mma16(aop, bop, Xacc);
                 }
-                settle(Xacc);
                 const bf16x4 tbb = ld4(Tm, LT, 16 * b + lr, 16 * b + 4 * lg);
                 f32x4 Yv = mma16(tbb, to_bf4(Xacc), zero);
-                settle(Yv);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * c + lr] = (__bf16)(-Yv[j]);
             }
