@@ -92,11 +92,13 @@ __device__ __forceinline__ float reduce64(float x) {
 //   delta = beta (v - e^g u),  o = e^g w + (k.q) delta,
 //   S <- e^g S + k delta^T.
 // The operations per column do not depend on CPL, so every kernel built on
-// this function produces the same bits for the same column.
+// this function produces the same bits for the same column.  update = false
+// (uniform across the workgroup) gives the same o and leaves S as it was, for
+// a token whose successor state nothing reads.
 template <int R, int CPL>
 __device__ __forceinline__ void delta_step(float (&s)[CPL][R], const float (&k)[R], const float (&q)[R],
                                            const float (&v)[CPL], float eg, float beta, float kq,
-                                           float (&o)[CPL]) {
+                                           float (&o)[CPL], bool update = true) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         float u0 = 0.0f, u1 = 0.0f, w0 = 0.0f, w1 = 0.0f;
@@ -113,8 +115,10 @@ __device__ __forceinline__ void delta_step(float (&s)[CPL][R], const float (&k)[
         const float w = reduce16(w0 + w1);
         const float d = beta * (v[c] - eg * u);
         o[c] = fmaf(kq, d, eg * w);
+        if (update) {
 #pragma unroll
-        for (int m = 0; m < R; ++m) s[c][m] = fmaf(k[m], d, eg * s[c][m]);
+            for (int m = 0; m < R; ++m) s[c][m] = fmaf(k[m], d, eg * s[c][m]);
+        }
     }
 }
 

@@ -331,7 +331,10 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         };
         auto step = [&](const Opnd& p, int tt) {
             float o[CPL];
-            delta_step<R, CPL>(s, p.k, p.q, p.v, p.eg, p.beta, p.kq, o);
+            // one-page: nothing reads the state after the last candidate (the
+            // next step replays from the checkpoint), so its update is skipped
+            delta_step<R, CPL>(s, p.k, p.q, p.v, p.eg, p.beta, p.kq, o,
+                               !(LAYOUT == GDN_SPEC_ONEPAGE && tt == nc - 1));
             if (writer) {
                 float* dst = O + (int64_t)tt * o_stride;
                 if constexpr (CPL == 4) {
