@@ -249,3 +249,34 @@ def test_prefix_snapshot_after_commit_continues_bit_identically(state_dtype):
     assert torch.equal(A.committed_state(), B.committed_state())
     assert torch.equal(A.committed_window(), B.committed_window())
     assert int(A.err.item()) == 0 and int(B.err.item()) == 0
+
+
+@pytest.mark.parametrize("n_cand", [12, 16])
+def test_more_candidates_than_half_the_token_rows(ora, n_cand):
+    """Steps whose candidates (or replayed rows) exceed half of the kernel's
+    16 token rows run the replay and the candidates through the same rows
+    one after the other, up to the page layout's maximum of 16 candidates:
+    one-page equals slots bit for bit and the oracle within 1e-4."""
+    wl = _small(n_req=4, n_steps=5, n_cand=n_cand, seed=37)
+    inp = _inputs(wl, wk.F32)
+    inp["accepted"][1] = n_cand - 1          # a full-length replay in step 2
+    one = VerifyRun(wl, inp, ONEPAGE, wk.F32)
+    o1 = one.run()
+    slots = VerifyRun(wl, inp, SLOTS, wk.F32)
+    o2 = slots.run()
+    assert torch.equal(o1, o2)
+    assert torch.equal(one.committed_state(), slots.committed_state())
+    assert torch.equal(one.committed_window(), slots.committed_window())
+    dm = ora.dims_of(wl)
+    o_ref, win_ref, S_ref = ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"],
+                                       inp["b"], inp["accepted"], inp["window0"], inp["S0"])
+    o = host(o1)
+    worst = max(float(np.abs(o[:, r, :, h] - o_ref[:, r, :, h]).max() / np.abs(o_ref[:, r, :, h]).max())
+                for r in range(wl.n_req) for h in range(wl.h_v))
+    assert worst <= 1e-4, worst
+    S = host(one.committed_state())
+    worstS = max(float(np.abs(S[r, h] - S_ref[r, h]).max() / np.abs(S_ref[r, h]).max())
+                 for r in range(wl.n_req) for h in range(wl.h_v))
+    assert worstS <= 1e-4, worstS
+    np.testing.assert_array_equal(host(one.committed_window()), win_ref)
+    assert int(one.err.item()) == 0 and int(slots.err.item()) == 0
