@@ -168,16 +168,28 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
     // One-page: the replayed rows go straight into the LDS rows 0 .. n_replay-1,
     // all in flight at once: lane l of a wave lands at base + 4 l, and each
     // region's base is chosen so that lane lc writes its own channel's slot.
+    // That placement was checked for loads whose lanes start at lane 0 of
+    // their wave.  With d_k not a multiple of 64 the k channels start inside
+    // a wave (lane d_k), and there the replayed rows came out wrong (at
+    // d_k = 32 the one-page states left those of the slot design from the
+    // first replay on, consistent with the k row landing 32 floats early), so
+    // for such d_k the rows go through registers.
     if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
-        const int wbase = tid & ~63;
-        for (int i = 0; i < n_replay; ++i) {
-            const float* row = reinterpret_cast<const float*>(rec + i * row_bytes);
-            if (lc < DK)
-                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
-            else if (lc < 2 * DK)
-                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
-            else if (lc < NLC)
-                load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sv + i * BV + wbase - 2 * DK));
+        if constexpr (DK % 64 == 0) {
+            const int wbase = tid & ~63;
+            for (int i = 0; i < n_replay; ++i) {
+                const float* row = reinterpret_cast<const float*>(rec + i * row_bytes);
+                if (lc < DK)
+                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
+                else if (lc < 2 * DK)
+                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
+                else if (lc < NLC)
+                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sv + i * BV + wbase - 2 * DK));
+            }
+        } else {
+            if (lc < NLC)
+                for (int i = 0; i < n_replay; ++i)
+                    ydst[i * yld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc];
         }
     }
     // Every small input is taken (waited for) here, before the state's loads
