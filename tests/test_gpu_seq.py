@@ -296,3 +296,14 @@ def test_decode_stream_d64_two_blocks(ora):
     inp = wk.make_sequence_inputs(wl)
     n = len(wl.seqlens)
     _check_pages(ora, wl, inp, list(range(n)), None, n)
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
+def test_decode_stream_d32(ora, state_dtype):
+    """d_k = 32 (two state rows per lane in the staged layout) with d_v = 128
+    through the streaming kernel, fp32 and bf16 state."""
+    wl = wk.Workload("d32v128", h_k=4, h_v=8, d_k=32, d_v=128, conv_w=4, act_dtype=wk.BF16,
+                     state_dtype=state_dtype, seqlens=(1, 3, 4, 1, 2, 0, 1) * 10, seed=23)
+    inp = wk.make_sequence_inputs(wl)
+    n = len(wl.seqlens)
+    _check_pages(ora, wl, inp, list(range(n)), None, n, s_tol=TOL if state_dtype == wk.F32 else 2.0 ** -8)

@@ -302,3 +302,22 @@ def test_other_head_dims(ora, d_k, d_v):
                 for r in range(wl.n_req) for h in range(wl.h_v))
     assert worst <= 1e-4, worst
     np.testing.assert_array_equal(host(one.committed_window()), win_ref)
+
+
+def test_fp32_activations(ora):
+    """fp32 activations (x, a, b, conv weights and buffer): one-page equals
+    slots bit for bit and the oracle within 1e-4."""
+    wl = _small(n_req=3, n_steps=4, h_k=2, h_v=4, act_dtype=wk.F32, seed=41)
+    inp = _inputs(wl, wk.F32)
+    one = VerifyRun(wl, inp, ONEPAGE, wk.F32)
+    o1 = one.run()
+    slots = VerifyRun(wl, inp, SLOTS, wk.F32)
+    assert torch.equal(o1, slots.run())
+    dm = ora.dims_of(wl)
+    o_ref, win_ref, S_ref = ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"],
+                                       inp["b"], inp["accepted"], inp["window0"], inp["S0"])
+    o = host(o1)
+    worst = max(float(np.abs(o[:, r, :, h] - o_ref[:, r, :, h]).max() / np.abs(o_ref[:, r, :, h]).max())
+                for r in range(wl.n_req) for h in range(wl.h_v))
+    assert worst <= 1e-4, worst
+    np.testing.assert_array_equal(host(one.committed_window()), win_ref)
