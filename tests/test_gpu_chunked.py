@@ -115,3 +115,12 @@ def test_identical_launches_are_bit_identical():
         assert torch.equal(again[0], first[0])
         assert torch.equal(again[1].buf, first[1].buf)
         assert torch.equal(again[2].buf, first[2].buf)
+
+
+@pytest.mark.parametrize("d_v", [64, 192])
+def test_chunked_other_value_widths(ora, d_v):
+    """One and three 64-column blocks per value head (the rolled q/k window
+    is handed to the last of r * blocks workgroups)."""
+    wl = _small((130, 64, 7), seed=46, h_k=2, h_v=4, d_v=d_v)
+    inp = wk.make_sequence_inputs(wl)
+    _check(ora, wl, inp)

@@ -307,3 +307,14 @@ def test_decode_stream_d32(ora, state_dtype):
     inp = wk.make_sequence_inputs(wl)
     n = len(wl.seqlens)
     _check_pages(ora, wl, inp, list(range(n)), None, n, s_tol=TOL if state_dtype == wk.F32 else 2.0 ** -8)
+
+
+def test_more_sequences_than_threads(ora):
+    """More sequences than a workgroup has threads (600 > 512): the
+    longest-first ranking is off and workgroups keep the batch order."""
+    rng = np.random.default_rng(24)
+    lens = tuple(int(x) for x in rng.integers(5, 9, size=600))
+    wl = wk.TINY.replace(seqlens=lens, h_k=1, h_v=2, s0_std=0.05, window_std=1.0, seed=24)
+    inp = wk.make_sequence_inputs(wl)
+    n = len(lens)
+    _check_pages(ora, wl, inp, list(range(n)), None, n)
