@@ -318,3 +318,12 @@ def test_more_sequences_than_threads(ora):
     inp = wk.make_sequence_inputs(wl)
     n = len(lens)
     _check_pages(ora, wl, inp, list(range(n)), None, n)
+
+
+@pytest.mark.parametrize("n", [1, 3])
+def test_decode_stream_fewer_items_than_workgroups(ora, n):
+    """One and three decode sequences: fewer (sequence, head) items than the
+    resident grid, every workgroup takes at most one item."""
+    wl = wk.DECODE.replace(seqlens=(1,) * n, seed=25)
+    inp = wk.make_sequence_inputs(wl)
+    _check_pages(ora, wl, inp, list(range(n)), None, n)

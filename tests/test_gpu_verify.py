@@ -282,25 +282,27 @@ def test_more_candidates_than_half_the_token_rows(ora, n_cand):
     assert int(one.err.item()) == 0 and int(slots.err.item()) == 0
 
 
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
 @pytest.mark.parametrize("d_k,d_v", [(64, 96), (32, 32)])
-def test_other_head_dims(ora, d_k, d_v):
+def test_other_head_dims(ora, d_k, d_v, state_dtype):
     """Head dims other than 128: d_k = 64 and 32 with value blocks of 32
     columns (d_v not a multiple of 128), one-page equals slots bit for bit
-    and the oracle within 1e-4."""
-    wl = _small(n_req=3, n_steps=4, h_k=2, h_v=4, d_k=d_k, d_v=d_v, seed=39)
-    inp = _inputs(wl, wk.F32)
-    one = VerifyRun(wl, inp, ONEPAGE, wk.F32)
+    and the oracle within 1e-4 (3e-3 with bf16 checkpoints)."""
+    wl = _small(n_req=3, n_steps=4, h_k=2, h_v=4, d_k=d_k, d_v=d_v, seed=39, state_dtype=state_dtype)
+    inp = _inputs(wl, state_dtype)
+    one = VerifyRun(wl, inp, ONEPAGE, state_dtype)
     o1 = one.run()
-    slots = VerifyRun(wl, inp, SLOTS, wk.F32)
+    slots = VerifyRun(wl, inp, SLOTS, state_dtype)
     assert torch.equal(o1, slots.run())
     assert torch.equal(one.committed_state(), slots.committed_state())
     dm = ora.dims_of(wl)
     o_ref, win_ref, S_ref = ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"],
-                                       inp["b"], inp["accepted"], inp["window0"], inp["S0"])
+                                       inp["b"], inp["accepted"], inp["window0"], inp["S0"],
+                                       state_bf16=(state_dtype == wk.BF16))
     o = host(o1)
     worst = max(float(np.abs(o[:, r, :, h] - o_ref[:, r, :, h]).max() / np.abs(o_ref[:, r, :, h]).max())
                 for r in range(wl.n_req) for h in range(wl.h_v))
-    assert worst <= 1e-4, worst
+    assert worst <= (1e-4 if state_dtype == wk.F32 else 3e-3), worst
     np.testing.assert_array_equal(host(one.committed_window()), win_ref)
 
 
