@@ -17,8 +17,8 @@ N_SEQ_PAGES = 4      # pages 0..3: token-by-token sequences
 N_REQ = 6            # pages 4..9: verify requests
 
 
-def _workloads(state_dtype, seed):
-    base = dict(h_k=4, h_v=8, d_k=128, d_v=128, conv_w=4, act_dtype=wk.BF16, state_dtype=state_dtype, seed=seed)
+def _workloads(state_dtype, seed, d_k=128, d_v=128):
+    base = dict(h_k=4, h_v=8, d_k=d_k, d_v=d_v, conv_w=4, act_dtype=wk.BF16, state_dtype=state_dtype, seed=seed)
     ws = wk.Workload("mixed_seq", seqlens=(45, 83, 17, 1), **base)
     wv = wk.Workload("mixed_verify", n_req=N_REQ, n_cand=8, n_steps=3, **base)
     return ws, wv
@@ -77,8 +77,8 @@ def _step_args(w, ws, wv, si, vi, step, seq_rows, seq_cu, pages, vstep):
     return seq, ver
 
 
-def _run(layout, state_dtype, fused):
-    ws, wv = _workloads(state_dtype, seed=71)
+def _run(layout, state_dtype, fused, d_k=128, d_v=128):
+    ws, wv = _workloads(state_dtype, seed=71, d_k=d_k, d_v=d_v)
     si = wk.make_sequence_inputs(ws)
     vi = wk.make_verify_inputs(wv)
     w = World(ws, wv, si, vi, layout)
@@ -257,3 +257,18 @@ def test_spec_pages_empty_sequence_keeps_its_header():
     assert int(h[0, :4].abs().sum()) == 0 and int(h[2, :4].abs().sum()) == 0
     assert torch.equal(pages.buf[1], before)
     assert int(err.item()) == 0 and not torch.isnan(o).any()
+
+
+@pytest.mark.parametrize("d_k,d_v", [(64, 96), (32, 32)])
+def test_mixed_step_small_head_dims(d_k, d_v):
+    """The mixed kernel's instantiations with 32-column verify blocks
+    (d_v not a multiple of 128), including d_k = 32."""
+    fused = _run(0, wk.F32, True, d_k, d_v)
+    sep = _run(0, wk.F32, False, d_k, d_v)
+    for (so_f, vo_f, snap_f), (so_s, vo_s, snap_s) in zip(fused, sep):
+        for got, ref in ((so_f, so_s), (vo_f, vo_s)):
+            if got is not None:
+                assert not torch.isnan(got).any()
+                assert torch.equal(got, ref)
+        for got, ref in zip(snap_f, snap_s):
+            assert torch.equal(got, ref)
