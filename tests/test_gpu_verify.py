@@ -323,3 +323,43 @@ def test_fp32_activations(ora):
                 for r in range(wl.n_req) for h in range(wl.h_v))
     assert worst <= 1e-4, worst
     np.testing.assert_array_equal(host(one.committed_window()), win_ref)
+
+
+def test_candidate_count_varies_between_steps(ora):
+    """Steps with 8, 3, 1, 8 and 5 candidates: the conv buffer rolls by the
+    width the record holds, not by the current step's ("A defect found and
+    fixed before the tag" of "r9700-stack v0.2.4").  Checked against the
+    oracle run one step at a time from each step's committed state and
+    window, and one-page against slots bit for bit."""
+    Ks = (8, 3, 1, 8, 5)
+    wl = _small(n_req=3, n_steps=len(Ks), seed=43)
+    inp = _inputs(wl, wk.F32)
+    rng = np.random.default_rng(43)
+    acc = np.stack([rng.integers(0, K, size=wl.n_req) for K in Ks]).astype(np.int32)
+    runs = {lay: VerifyRun(wl, inp, lay, wk.F32) for lay in (ONEPAGE, SLOTS)}
+    outs = {lay: [] for lay in runs}
+    zero = np.zeros(wl.n_req, np.int32)
+    for s, K in enumerate(Ks):
+        for lay, run in runs.items():
+            outs[lay].append(host(run.step(s, acc[s - 1] if s else zero, n_cand=K)))
+    for run in runs.values():
+        run.step(0, acc[-1], n_cand=0)
+    for a, b in zip(outs[ONEPAGE], outs[SLOTS]):
+        assert np.array_equal(a, b)
+    dm = ora.dims_of(wl)
+    win, S = inp["window0"], inp["S0"]
+    for s, K in enumerate(Ks):
+        o_ref, win, S = ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"][s:s + 1, :, :K],
+                                   inp["a"][s:s + 1, :, :K], inp["b"][s:s + 1, :, :K], acc[s:s + 1], win, S)
+        got = outs[ONEPAGE][s]
+        for r in range(wl.n_req):
+            for h in range(wl.h_v):
+                ref = o_ref[0, r, :, h]
+                assert np.abs(got[r, :, h] - ref).max() <= 1e-4 * np.abs(ref).max(), (s, r, h)
+    one = runs[ONEPAGE]
+    np.testing.assert_array_equal(host(one.committed_window()), win)
+    Sg = host(one.committed_state())
+    for r in range(wl.n_req):
+        for h in range(wl.h_v):
+            assert np.abs(Sg[r, h] - S[r, h]).max() <= 1e-4 * np.abs(S[r, h]).max()
+    assert int(one.err.item()) == 0
