@@ -124,3 +124,13 @@ def test_chunked_other_value_widths(ora, d_v):
     wl = _small((130, 64, 7), seed=46, h_k=2, h_v=4, d_v=d_v)
     inp = wk.make_sequence_inputs(wl)
     _check(ora, wl, inp)
+
+
+def test_chunked_more_sequences_than_threads(ora):
+    """300 sequences (more than the 256 threads that rank them): the
+    longest-first ranking is off and workgroups keep the batch order."""
+    rng = np.random.default_rng(47)
+    lens = tuple(int(x) for x in rng.integers(1, 70, size=300))
+    wl = _small(lens, seed=47, h_k=1, h_v=2, d_v=64)
+    inp = wk.make_sequence_inputs(wl)
+    _check(ora, wl, inp)
