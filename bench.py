@@ -305,6 +305,50 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"repeated {n} times in {budget_s:.0f} s"}
 
 
+def cpu_other_workloads(budget_s=4.0):
+    """The fp64 oracle on bounded samples of the other workloads (context
+    beside each GPU figure; the headline's baseline is cpu_baseline)."""
+    import oracle as ora
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    out = {}
+
+    def timed(fn):
+        fn()  # load + warm
+        n, t0 = 0, time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < budget_s:
+            fn()
+            n += 1
+        return (time.perf_counter() - t0) / n, n
+
+    # short prefill: the whole ragged batch
+    wl = wk.SHORT_PREFILL
+    inp = wk.make_sequence_inputs(wl)
+    dm = ora.dims_of(wl)
+    dt, n = timed(lambda: ora.layer(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"], inp["b"],
+                                    inp["cu_seqlens"], inp["window0"], inp["S0"]))
+    out["short_prefill"] = {"value": round(wl.n_tokens / dt), "unit": "tokens/s/layer", "cores": threads,
+                            "kind": "oracle", "sample": f"the whole batch ({wl.n_tokens} tokens), {n} runs"}
+    # long prefill: the first 1024 tokens of one sequence (the oracle's cost is linear in tokens)
+    T = 1024
+    wl = wk.LONG_PREFILL.replace(seqlens=(T,))
+    inp = wk.make_sequence_inputs(wl)
+    dm = ora.dims_of(wl)
+    dt, n = timed(lambda: ora.layer(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"], inp["b"],
+                                    inp["cu_seqlens"], inp["window0"], inp["S0"]))
+    out["long_prefill"] = {"value": round(T / dt), "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
+                           "sample": f"one sequence of {T} tokens, all {wl.h_v} heads, {n} runs (sequential form)"}
+    # verify: all steps of the workload, per step
+    wl = wk.SPEC_VERIFY
+    inp = wk.make_verify_inputs(wl)
+    dm = ora.dims_of(wl)
+    dt, n = timed(lambda: ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"], inp["b"],
+                                     inp["accepted"], inp["window0"], inp["S0"]))
+    out["spec_verify"] = {"value": round(dt / wl.n_steps * 1e6, 1), "unit": "us/step", "cores": threads,
+                          "kind": "oracle", "sample": f"{wl.n_steps} steps x {wl.n_req} requests x {wl.n_cand} "
+                                                      f"candidates, fp32 state, {n} runs"}
+    return out
+
+
 # ------------------------------------------------------ dispatch sweep
 SWEEP_SEQS = (1, 2, 4, 8, 16, 32)
 SWEEP_LENS = (16, 32, 64, 96, 128, 192, 256, 384, 512, 768, 1024, 2048, 4096, 8192)
@@ -537,6 +581,10 @@ def main():
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wk.DECODE)
+        log("cpu oracle on the other workloads")
+        for name, base in cpu_other_workloads().items():
+            if name in other and isinstance(other[name], dict):
+                other[name]["cpu_baseline"] = base
     print(json.dumps(result), flush=True)
 
 
