@@ -10,7 +10,8 @@
 //                    column group cg = 4w + (l >> 4)  (columns cg*CPL .. +CPL-1).
 // CPL = 1 suits long token loops (fewest operations per token on the
 // critical path); CPL = 4 suits decode and verify (a whole 128-column head
-// per workgroup, loaded with 16-byte vector loads straight into registers).
+// per workgroup, loaded with 16-byte vector loads straight into registers);
+// CPL = 2 serves decode on heads of 64 columns.
 #pragma once
 
 #include "gdn_device.hpp"
@@ -40,9 +41,27 @@ template <> struct RowVec<float, 4> {
         *reinterpret_cast<f32x4v*>(p) = t;
     }
 };
+template <> struct RowVec<float, 2> {
+    __device__ static void load(const float* p, float (&v)[2]) {
+        const float2 t = *reinterpret_cast<const float2*>(p);
+        v[0] = t.x; v[1] = t.y;
+    }
+    __device__ static void store(float* p, const float (&v)[2]) {
+        *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    }
+};
 template <> struct RowVec<bf16_t, 1> {
     __device__ static void load(const bf16_t* p, float (&v)[1]) { v[0] = to_f32(*p); }
     __device__ static void store(bf16_t* p, const float (&v)[1]) { *p = f32_to_bf16(v[0]); }
+};
+template <> struct RowVec<bf16_t, 2> {
+    __device__ static void load(const bf16_t* p, float (&v)[2]) {
+        const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
+        v[0] = __uint_as_float(t << 16); v[1] = __uint_as_float(t & 0xffff0000u);
+    }
+    __device__ static void store(bf16_t* p, const float (&v)[2]) {
+        *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    }
 };
 template <> struct RowVec<bf16_t, 4> {
     __device__ static void load(const bf16_t* p, float (&v)[4]) {
@@ -185,6 +204,71 @@ template <int DK> struct StateStage<bf16_t, DK, 4> {
     }
 };
 
+// fp32, 2 columns (a 64-column block): a row is 16 pieces of 16 bytes.
+// Load instruction m of wave w covers rows 4(wR/2+m) .. 4(wR/2+m)+3; lane l
+// takes row 4(wR/2+m) + l/16, piece (l mod 16) ^ rowgroup(row), and lands at
+// m * 8 KiB + w * 1 KiB + 16 l.  A lane's two columns 2cg, 2cg+1 are the
+// half (cg mod 2) of piece cg/2.
+template <int DK> struct StateStage<float, DK, 2> {
+    static constexpr int R = DK / 16;
+    static_assert(R % 2 == 0, "four rows per wave load");
+    static constexpr int BYTES = R * BLOCK_THREADS * 8;
+    __device__ static void fetch(const float* blk, int64_t ld, unsigned char* stage, int tid) {
+        const int w = tid >> 6, l = tid & 63;
+        unsigned char* wbase = stage + w * 1024;
+#pragma unroll
+        for (int m = 0; m < R / 2; ++m) {
+            const int r = 4 * (w * (R / 2) + m) + (l >> 4);
+            const int piece = (l & 15) ^ ((r / R) & 15);
+            __builtin_amdgcn_global_load_lds((gmem_void*)(blk + (int64_t)r * ld + piece * 4),
+                                             (lds_void*)(wbase + m * BLOCK_THREADS * 16), 16, 0, 0);
+        }
+    }
+    __device__ static void read(const unsigned char* stage, int tid, float (&s)[2][R]) {
+        const int rg = lane_rowgroup(tid), cg = lane_colgroup(tid);
+#pragma unroll
+        for (int mm = 0; mm < R; ++mm) {
+            const int r = rg * R + mm;
+            const int q = r >> 2, w = q / (R / 2), m = q % (R / 2);
+            const int l = ((r & 3) << 4) | ((cg >> 1) ^ rg);
+            const float2 t = *reinterpret_cast<const float2*>(stage + m * BLOCK_THREADS * 16 + w * 1024 + l * 16 +
+                                                              (cg & 1) * 8);
+            s[0][mm] = t.x; s[1][mm] = t.y;
+        }
+    }
+};
+
+// bf16, 2 columns: a row is 32 pieces of 4 bytes (two columns each).  Load
+// instruction m of wave w covers rows 2(wR+m) and 2(wR+m)+1; lane l takes
+// row 2(wR+m) + l/32, piece (l mod 32) ^ rowgroup(row), and lands at
+// m * 2 KiB + w * 256 B + 4 l.  A lane's two columns are piece cg.
+template <int DK> struct StateStage<bf16_t, DK, 2> {
+    static constexpr int R = DK / 16;
+    static constexpr int BYTES = R * BLOCK_THREADS * 4;
+    __device__ static void fetch(const bf16_t* blk, int64_t ld, unsigned char* stage, int tid) {
+        const int w = tid >> 6, l = tid & 63;
+        unsigned char* wbase = stage + w * 256;
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            const int r = 2 * (w * R + m) + (l >> 5);
+            const int piece = (l & 31) ^ ((r / R) & 15);
+            __builtin_amdgcn_global_load_lds((gmem_void*)(blk + (int64_t)r * ld + 2 * piece),
+                                             (lds_void*)(wbase + m * BLOCK_THREADS * 4), 4, 0, 0);
+        }
+    }
+    __device__ static void read(const unsigned char* stage, int tid, float (&s)[2][R]) {
+        const int rg = lane_rowgroup(tid), cg = lane_colgroup(tid);
+#pragma unroll
+        for (int mm = 0; mm < R; ++mm) {
+            const int r = rg * R + mm;
+            const int q = r >> 1, w = q / R, m = q % R;
+            const int l = ((r & 1) << 5) | (cg ^ rg);
+            const uint32_t t = *reinterpret_cast<const uint32_t*>(stage + m * BLOCK_THREADS * 4 + w * 256 + l * 4);
+            s[0][mm] = __uint_as_float(t << 16); s[1][mm] = __uint_as_float(t & 0xffff0000u);
+        }
+    }
+};
+
 // Wait for every vector-memory operation of this wave, direct global->LDS
 // loads included.  The compiler does not reliably order reads of LDS
 // written by such loads when the loads were issued in an earlier loop
@@ -224,6 +308,19 @@ __device__ __forceinline__ void lds_cols(const float* row, int tid, float (&out)
     } else {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) out[c] = p[c];
+    }
+}
+
+// This lane's CPL output columns, one store.
+template <int CPL>
+__device__ __forceinline__ void store_cols(float* p, const float (&v)[CPL]) {
+    if constexpr (CPL == 4) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (CPL == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) p[c] = v[c];
     }
 }
 

@@ -13,7 +13,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
 
 // Persistent variant for short sequences (decode): the grid holds only as
 // many workgroups as stay resident, and workgroup b walks the items (sequence,
-// head, 128-column block) b, b + grid, b + 2 grid, ...  While item i is
+// head, 32 CPL-column block) b, b + grid, b + 2 grid, ...  While item i is
 // convolved, gated, updated and stored from registers, everything item i+1
 // reads -- its state block, x row, gate inputs, taps and conv window -- is
 // already streaming into LDS by direct global->LDS loads, which hold no
@@ -32,10 +32,10 @@ __global__ __launch_bounds__(BLOCK_THREADS) void k_gdn_seq(const SeqArgs A) {
 //
 // The arithmetic per column is the token-by-token kernel's (same conv,
 // gate_qk, gate_scalars and delta_step), so the two agree bit for bit.
-template <typename ActT, typename StT, int DK>
+template <typename ActT, typename StT, int DK, int CPL>
 __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void k_gdn_seq_stream(
     const SeqArgs A) {
-    constexpr int CPL = 4, R = DK / 16, BV = 32 * CPL;
+    constexpr int R = DK / 16, BV = 32 * CPL;
     constexpr int NLC = 2 * DK + BV;       // conv channels of an item: q, k (key head), v (block)
     constexpr int SL = LDS_ELEM_SLOT;      // bytes per lane slot of a staged element
     using Stage = StateStage<StT, DK, CPL>;
@@ -263,9 +263,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
                     lds_rows<R>(sq, tid, q);
                     lds_cols<CPL>(sv, tid, v);
                     delta_step<R, CPL>(s, k, q, v, ssc[0], ssc[1], ssc[2], o);
-                    if (writer)
-                        *reinterpret_cast<float4*>(O + (int64_t)t * o_stride) =
-                            make_float4(o[0], o[1], o[2], o[3]);
+                    if (writer) store_cols<CPL>(O + (int64_t)t * o_stride, o);
                 }
                 lds_barrier();
             }
@@ -340,17 +338,17 @@ static int resident_grid(const void* kernel, int (&cache)[MAX_CACHED_DEVICES]) {
     return v;
 }
 
-template <typename ActT, typename StT, int DK>
+template <typename ActT, typename StT, int DK, int CPL>
 static hipError_t launch_seq_stream(const SeqArgs& a, hipStream_t s) {
     static int cache[MAX_CACHED_DEVICES] = {};
-    const int64_t items = (int64_t)a.n_seqs * a.h_v * (a.d_v / 128);
+    const int64_t items = (int64_t)a.n_seqs * a.h_v * (a.d_v / (32 * CPL));
     if (items == 0) return hipSuccess;
     if (items > 0x40000000) return hipErrorInvalidValue;  // item indices up to 2 items stay in int
-    const void* k = reinterpret_cast<const void*>(&k_gdn_seq_stream<ActT, StT, DK>);
+    const void* k = reinterpret_cast<const void*>(&k_gdn_seq_stream<ActT, StT, DK, CPL>);
     const int slots = resident_grid(k, cache);
     if (slots <= 0) return hipErrorInvalidValue;
     const int grid = items < slots ? (int)items : slots;
-    hipLaunchKernelGGL((k_gdn_seq_stream<ActT, StT, DK>), dim3(grid), dim3(BLOCK_THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_gdn_seq_stream<ActT, StT, DK, CPL>), dim3(grid), dim3(BLOCK_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
@@ -364,12 +362,18 @@ static hipError_t launch_seq_t(const SeqArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Few tokens per sequence (decode): whole heads per workgroup and the
-// streaming persistent kernel.  Longer sequences: 32 columns per workgroup,
+// Few tokens per sequence (decode): the streaming persistent kernel on 128-
+// (else 64-) column items.  Longer sequences: 32 columns per workgroup,
 // the shortest per-token critical path.
 template <typename ActT, typename StT, int DK>
 static hipError_t launch_seq_shape(const SeqArgs& a, int max_seqlen, hipStream_t s) {
-    if (max_seqlen >= 1 && max_seqlen <= 4 && a.d_v % 128 == 0) return launch_seq_stream<ActT, StT, DK>(a, s);
+    if (max_seqlen >= 1 && max_seqlen <= 4) {
+        // 128-column items where the head allows them: at the 64 x 1 decode
+        // shape 64-column items measured slower (77.0 against 67.5 us per
+        // step; each item's conv, gating and barrier chain is a fixed cost).
+        if (a.d_v % 128 == 0) return launch_seq_stream<ActT, StT, DK, 4>(a, s);
+        if (a.d_v % 64 == 0) return launch_seq_stream<ActT, StT, DK, 2>(a, s);
+    }
     return launch_seq_t<ActT, StT, DK, 1, 16>(a, s);
 }
 

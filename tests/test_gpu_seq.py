@@ -299,6 +299,18 @@ def test_decode_stream_d64_two_blocks(ora):
 
 
 @pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
+def test_decode_stream_one_block_per_head(ora, state_dtype):
+    """d_v = 64 takes the streaming kernel with 64-column items (two state
+    columns per lane): one item per head, so each key head's window is
+    owned by its r value heads alone (arrival count r)."""
+    wl = wk.Workload("d64v64", h_k=4, h_v=8, d_k=64, d_v=64, conv_w=4, act_dtype=wk.BF16,
+                     state_dtype=state_dtype, seqlens=(1, 4, 2, 0, 3, 1) * 12, seed=26, scale=64 ** -0.5)
+    inp = wk.make_sequence_inputs(wl)
+    n = len(wl.seqlens)
+    _check_pages(ora, wl, inp, list(range(n)), None, n, s_tol=TOL if state_dtype == wk.F32 else 2.0 ** -8)
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
 def test_decode_stream_d32(ora, state_dtype):
     """d_k = 32 (two state rows per lane in the staged layout) with d_v = 128
     through the streaming kernel, fp32 and bf16 state."""
