@@ -501,8 +501,24 @@ def main():
                          "kernel": "k_gdn_seq", "algorithmic_flops": fl},
             "config": {"seqlens": list(wl.seqlens)}}
         log(f"short_prefill: {k_ms * 1e3:.1f} us, {tf:.2f} TFLOP/s")
+        # the same batch through the chunked kernel, the path gdn_prefill
+        # selects for it (its longest sequence is above the token-by-token limit)
+        path = g.gdn_prefill_path(w.dims, w.batch)
         del w
         torch.cuda.empty_cache()
+        try:
+            w = SeqWorkload(g, torch, wl, chunk=64)
+            c_ms, _ = measure(torch, w, max(args.steps // 4, 10), 5)
+            other["short_prefill"]["chunked_path"] = {
+                "value": round(wl.n_tokens / (c_ms * 1e-3)), "unit": "tokens/s/layer",
+                "us_per_call": round(c_ms * 1e3, 2), "us_per_call_percentiles": dict(LAST_PERCENTILES),
+                "kernel": "k_gdn_chunk", "chunk": 64,
+                "selected_by_gdn_prefill": path == g.GDN_PATH_CHUNKED}
+            log(f"short_prefill, chunked kernel: {c_ms * 1e3:.1f} us")
+            del w
+            torch.cuda.empty_cache()
+        except g.GdnError as e:
+            other["short_prefill"]["chunked_path"] = {"value": None, "note": f"not available: {e}"}
 
     # ---- long chunked prefill
     if "long_prefill" in only:
