@@ -60,7 +60,7 @@ template <> struct RowVec<bf16_t, 2> {
         v[0] = __uint_as_float(t << 16); v[1] = __uint_as_float(t & 0xffff0000u);
     }
     __device__ static void store(bf16_t* p, const float (&v)[2]) {
-        *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        *reinterpret_cast<uint32_t*>(p) = f32x2_to_bf16x2(v[0], v[1]);
     }
 };
 template <> struct RowVec<bf16_t, 4> {
@@ -70,8 +70,7 @@ template <> struct RowVec<bf16_t, 4> {
         v[2] = __uint_as_float(t[1] << 16); v[3] = __uint_as_float(t[1] & 0xffff0000u);
     }
     __device__ static void store(bf16_t* p, const float (&v)[4]) {
-        const u32x2v t = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                          (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+        const u32x2v t = {f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])};
         *reinterpret_cast<u32x2v*>(p) = t;
     }
 };

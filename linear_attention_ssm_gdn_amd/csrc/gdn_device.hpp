@@ -18,12 +18,14 @@ using bf16_t = uint16_t;
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (NaN stays NaN), by gfx950's
+// conversion instruction (v_cvt_pk_bf16_f32), one instruction per pair.
+typedef float gdn_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 gdn_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// Two values converted together and packed, a in the low half.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((gdn_f32x2){a, b}, gdn_bf16x2));
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
