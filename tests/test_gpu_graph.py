@@ -180,3 +180,83 @@ def test_verify_steps_replayed_from_a_graph_equal_eager_launches(layout):
         assert torch.equal(graph["conv"].buf, eager["conv"].buf), s
         assert int(graph["err"].item()) == 0 and int(eager["err"].item()) == 0, s
         assert int(graph["conv"].sync.abs().sum()) == 0, s
+
+
+def test_mixed_steps_replayed_from_a_graph_equal_eager_launches():
+    """One launch mixing four decode sequences (a token each) with six
+    one-page verify requests in a shared conv pool, captured once and
+    replayed for three steps with new tokens, candidates, acceptance counts
+    and parity written in between."""
+    g = gdn()
+    base = dict(h_k=4, h_v=8, d_k=128, d_v=128, conv_w=4, act_dtype=wk.BF16, state_dtype=wk.F32, seed=44)
+    ws = wk.Workload("graph_mixed_seq", seqlens=(1, 1, 1, 1), **base)
+    wv = wk.Workload("graph_mixed_verify", n_req=6, n_cand=8, n_steps=3, **base)
+    si, vi = wk.make_sequence_inputs(ws), wk.make_verify_inputs(wv)
+    dims = dims_of(ws, n_spec=wv.n_cand - 1)
+    NS, R, K, C = len(ws.seqlens), wv.n_req, wv.n_cand, ws.c_conv
+    params = params_of(si, ws)
+    batch = make_batch(si["cu_seqlens"], list(range(NS)), NS)
+    req_page = torch.arange(NS, NS + R, dtype=torch.int32, device=DEV)
+    tokens = [wk.make_sequence_inputs(ws.replace(seed=ws.seed + 300 + s)) for s in range(wv.n_steps)]
+    act = dims.act_torch
+
+    def make():
+        conv = g.ConvPool.alloc(dims, NS + R, 3 + dims.n_spec, DEV)
+        state = g.StatePool.alloc(dims, NS, DEV)
+        pages = g.SpecPages.alloc(dims, 0, NS + R, DEV)
+        for s in range(NS):
+            conv.buf[s, :3] = dev(si["window0"][s], act)
+            state.buf[s] = dev(si["S0"][s], dims.state_torch)
+        st = pages.states()
+        for r in range(R):
+            st[NS + r, 0] = dev(vi["S0"][r], dims.state_torch)
+            conv.buf[NS + r, :3] = dev(vi["window0"][r], act)
+        seq = dict(x=torch.empty((NS, C), dtype=act, device=DEV), a=torch.empty((NS, ws.h_v), dtype=act, device=DEV),
+                   b=torch.empty((NS, ws.h_v), dtype=act, device=DEV), batch=batch, conv=conv, state=state,
+                   o=torch.empty((NS, ws.h_v, ws.d_v), device=DEV))
+        ver = dict(pages=pages, x=torch.empty((R * K, C), dtype=act, device=DEV),
+                   a=torch.empty((R * K, ws.h_v), dtype=act, device=DEV),
+                   b=torch.empty((R * K, ws.h_v), dtype=act, device=DEV), n_req=R, n_cand=K, req_page=req_page,
+                   num_accepted=torch.zeros(R, dtype=torch.int32, device=DEV),
+                   step_parity=torch.zeros(R, dtype=torch.uint8, device=DEV), conv=conv,
+                   o=torch.empty((R * K, ws.h_v, ws.d_v), device=DEV))
+        return dict(seq=seq, ver=ver, err=torch.zeros(1, dtype=torch.int32, device=DEV))
+
+    def call(w):
+        g.gdn_mixed_step(dims, params, seq=w["seq"], verify=w["ver"], err=w["err"])
+
+    def load(w, s):
+        sq, vr, f = w["seq"], w["ver"], tokens[s]
+        for k in ("x", "a", "b"):
+            sq[k].copy_(dev(f[k], act))
+        vr["x"].copy_(dev(vi["x"][s].reshape(R * K, C), act))
+        vr["a"].copy_(dev(vi["a"][s].reshape(R * K, ws.h_v), act))
+        vr["b"].copy_(dev(vi["b"][s].reshape(R * K, ws.h_v), act))
+        prev = vi["accepted"][s - 1] if s > 0 else np.zeros(R, np.int32)
+        vr["num_accepted"].copy_(torch.as_tensor(np.asarray(prev, np.int32)))
+        vr["step_parity"].fill_((s + 1) & 1)
+        sq["o"].fill_(float("nan"))
+        vr["o"].fill_(float("nan"))
+
+    eager, graph, spare = make(), make(), make()
+    load(spare, 0)
+    _warm(lambda: call(spare))
+    load(graph, 0)
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        call(graph)
+
+    for s in range(wv.n_steps):
+        load(eager, s)
+        load(graph, s)
+        call(eager)
+        cg.replay()
+        torch.cuda.synchronize()
+        for part in ("seq", "ver"):
+            assert not torch.isnan(eager[part]["o"]).any(), (s, part)
+            assert torch.equal(graph[part]["o"], eager[part]["o"]), (s, part)
+        assert torch.equal(graph["seq"]["state"].buf, eager["seq"]["state"].buf), s
+        assert torch.equal(graph["ver"]["pages"].buf, eager["ver"]["pages"].buf), s
+        assert torch.equal(graph["seq"]["conv"].buf, eager["seq"]["conv"].buf), s
+        assert int(graph["err"].item()) == 0 and int(eager["err"].item()) == 0, s
+        assert int(graph["seq"]["conv"].sync.abs().sum()) == 0, s
