@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import gdn_workloads as wk
-from gpu_util import gdn, host, max_slice_rel_S, max_slice_rel_o, oracle_seq, run_seq
+from gpu_util import DEV, gdn, host, max_slice_rel_S, max_slice_rel_o, oracle_seq, run_seq
 
 pytestmark = pytest.mark.gpu
 
@@ -134,3 +134,31 @@ def test_chunked_more_sequences_than_threads(ora):
     wl = _small(lens, seed=47, h_k=1, h_v=2, d_v=64)
     inp = wk.make_sequence_inputs(wl)
     _check(ora, wl, inp)
+
+
+def test_chunked_padding_and_bad_page(ora):
+    """A padding sequence (page -1) is skipped and writes nothing; a page
+    beyond the pools is skipped and reported (GDN_DEVERR_PAGE); the other
+    sequences of the launch still match the oracle, and pages no valid
+    sequence names stay untouched."""
+    g = gdn()
+    wl = _small((130, 64, 70, 65), seed=48)
+    inp = wk.make_sequence_inputs(wl)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pages = [2, -1, 0, 9]
+    o, conv, state = run_seq(wl, inp, pages=pages, n_pages=4, chunk=64, err=err)
+    assert int(err.item()) & g.GDN_DEVERR_PAGE
+    o_ref, win_ref, S_ref = oracle_seq(ora, wl, inp)
+    cu = inp["cu_seqlens"]
+    oh, Sh, Ch = host(o), host(state.buf), host(conv.buf)
+    for s, p in enumerate(pages):
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        if p < 0 or p >= 4:
+            assert np.isnan(oh[rows]).all(), s
+            continue
+        assert max_slice_rel_o(oh[rows], o_ref[rows], [0, cu[s + 1] - cu[s]]) <= TOL, s
+        assert max_slice_rel_S(Sh[p:p + 1], S_ref[s:s + 1]) <= TOL, s
+        np.testing.assert_array_equal(Ch[p], win_ref[s])
+    for p in (1, 3):
+        assert float(state.buf[p].abs().sum()) == 0.0 and float(conv.buf[p].float().abs().sum()) == 0.0
+    assert int(conv.sync.abs().sum()) == 0
