@@ -44,6 +44,16 @@
  *   zero when its kernels complete; a call aborted midway must be followed
  *   by re-zeroing them.
  * - Calls that touch the same pages must be ordered (same stream, or events).
+ * - Every compute call can be captured in a HIP graph and replayed: its host
+ *   arguments are shapes, strides, host bounds and device pointers; every
+ *   value that changes from step to step (lengths, page indices, acceptance
+ *   counts, parity) is read on the device; no call issues a memset, a copy or
+ *   an allocation, and the sync words return to zero inside the kernels
+ *   ("r9700-stack v0.2.4", "A defect found and fixed before the tag": a
+ *   result must not depend on whether the step runs in a graph).  The first
+ *   short-sequence (decode) call on a device queries its compute-unit count
+ *   and the kernel's occupancy (host queries, cached per device); make that
+ *   first call outside capture.
  */
 #ifndef GDN_H
 #define GDN_H
