@@ -339,3 +339,21 @@ def test_decode_stream_fewer_items_than_workgroups(ora, n):
     wl = wk.DECODE.replace(seqlens=(1,) * n, seed=25)
     inp = wk.make_sequence_inputs(wl)
     _check_pages(ora, wl, inp, list(range(n)), None, n)
+
+
+def test_bf16_state_store_rounds_to_nearest_even():
+    """One decode token from a start state that bf16 represents exactly runs
+    the same fp32 arithmetic with either state dtype, so the bf16 run must
+    store exactly the round-to-nearest-even of the fp32 run's new state
+    (torch's conversion), and both runs give the same outputs bit for bit.
+    Pins the kernels' fp32 -> bf16 conversion to that rounding."""
+    wl = wk.DECODE.replace(seqlens=(1,) * 8, seed=27)
+    inp = wk.make_sequence_inputs(wl)
+    inp["S0"] = wk.round_to(inp["S0"], wk.BF16)
+    o32, _, st32 = run_seq(wl, inp)
+    o16, _, st16 = run_seq(wl.replace(state_dtype=wk.BF16), inp)
+    assert torch.equal(o32, o16)
+    ref = st32.buf.to(torch.bfloat16)
+    assert torch.equal(st16.buf.view(torch.int16), ref.view(torch.int16))
+    # the step moved the state: not every value was already representable
+    assert not torch.equal(st32.buf, ref.to(torch.float32))
