@@ -162,3 +162,11 @@ def test_chunked_padding_and_bad_page(ora):
     for p in (1, 3):
         assert float(state.buf[p].abs().sum()) == 0.0 and float(conv.buf[p].float().abs().sum()) == 0.0
     assert int(conv.sync.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("h_k,h_v", [(4, 4), (2, 8)])
+def test_chunked_gqa_ratios(ora, h_k, h_v):
+    """One and four value heads per key head (the workloads use two): the key
+    head's K K^T and Q K^T shared by r value heads, and the window hand-off."""
+    wl = _small((130, 64, 7), seed=49, h_k=h_k, h_v=h_v)
+    _check(ora, wl, wk.make_sequence_inputs(wl))

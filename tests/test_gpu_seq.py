@@ -357,3 +357,13 @@ def test_bf16_state_store_rounds_to_nearest_even():
     assert torch.equal(st16.buf.view(torch.int16), ref.view(torch.int16))
     # the step moved the state: not every value was already representable
     assert not torch.equal(st32.buf, ref.to(torch.float32))
+
+
+@pytest.mark.parametrize("h_k,h_v", [(4, 4), (2, 8)])
+@pytest.mark.parametrize("lens", [(1, 2, 1, 3), (1, 40, 7)])
+def test_gqa_ratios(ora, h_k, h_v, lens):
+    """One and four value heads per key head (the workloads use two), through
+    the streaming decode kernel (lengths <= 4) and the general one: key-head
+    mapping and the q/k window written after r * blocks arrivals."""
+    wl = wk.DECODE.replace(h_k=h_k, h_v=h_v, seqlens=lens, seed=28)
+    _check(ora, wl, wk.make_sequence_inputs(wl))

@@ -363,3 +363,27 @@ def test_candidate_count_varies_between_steps(ora):
         for h in range(wl.h_v):
             assert np.abs(Sg[r, h] - S[r, h]).max() <= 1e-4 * np.abs(S[r, h]).max()
     assert int(one.err.item()) == 0
+
+
+@pytest.mark.parametrize("h_k,h_v", [(4, 4), (2, 8)])
+def test_gqa_ratios(ora, h_k, h_v):
+    """One and four value heads per key head (the workloads use two): the
+    key-head mapping, the q/k record rows written by one workgroup per key
+    head and the window hand-off after r arrivals; one-page equals slots bit
+    for bit and the oracle within 1e-4."""
+    wl = _small(n_req=3, n_steps=4, h_k=h_k, h_v=h_v, seed=47)
+    inp = _inputs(wl, wk.F32)
+    one = VerifyRun(wl, inp, ONEPAGE, wk.F32)
+    o1 = one.run()
+    slots = VerifyRun(wl, inp, SLOTS, wk.F32)
+    assert torch.equal(o1, slots.run())
+    assert torch.equal(one.committed_state(), slots.committed_state())
+    dm = ora.dims_of(wl)
+    o_ref, win_ref, S_ref = ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"],
+                                       inp["b"], inp["accepted"], inp["window0"], inp["S0"])
+    o = host(o1)
+    worst = max(float(np.abs(o[:, r, :, h] - o_ref[:, r, :, h]).max() / np.abs(o_ref[:, r, :, h]).max())
+                for r in range(wl.n_req) for h in range(wl.h_v))
+    assert worst <= 1e-4, worst
+    np.testing.assert_array_equal(host(one.committed_window()), win_ref)
+    assert int(one.err.item()) == 0 and int(one.conv.sync.abs().sum()) == 0
