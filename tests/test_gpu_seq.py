@@ -367,3 +367,14 @@ def test_gqa_ratios(ora, h_k, h_v, lens):
     mapping and the q/k window written after r * blocks arrivals."""
     wl = wk.DECODE.replace(h_k=h_k, h_v=h_v, seqlens=lens, seed=28)
     _check(ora, wl, wk.make_sequence_inputs(wl))
+
+
+def test_decode_stream_many_claims(ora):
+    """200 sequences of 1-4 tokens at the decode shape: 6,400 items, about
+    twelve per resident workgroup, so most are handed out from the work
+    counter; every sequence matches the oracle and the counter returns to
+    zero."""
+    rng = np.random.default_rng(29)
+    lens = tuple(int(x) for x in rng.integers(1, 5, size=200))
+    wl = wk.DECODE.replace(seqlens=lens, seed=29)
+    _check(ora, wl, wk.make_sequence_inputs(wl))
