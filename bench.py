@@ -439,7 +439,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the GDN core shards by head or request with no exchange, "
-              "and this build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+              "and the benchmark runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import linear_attention_ssm_gdn_amd as g
