@@ -236,6 +236,8 @@ def test_conv_update_silu_parity(ora):
     np.testing.assert_array_equal(host(conv.buf), win_ref)
     yb, _ = _conv_call(wl, inp, True, "bf16", has_init=has)
     assert rel(host(yb), y_ref) <= 2.0 ** -8
+    # the bf16 output is the fp32 output rounded to nearest even, bit for bit
+    assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16))
 
 
 def test_fused_conv_window_equals_conv_update():

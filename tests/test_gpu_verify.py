@@ -387,3 +387,29 @@ def test_gqa_ratios(ora, h_k, h_v):
     assert worst <= 1e-4, worst
     np.testing.assert_array_equal(host(one.committed_window()), win_ref)
     assert int(one.err.item()) == 0 and int(one.conv.sync.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
+def test_two_column_blocks_per_head(ora, state_dtype):
+    """d_v = 256: two 128-column workgroups per value head, of which only the
+    first records the key head's q/k rows and the gate inputs, and the done
+    counter reaches h_v x 2 before the flag flips; one-page equals slots bit
+    for bit and the oracle within 1e-4 (3e-3 with bf16 checkpoints)."""
+    wl = _small(n_req=3, n_steps=4, h_k=2, h_v=4, d_k=128, d_v=256, seed=53, state_dtype=state_dtype)
+    inp = _inputs(wl, state_dtype)
+    one = VerifyRun(wl, inp, ONEPAGE, state_dtype)
+    o1 = one.run()
+    slots = VerifyRun(wl, inp, SLOTS, state_dtype)
+    assert torch.equal(o1, slots.run())
+    assert torch.equal(one.committed_state(), slots.committed_state())
+    dm = ora.dims_of(wl)
+    o_ref, win_ref, S_ref = ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"], inp["a"],
+                                       inp["b"], inp["accepted"], inp["window0"], inp["S0"],
+                                       state_bf16=(state_dtype == wk.BF16))
+    o = host(o1)
+    worst = max(float(np.abs(o[:, r, :, h] - o_ref[:, r, :, h]).max() / np.abs(o_ref[:, r, :, h]).max())
+                for r in range(wl.n_req) for h in range(wl.h_v))
+    assert worst <= (1e-4 if state_dtype == wk.F32 else 3e-3), worst
+    np.testing.assert_array_equal(host(one.committed_window()), win_ref)
+    hdr = one.pages.header()
+    assert int(one.err.item()) == 0 and int((hdr[:, 0] >> 8).abs().sum()) == 0  # done counters back to zero
