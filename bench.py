@@ -42,6 +42,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def failed(other, name, e):
+    """Record a workload that raised, so the JSON line still comes out."""
+    log(f"{name}: failed: {type(e).__name__}: {e}")
+    other[name] = {"value": None, "error": f"{type(e).__name__}: {e}"}
+
+
 # ------------------------------------------------------------ byte / flop models
 def decode_bytes(wl) -> int:
     """Algorithmic HBM bytes of one token-by-token launch: every byte the
@@ -486,121 +492,136 @@ def main():
 
     # ---- short ragged prefill (token by token)
     if "short_prefill" in only:
-        wl = wk.SHORT_PREFILL
-        log("short_prefill")
-        w = SeqWorkload(g, torch, wl)
-        k_ms, wall_ms = measure(torch, w, max(args.steps // 4, 10), 5)
-        fl = recurrence_flops(wl)
-        tf = fl / (k_ms * 1e-3) / 1e12
-        other["short_prefill"] = {
-            "value": round(wl.n_tokens / (k_ms * 1e-3)), "unit": "tokens/s/layer", "us_per_call": round(k_ms * 1e3, 2),
-            "us_per_token_critical_path": round(k_ms * 1e3 / max(wl.seqlens), 4),
-            "us_per_call_percentiles": dict(LAST_PERCENTILES),
-            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": read_traffic("k_gdn_seq", "short_prefill"),
-                         "kernel": "k_gdn_seq", "algorithmic_flops": fl},
-            "config": {"seqlens": list(wl.seqlens)}}
-        log(f"short_prefill: {k_ms * 1e3:.1f} us, {tf:.2f} TFLOP/s")
-        # the same batch through the chunked kernel, the path gdn_prefill
-        # selects for it (its longest sequence is above the token-by-token limit)
-        path = g.gdn_prefill_path(w.dims, w.batch)
-        del w
-        torch.cuda.empty_cache()
         try:
-            w = SeqWorkload(g, torch, wl, chunk=64)
-            c_ms, _ = measure(torch, w, max(args.steps // 4, 10), 5)
-            other["short_prefill"]["chunked_path"] = {
-                "value": round(wl.n_tokens / (c_ms * 1e-3)), "unit": "tokens/s/layer",
-                "us_per_call": round(c_ms * 1e3, 2), "us_per_call_percentiles": dict(LAST_PERCENTILES),
-                "kernel": "k_gdn_chunk", "chunk": 64,
-                "selected_by_gdn_prefill": path == g.GDN_PATH_CHUNKED}
-            log(f"short_prefill, chunked kernel: {c_ms * 1e3:.1f} us")
+            wl = wk.SHORT_PREFILL
+            log("short_prefill")
+            w = SeqWorkload(g, torch, wl)
+            k_ms, wall_ms = measure(torch, w, max(args.steps // 4, 10), 5)
+            fl = recurrence_flops(wl)
+            tf = fl / (k_ms * 1e-3) / 1e12
+            other["short_prefill"] = {
+                "value": round(wl.n_tokens / (k_ms * 1e-3)), "unit": "tokens/s/layer", "us_per_call": round(k_ms * 1e3, 2),
+                "us_per_token_critical_path": round(k_ms * 1e3 / max(wl.seqlens), 4),
+                "us_per_call_percentiles": dict(LAST_PERCENTILES),
+                "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": read_traffic("k_gdn_seq", "short_prefill"),
+                             "kernel": "k_gdn_seq", "algorithmic_flops": fl},
+                "config": {"seqlens": list(wl.seqlens)}}
+            log(f"short_prefill: {k_ms * 1e3:.1f} us, {tf:.2f} TFLOP/s")
+            # the same batch through the chunked kernel, the path gdn_prefill
+            # selects for it (its longest sequence is above the token-by-token limit)
+            path = g.gdn_prefill_path(w.dims, w.batch)
             del w
             torch.cuda.empty_cache()
-        except g.GdnError as e:
-            other["short_prefill"]["chunked_path"] = {"value": None, "note": f"not available: {e}"}
+            try:
+                w = SeqWorkload(g, torch, wl, chunk=64)
+                c_ms, _ = measure(torch, w, max(args.steps // 4, 10), 5)
+                other["short_prefill"]["chunked_path"] = {
+                    "value": round(wl.n_tokens / (c_ms * 1e-3)), "unit": "tokens/s/layer",
+                    "us_per_call": round(c_ms * 1e3, 2), "us_per_call_percentiles": dict(LAST_PERCENTILES),
+                    "kernel": "k_gdn_chunk", "chunk": 64,
+                    "selected_by_gdn_prefill": path == g.GDN_PATH_CHUNKED}
+                log(f"short_prefill, chunked kernel: {c_ms * 1e3:.1f} us")
+                del w
+                torch.cuda.empty_cache()
+            except g.GdnError as e:
+                other["short_prefill"]["chunked_path"] = {"value": None, "note": f"not available: {e}"}
+        except Exception as e:  # a failure here must not cost the headline line
+            failed(other, "short_prefill", e)
 
     # ---- long chunked prefill
     if "long_prefill" in only:
-        wl = wk.LONG_PREFILL
         try:
-            g.gdn_chunked_workspace_bytes(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v), len(wl.seqlens), wl.n_tokens,
-                                          wl.chunk)
-            log("long_prefill")
-            w = SeqWorkload(g, torch, wl, chunk=wl.chunk)
-            k_ms, wall_ms = measure(torch, w, max(args.steps // 20, 5), 2)
-            fl = chunked_flops(wl)
-            tf = fl / (k_ms * 1e-3) / 1e12
-            other["long_prefill"] = {
-                "value": round(wl.n_tokens / (k_ms * 1e-3)), "unit": "tokens/s/layer", "us_per_call": round(k_ms * 1e3, 1),
-                "us_per_call_percentiles": dict(LAST_PERCENTILES),
-                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                             "traffic": read_traffic("k_gdn_chunk", "long_prefill"), "kernel": "k_gdn_chunk",
-                             "algorithmic_flops": fl,
-                             "hbm_frac": round(chunked_bytes(wl) / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-                "config": {"n_seqs": len(wl.seqlens), "seqlen": wl.seqlens[0], "chunk": wl.chunk}}
-            log(f"long_prefill: {k_ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
-            del w
-            torch.cuda.empty_cache()
-        except g.GdnError as e:
-            other["long_prefill"] = {"value": None, "note": f"not available: {e}"}
+            wl = wk.LONG_PREFILL
+            try:
+                g.gdn_chunked_workspace_bytes(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v), len(wl.seqlens), wl.n_tokens,
+                                              wl.chunk)
+                log("long_prefill")
+                w = SeqWorkload(g, torch, wl, chunk=wl.chunk)
+                k_ms, wall_ms = measure(torch, w, max(args.steps // 20, 5), 2)
+                fl = chunked_flops(wl)
+                tf = fl / (k_ms * 1e-3) / 1e12
+                other["long_prefill"] = {
+                    "value": round(wl.n_tokens / (k_ms * 1e-3)), "unit": "tokens/s/layer", "us_per_call": round(k_ms * 1e3, 1),
+                    "us_per_call_percentiles": dict(LAST_PERCENTILES),
+                    "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                 "traffic": read_traffic("k_gdn_chunk", "long_prefill"), "kernel": "k_gdn_chunk",
+                                 "algorithmic_flops": fl,
+                                 "hbm_frac": round(chunked_bytes(wl) / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                    "config": {"n_seqs": len(wl.seqlens), "seqlen": wl.seqlens[0], "chunk": wl.chunk}}
+                log(f"long_prefill: {k_ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+                del w
+                torch.cuda.empty_cache()
+            except g.GdnError as e:
+                other["long_prefill"] = {"value": None, "note": f"not available: {e}"}
+        except Exception as e:  # a failure here must not cost the headline line
+            failed(other, "long_prefill", e)
 
     # ---- speculative verify (one page), fp32 and bf16 state
     if "spec_verify" in only:
-        wl = wk.SPEC_VERIFY
-        res = {}
-        for sd in (wk.F32, wk.BF16):
-            log(f"spec_verify {sd}")
-            w = VerifyWorkload(g, torch, wl, sd)
-            k_ms, wall_ms = measure(torch, w, max(args.steps // 2, 10), 10)
-            nb = verify_bytes(wl, sd, w.mean_replay)
-            gbs = nb / (k_ms * 1e-3) / 1e9
-            res[sd] = {"value": round(k_ms * 1e3, 2), "unit": "us/step", "us_per_step_percentiles": dict(LAST_PERCENTILES),
-                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                    "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                    "traffic": read_traffic("k_gdn_verify", "spec_verify_" + sd),
-                                    "kernel": "k_gdn_verify", "algorithmic_bytes": nb}}
-            log(f"spec_verify {sd}: {k_ms * 1e3:.2f} us/step, {gbs:.0f} GB/s")
-            del w
-            torch.cuda.empty_cache()
-        lay1 = g.gdn_spec_page_layout(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, n_spec=wl.n_cand - 1), 0)["page_bytes"]
-        lay8 = g.gdn_spec_page_layout(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, n_spec=wl.n_cand - 1), 1)["page_bytes"]
-        other["spec_verify"] = {"state_f32": res[wk.F32], "state_bf16": res[wk.BF16],
-                                "page_bytes_onepage_f32": lay1, "page_bytes_slots_f32": lay8,
-                                "config": {"n_req": wl.n_req, "n_cand": wl.n_cand}}
+        try:
+            wl = wk.SPEC_VERIFY
+            res = {}
+            for sd in (wk.F32, wk.BF16):
+                log(f"spec_verify {sd}")
+                w = VerifyWorkload(g, torch, wl, sd)
+                k_ms, wall_ms = measure(torch, w, max(args.steps // 2, 10), 10)
+                nb = verify_bytes(wl, sd, w.mean_replay)
+                gbs = nb / (k_ms * 1e-3) / 1e9
+                res[sd] = {"value": round(k_ms * 1e3, 2), "unit": "us/step", "us_per_step_percentiles": dict(LAST_PERCENTILES),
+                           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                        "traffic": read_traffic("k_gdn_verify", "spec_verify_" + sd),
+                                        "kernel": "k_gdn_verify", "algorithmic_bytes": nb}}
+                log(f"spec_verify {sd}: {k_ms * 1e3:.2f} us/step, {gbs:.0f} GB/s")
+                del w
+                torch.cuda.empty_cache()
+            lay1 = g.gdn_spec_page_layout(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, n_spec=wl.n_cand - 1), 0)["page_bytes"]
+            lay8 = g.gdn_spec_page_layout(g.Dims(wl.h_k, wl.h_v, wl.d_k, wl.d_v, n_spec=wl.n_cand - 1), 1)["page_bytes"]
+            other["spec_verify"] = {"state_f32": res[wk.F32], "state_bf16": res[wk.BF16],
+                                    "page_bytes_onepage_f32": lay1, "page_bytes_slots_f32": lay8,
+                                    "config": {"n_req": wl.n_req, "n_cand": wl.n_cand}}
+        except Exception as e:  # a failure here must not cost the headline line
+            failed(other, "spec_verify", e)
 
     # ---- mixed steps: a prefill batch + a verify batch, one launch vs two
     if "mixed_step" in only:
-        res = {}
-        small_seq = wk.SHORT_PREFILL.replace(name="small_prefill", seqlens=(45, 17, 9, 3))
-        small_ver = wk.SPEC_VERIFY.replace(name="small_verify", n_req=8)
-        for name, sw, vw in (("short_prefill_plus_verify", wk.SHORT_PREFILL, wk.SPEC_VERIFY),
-                             ("small_prefill_plus_verify", small_seq, small_ver)):
-            log(f"mixed_step {name}")
-            w = MixedWorkload(g, torch, sw, vw)
-            n = max(args.steps // 4, 10)
-            w.fused = True
-            f_ms, _ = measure(torch, w, n, 5)
-            w.fused = False
-            s_ms, _ = measure(torch, w, n, 5)
-            res[name] = {"value": round(f_ms * 1e3, 1), "unit": "us/step", "us_separate_launches": round(s_ms * 1e3, 1),
-                         "speedup_vs_separate": round(s_ms / f_ms, 3),
-                         "config": {"prefill_seqlens": list(sw.seqlens), "verify_n_req": vw.n_req,
-                                    "verify_n_cand": vw.n_cand, "state_dtype": "f32"}}
-            log(f"mixed_step {name}: {f_ms * 1e3:.1f} us fused, {s_ms * 1e3:.1f} us as two launches")
-            del w
-            torch.cuda.empty_cache()
-        other["mixed_step"] = res
+        try:
+            res = {}
+            small_seq = wk.SHORT_PREFILL.replace(name="small_prefill", seqlens=(45, 17, 9, 3))
+            small_ver = wk.SPEC_VERIFY.replace(name="small_verify", n_req=8)
+            for name, sw, vw in (("short_prefill_plus_verify", wk.SHORT_PREFILL, wk.SPEC_VERIFY),
+                                 ("small_prefill_plus_verify", small_seq, small_ver)):
+                log(f"mixed_step {name}")
+                w = MixedWorkload(g, torch, sw, vw)
+                n = max(args.steps // 4, 10)
+                w.fused = True
+                f_ms, _ = measure(torch, w, n, 5)
+                w.fused = False
+                s_ms, _ = measure(torch, w, n, 5)
+                res[name] = {"value": round(f_ms * 1e3, 1), "unit": "us/step", "us_separate_launches": round(s_ms * 1e3, 1),
+                             "speedup_vs_separate": round(s_ms / f_ms, 3),
+                             "config": {"prefill_seqlens": list(sw.seqlens), "verify_n_req": vw.n_req,
+                                        "verify_n_cand": vw.n_cand, "state_dtype": "f32"}}
+                log(f"mixed_step {name}: {f_ms * 1e3:.1f} us fused, {s_ms * 1e3:.1f} us as two launches")
+                del w
+                torch.cuda.empty_cache()
+            other["mixed_step"] = res
+        except Exception as e:  # a failure here must not cost the headline line
+            failed(other, "mixed_step", e)
 
     result["other_workloads"] = other
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wk.DECODE)
         log("cpu oracle on the other workloads")
-        for name, base in cpu_other_workloads().items():
-            if name in other and isinstance(other[name], dict):
-                other[name]["cpu_baseline"] = base
+        try:
+            for name, base in cpu_other_workloads().items():
+                if name in other and isinstance(other[name], dict):
+                    other[name]["cpu_baseline"] = base
+        except Exception as e:  # the oracle legs are context; the line still comes out
+            log(f"cpu oracle on the other workloads: failed: {type(e).__name__}: {e}")
     print(json.dumps(result), flush=True)
 
 
