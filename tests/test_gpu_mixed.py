@@ -272,3 +272,61 @@ def test_mixed_step_small_head_dims(d_k, d_v):
                 assert torch.equal(got, ref)
         for got, ref in zip(snap_f, snap_s):
             assert torch.equal(got, ref)
+
+
+def test_mixed_step_at_the_benchmark_shape():
+    """The benchmark's mix: the full short-prefill batch (8 sequences, 2,159
+    rows) with 32 one-page verify requests of 8 candidates, H_k = 16,
+    H_v = 32, d = 128, in one launch, equals the two separate launches bit
+    for bit: outputs, states, pages and the shared conv pool."""
+    g = gdn()
+    ws = wk.SHORT_PREFILL
+    wv = wk.SPEC_VERIFY
+    si, vi = wk.make_sequence_inputs(ws), wk.make_verify_inputs(wv)
+    dims = dims_of(ws, n_spec=wv.n_cand - 1)
+    NS, R, K, C = len(ws.seqlens), wv.n_req, wv.n_cand, ws.c_conv
+    params = params_of(si, ws)
+    x, a, b = dev(si["x"], dims.act_torch), dev(si["a"], dims.act_torch), dev(si["b"], dims.act_torch)
+    batch = make_batch(si["cu_seqlens"], list(range(NS)), x.shape[0])
+    rp = torch.arange(NS, NS + R, dtype=torch.int32, device=DEV)
+
+    def vstep(step):
+        """Step `step` of the verify workload: candidates, the previous
+        step's acceptance counts (the second step replays), parity."""
+        prev = vi["accepted"][step - 1] if step > 0 else np.zeros(R, np.int32)
+        return (dev(vi["x"][step].reshape(R * K, C), dims.act_torch),
+                dev(vi["a"][step].reshape(R * K, ws.h_v), dims.act_torch),
+                dev(vi["b"][step].reshape(R * K, ws.h_v), dims.act_torch),
+                torch.tensor(np.asarray(prev, np.int32), device=DEV),
+                torch.full((R,), (step + 1) & 1, dtype=torch.uint8, device=DEV))
+
+    def world():
+        conv = g.ConvPool.alloc(dims, NS + R, 3 + dims.n_spec, DEV)
+        state = g.StatePool(dev(si["S0"], dims.state_torch))
+        pages = g.SpecPages.alloc(dims, 0, NS + R, DEV)
+        conv.buf[:NS, :3] = dev(si["window0"], dims.act_torch)
+        conv.buf[NS:, :3] = dev(vi["window0"], dims.act_torch)
+        pages.states()[NS:, 0] = dev(vi["S0"], dims.state_torch)
+        o_s = torch.full((x.shape[0], ws.h_v, ws.d_v), float("nan"), device=DEV)
+        o_v = torch.full((R * K, ws.h_v, ws.d_v), float("nan"), device=DEV)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        return conv, state, pages, o_s, o_v, err
+
+    fused, sep = world(), world()
+    for step in (0, 1):
+        vx, va, vb, acc, par = vstep(step)
+        conv, state, pages, o_s, o_v, err = fused
+        g.gdn_mixed_step(dims, params, seq=dict(x=x, a=a, b=b, batch=batch, conv=conv, state=state, o=o_s),
+                         verify=dict(pages=pages, x=vx, a=va, b=vb, n_req=R, n_cand=K, req_page=rp,
+                                     num_accepted=acc, step_parity=par, conv=conv, o=o_v), err=err)
+        conv, state, pages, o_s, o_v, err = sep
+        g.gdn_recurrent_seq(dims, params, x, a, b, batch, conv, state, o=o_s, err=err)
+        g.gdn_spec_verify(dims, params, pages, vx, va, vb, R, K, rp, acc, par, conv, o=o_v, err=err)
+        torch.cuda.synchronize()
+        for got, ref in zip(fused, sep):
+            t_got = got.buf if hasattr(got, "buf") else got
+            t_ref = ref.buf if hasattr(ref, "buf") else ref
+            assert torch.equal(t_got, t_ref), step
+        assert not torch.isnan(fused[3]).any() and not torch.isnan(fused[4]).any(), step
+        assert int(fused[5].item()) == 0, step
+        assert int(fused[0].sync.abs().sum()) == 0, step
