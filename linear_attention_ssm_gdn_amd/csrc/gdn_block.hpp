@@ -279,9 +279,37 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // moving those reads past the wait.
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// This lane's R rows of a d_k-long LDS row.
+// Layout of a d_k-long q or k row in LDS.  Lane g of a 16-lane row owns
+// elements g*R .. g*R+R-1 (R = d_k/16).  With d_k = 128 a lane reads its 8
+// elements as two 16-byte pieces; stored in element order those pieces sit
+// 32 bytes apart across the 16 lanes, so lanes g and g+8 meet in the same
+// banks.  The row therefore holds every lane's first piece (elements g*8 ..
+// g*8+3 at 4g), then every lane's second piece (g*8+4 .. g*8+7 at 64+4g): each
+// read instruction of the 16 lanes covers 256 consecutive bytes.  Smaller
+// d_k already read 256 contiguous bytes per instruction in element order.
+template <int DK>
+__device__ __forceinline__ int qk_pos(int e) {
+    if constexpr (DK == 128) return ((e & 7) >> 2) * 64 + (e >> 3) * 4 + (e & 3);
+    else return e;
+}
+// The element stored at position p (the inverse of qk_pos).
+template <int DK>
+__device__ __forceinline__ int qk_elem(int p) {
+    if constexpr (DK == 128) return ((p & 63) >> 2) * 8 + (p >> 6) * 4 + (p & 3);
+    else return p;
+}
+
+// This lane's R elements of a q or k row in the qk_pos layout.
 template <int R>
 __device__ __forceinline__ void lds_rows(const float* row, int tid, float (&out)[R]) {
+    if constexpr (R == 8) {
+        const int g = lane_rowgroup(tid);
+        const float4 t0 = *reinterpret_cast<const float4*>(row + 4 * g);
+        const float4 t1 = *reinterpret_cast<const float4*>(row + 64 + 4 * g);
+        out[0] = t0.x; out[1] = t0.y; out[2] = t0.z; out[3] = t0.w;
+        out[4] = t1.x; out[5] = t1.y; out[6] = t1.z; out[7] = t1.w;
+        return;
+    }
     const float* p = row + lane_rowgroup(tid) * R;
     if constexpr (R % 4 == 0) {
 #pragma unroll
@@ -351,10 +379,17 @@ __device__ __forceinline__ float gate_qk(float* qrow, float* krow, float scale, 
         kv[e] *= rk;
         kq = fmaf(kv[e], qv[e], kq);
     }
-    float* qd = qrow + l16 * E;
-    float* kd = krow + l16 * E;
+    if constexpr (E == 8) {  // the qk_pos layout of d_k = 128
+        *reinterpret_cast<float4*>(qrow + 4 * l16) = make_float4(qv[0], qv[1], qv[2], qv[3]);
+        *reinterpret_cast<float4*>(qrow + 64 + 4 * l16) = make_float4(qv[4], qv[5], qv[6], qv[7]);
+        *reinterpret_cast<float4*>(krow + 4 * l16) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+        *reinterpret_cast<float4*>(krow + 64 + 4 * l16) = make_float4(kv[4], kv[5], kv[6], kv[7]);
+    } else {
+        float* qd = qrow + l16 * E;
+        float* kd = krow + l16 * E;
 #pragma unroll
-    for (int e = 0; e < E; ++e) { qd[e] = qv[e]; kd[e] = kv[e]; }
+        for (int e = 0; e < E; ++e) { qd[e] = qv[e]; kd[e] = kv[e]; }
+    }
     return reduce16(kq);
 }
 

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) __attribute__((amdgpu_waves_per_eu(4
     const int cg = lane_colgroup(tid);
     const bool writer = lane_rowgroup(tid) == 0;
     const int64_t o_stride = (int64_t)A.h_v * A.d_v;
-    float* ydst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
+    float* ydst = lc < DK ? sq + qk_pos<DK>(lc) : lc < 2 * DK ? sk + qk_pos<DK>(lc - DK) : sv + (lc - 2 * DK);
 
     struct Item {
         int h, colbase, page, r0, T;

@@ -121,7 +121,7 @@ __device__ __forceinline__ void seq_block(const SeqArgs& A, const int block) {
             xm1 = to_f32(win[2 * C + gc]);
         }
     }
-    float* ydst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
+    float* ydst = lc < DK ? sq + qk_pos<DK>(lc) : lc < 2 * DK ? sk + qk_pos<DK>(lc - DK) : sv + (lc - 2 * DK);
     const int yld = lc < 2 * DK ? DK : BV;
     const float exp_alog = expf(A.a_log[h]);
     const float dtb = A.dt_bias[h];

@@ -110,7 +110,7 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         xw1 = to_f32(cbuf[(int64_t)(acc + 1) * C + gc]);
         xw2 = to_f32(cbuf[(int64_t)(acc + 2) * C + gc]);
     }
-    float* ydst = lc < DK ? sq + lc : lc < 2 * DK ? sk + (lc - DK) : sv + (lc - 2 * DK);
+    float* ydst = lc < DK ? sq + qk_pos<DK>(lc) : lc < 2 * DK ? sk + qk_pos<DK>(lc - DK) : sv + (lc - 2 * DK);
     const int yld = lc < 2 * DK ? DK : BV;
     float exp_alog_v = expf(A.a_log[h]);
     float dtb = A.dt_bias[h];
@@ -176,13 +176,16 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
     // for such d_k the rows go through registers.
     if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
         if constexpr (DK % 64 == 0) {
+            // the lane landing at q/k position p fetches the element qk_elem(p)
             const int wbase = tid & ~63;
+            const int64_t gq = lc < DK ? gc - lc + qk_elem<DK>(lc)
+                             : lc < 2 * DK ? gc - (lc - DK) + qk_elem<DK>(lc - DK) : gc;
             for (int i = 0; i < n_replay; ++i) {
                 const float* row = reinterpret_cast<const float*>(rec + i * row_bytes);
                 if (lc < DK)
-                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
+                    load_lds_elem(row + gq, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
                 else if (lc < 2 * DK)
-                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
+                    load_lds_elem(row + gq, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
                 else if (lc < NLC)
                     load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sv + i * BV + wbase - 2 * DK));
             }
