@@ -33,7 +33,12 @@
  *   - a speculative acceptance a counts accepted drafts, so 1 + a candidate
  *     rows are committed;
  *   - a bf16 state is rounded (nearest-even) once per verify step, when the
- *     committed state is stored.
+ *     committed state is stored;
+ *   - a verify page's flag word holds the live record slot (bit 0), the
+ *     parity of the step that wrote it (bit 1) and a done counter (bits
+ *     8..31, zero between steps); the conv buffer holds W-1 + n_spec rows and
+ *     a step's window is rows a..a+W-2, a the replayed acceptance
+ *     (ora_book_step).
  *
  * Parity pins (tests/test_oracle.py): every function below is pinned by
  * closed forms, special cases and brute-force cross-checks; none is pinned
@@ -503,6 +508,82 @@ int ora_verify(const ora_dims* d, const double* conv_w, const double* a_log,
             free_gated(&gs);
         }
         free(Srun); free(Sacc); free(wnext);
+    }
+    return 0;
+}
+
+/* ------------------------------------------- page bookkeeping of verify */
+
+/*
+ * Bookkeeping of one speculative verify step for one request's page
+ * [R924, "What it does": the two record slots and the flag word's three
+ * fields; "A defect found and fixed before the tag": the conv buffer rolls
+ * by the rows the record holds, not by a tensor's width].  Integers and data
+ * movement only: nothing of the method's arithmetic happens here.
+ *
+ *   hdr[4]  = {flag, n_rows[0], n_rows[1], accepted}.  flag bit 0 is the
+ *             live record slot L, bit 1 the parity P of the step that wrote
+ *             the page, bits 8..31 a done counter that is 0 between steps.
+ *             An all-zero header is a fresh page: slot 0 live, no rows.
+ *   cbuf    = the request's conv buffer, `rows` rows of C channels, oldest
+ *             first (values only moved, carried as doubles).
+ *   x       = the step's n_cand pre-conv candidate rows [n_cand][C].
+ *
+ * The step is refused and nothing changes when its parity equals P (the
+ * step was applied already: ORA_BOOK_PARITY), or when the live slot holds
+ * rows and num_accepted is not one of them or the slot holds more than
+ * n_spec + 1 rows (ORA_BOOK_ACCEPTED).  Otherwise, with a = num_accepted
+ * when the live slot holds rows and a = 0 when it holds none:
+ *   - the step replays rows 0..a of slot L (none when it holds no rows);
+ *   - its conv window is cbuf rows a .. a+W-2;
+ *   - cbuf becomes [rows a+1 .. a+W-2, x_0 .. x_{n_cand-1}] when n_cand > 0,
+ *     [rows a .. a+W-2] when n_cand == 0; rows past those keep their values;
+ *   - the candidates go to slot 1-L, and the header becomes
+ *     {(1-L) | parity << 1, n_rows[1-L] = n_cand, n_rows[L] as it was,
+ *     accepted = a}.
+ * out (4 ints, optional): a, the number of replayed rows, the replayed slot
+ * and the written slot.
+ */
+#define ORA_BOOK_ACCEPTED 1
+#define ORA_BOOK_PARITY 2
+#define ORA_BOOK_ARG 16
+
+int ora_book_step(int32_t W, int32_t n_spec, int32_t C, int32_t rows, int32_t n_cand,
+                  int32_t num_accepted, int32_t parity, uint32_t* hdr, double* cbuf,
+                  const double* x, int32_t* out) {
+    if (W < 2 || n_spec < 0 || C < 0 || rows < W - 1 + n_spec || n_cand < 0 || n_cand > n_spec + 1 ||
+        (parity != 0 && parity != 1))
+        return ORA_BOOK_ARG;
+    const uint32_t flag = hdr[0];
+    const int32_t L = (int32_t)(flag & 1u);
+    const int32_t P = (int32_t)((flag >> 1) & 1u);
+    const int32_t held = (int32_t)hdr[1 + L];
+    if (parity == P) return ORA_BOOK_PARITY;
+    int32_t a = 0;
+    if (held > 0) {
+        if (num_accepted < 0 || num_accepted >= held || held > n_spec + 1) return ORA_BOOK_ACCEPTED;
+        a = num_accepted;
+    }
+    /* the window a .. a+W-2, read before any row is written */
+    double* win = (double*)malloc(sizeof(double) * (size_t)(W - 1) * (size_t)(C > 0 ? C : 1));
+    for (int32_t j = 0; j < W - 1; ++j)
+        memcpy(win + (int64_t)j * C, cbuf + (int64_t)(a + j) * C, sizeof(double) * (size_t)C);
+    if (n_cand > 0) {
+        for (int32_t j = 0; j < W - 2; ++j)
+            memcpy(cbuf + (int64_t)j * C, win + (int64_t)(j + 1) * C, sizeof(double) * (size_t)C);
+        memcpy(cbuf + (int64_t)(W - 2) * C, x, sizeof(double) * (size_t)n_cand * (size_t)C);
+    } else {
+        memcpy(cbuf, win, sizeof(double) * (size_t)(W - 1) * (size_t)C);
+    }
+    free(win);
+    hdr[0] = (uint32_t)(1 - L) | ((uint32_t)parity << 1);
+    hdr[1 + (1 - L)] = (uint32_t)n_cand;
+    hdr[3] = (uint32_t)a;
+    if (out) {
+        out[0] = a;
+        out[1] = held > 0 ? a + 1 : 0;
+        out[2] = L;
+        out[3] = 1 - L;
     }
     return 0;
 }

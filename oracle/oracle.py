@@ -44,6 +44,7 @@ def lib():
         L.ora_layer.restype = ctypes.c_int
         L.ora_verify.restype = ctypes.c_int
         L.ora_conv_update.restype = ctypes.c_int
+        L.ora_book_step.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -217,6 +218,53 @@ def verify(dm: OraDims, conv_w, a_log, dt_bias, x, a, b, accepted, window0, S0,
     if rc != 0:
         raise ValueError(f"ora_verify returned {rc}")
     return o, win, S
+
+
+# ------------------------------------------------- verify page bookkeeping
+BOOK_ACCEPTED, BOOK_PARITY, BOOK_ARG = 1, 2, 16
+
+
+def book_step(W: int, n_spec: int, hdr, cbuf, x, num_accepted: int, parity: int):
+    """One verify step's page bookkeeping for one request (``ora_book_step``).
+    hdr: 4 uint32 {flag, n_rows[0], n_rows[1], accepted}; cbuf [rows][C] conv
+    buffer; x [n_cand][C] candidate rows (n_cand may be 0).  Returns
+    (err, hdr', cbuf', info) with info = (a, replayed rows, replayed slot,
+    written slot); on a refusal hdr' and cbuf' equal the inputs."""
+    h = np.ascontiguousarray(hdr, dtype=np.uint32).copy()
+    cb = _d(cbuf).copy()
+    rows, C = cb.shape
+    xx = _d(x).reshape(-1, C) if x is not None else np.zeros((0, C))
+    out = np.zeros(4, dtype=np.int32)
+    err = lib().ora_book_step(ctypes.c_int32(W), ctypes.c_int32(n_spec), ctypes.c_int32(C), ctypes.c_int32(rows),
+                              ctypes.c_int32(xx.shape[0]), ctypes.c_int32(int(num_accepted)),
+                              ctypes.c_int32(int(parity)), h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                              _ptr(cb), _ptr(xx), _ptr(out, _ip))
+    return int(err), h, cb, tuple(int(v) for v in out)
+
+
+def book_batch(W: int, n_spec: int, hdrs, cbufs, req_page, x, num_accepted, parity):
+    """The bookkeeping of one verify step over a request batch: request r
+    works on page req_page[r] (< 0: padding, nothing touched; >= the number
+    of pages: refused, nothing touched).  hdrs [n_pages][4], cbufs
+    [n_pages][rows][C], x [n_req][n_cand][C].  Returns (per-request error
+    codes, with -1 for a page out of range, hdrs', cbufs')."""
+    hdrs = np.ascontiguousarray(hdrs, dtype=np.uint32).copy()
+    cbufs = _d(cbufs).copy()
+    errs = []
+    for r, p in enumerate(req_page):
+        p = int(p)
+        if p < 0:
+            errs.append(0)
+            continue
+        if p >= hdrs.shape[0]:
+            errs.append(-1)
+            continue
+        e, h, cb, _ = book_step(W, n_spec, hdrs[p], cbufs[p], x[r] if x is not None else None,
+                                num_accepted[r], parity[r])
+        errs.append(e)
+        if e == 0:
+            hdrs[p], cbufs[p] = h, cb
+    return errs, hdrs, cbufs
 
 
 def max_rel(y, ref) -> float:

@@ -129,6 +129,96 @@ def test_conv_f32_model_within_rounding(ora):
     assert y32.dtype == np.float32
 
 
+def _round_f32_exact(v):
+    """Round an exact rational to the nearest binary32 value, ties to even
+    (normal and subnormal range; the inputs here never overflow)."""
+    from fractions import Fraction
+    if v == 0:
+        return 0.0
+    sign = -1.0 if v < 0 else 1.0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+1), within one
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    m = a / quantum
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    r = n * quantum
+    assert r < Fraction(2) ** 128
+    return sign * float(r)   # exact: r is a binary32 value
+
+
+def _conv_chain_exact(x, w, win, order, fused=True):
+    """The conv without activation evaluated in exact rationals, rounded to
+    binary32 after every operation of a chain acc = 0, acc = fma(w_j, x_j, acc)
+    over the taps in `order` (fused: one rounding per tap; unfused: the
+    product rounded, then the sum)."""
+    from fractions import Fraction
+    T, C = x.shape
+    Wd = w.shape[1]
+    full = np.concatenate([win, x]).astype(np.float32)
+    y = np.zeros((T, C), np.float32)
+    for t in range(T):
+        for c in range(C):
+            acc = Fraction(0)
+            for j in order:
+                prod = Fraction(float(w[c, j])) * Fraction(float(full[t + j, c]))
+                if not fused:
+                    prod = Fraction(_round_f32_exact(prod))
+                acc = Fraction(_round_f32_exact(prod + acc))
+            y[t, c] = float(acc)
+    return y
+
+
+def test_round_f32_exact_helper():
+    """The exact-rounding helper of the next test against numpy's binary64 ->
+    binary32 conversion (exact for these values: they are binary64 numbers
+    whose rounding to binary32 is not a double rounding)."""
+    from fractions import Fraction
+    r = rng(50)
+    vals = np.concatenate([r.standard_normal(2000), r.standard_normal(200) * 1e-40,
+                           [1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24, -(1.0 + 2.0 ** -24), 2.0 ** -150,
+                            3 * 2.0 ** -150, 2.0 ** -149]])
+    for v in vals:
+        assert _round_f32_exact(Fraction(float(v))) == float(np.float32(v)), v
+
+
+@pytest.mark.parametrize("dtype_in", ["f32", "bf16"])
+def test_conv_f32_model_equals_exact_fma_chain(ora, dtype_in):
+    """ora_conv_f32_model fixes the bits the single-precision conv must
+    produce: acc = 0, one fused multiply-add per tap, oldest tap first.  It is
+    checked here bit for bit against that chain evaluated in exact rationals
+    with one rounding per tap (inputs drawn in fp32 and in bf16, the two
+    activation dtypes).  The same inputs separate the chain from its
+    plausible variants (newest tap first; with fp32 inputs also product and
+    sum rounded separately), so the pin decides the order, not only the
+    rounding bound."""
+    r = rng(51)
+    T, C, Wd = 9, 12, 4
+    x = r.standard_normal((T, C)).astype(np.float32)
+    w = (0.25 * r.standard_normal((C, Wd))).astype(np.float32)
+    win = r.standard_normal((Wd - 1, C)).astype(np.float32)
+    if dtype_in == "bf16":
+        x, w, win = (wk.round_to(a, wk.BF16) for a in (x, w, win))
+    got = ora.conv_f32_model(x, w, win)
+    oldest_first = _conv_chain_exact(x, w, win, range(Wd))
+    np.testing.assert_array_equal(got, oldest_first)
+    newest_first = _conv_chain_exact(x, w, win, range(Wd - 1, -1, -1))
+    unfused = _conv_chain_exact(x, w, win, range(Wd), fused=False)
+    assert np.any(newest_first != oldest_first)
+    if dtype_in == "f32":
+        assert np.any(unfused != oldest_first)
+    else:
+        # a product of two bf16 values has at most 16 significant bits, so it
+        # is exact in binary32 and fusing makes no difference
+        np.testing.assert_array_equal(unfused, oldest_first)
+
+
 def test_conv_update_ragged_and_has_init(ora):
     r = rng(6)
     C, W = 5, 4
