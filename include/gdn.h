@@ -44,6 +44,10 @@
  *   zero when its kernels complete; a call aborted midway must be followed
  *   by re-zeroing them.
  * - Calls that touch the same pages must be ordered (same stream, or events).
+ *   Calls that share a conv pool's sync words must be ordered too, even on
+ *   disjoint pages: the decode kernel of gdn_recurrent_seq hands out its
+ *   work from the one work counter after the arrival counters, so two such
+ *   calls in flight at once would draw from the same counter.
  * - Every compute call can be captured in a HIP graph and replayed: its host
  *   arguments are shapes, strides, host bounds and device pointers; every
  *   value that changes from step to step (lengths, page indices, acceptance
@@ -65,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 /* status codes returned by every entry point */
 #define GDN_OK 0
@@ -86,6 +90,7 @@ extern "C" {
 #define GDN_DEVERR_BATCH 2u     /* cu_seqlens decreasing or beyond n_rows */
 #define GDN_DEVERR_ACCEPTED 4u  /* num_accepted >= rows held by the live record */
 #define GDN_DEVERR_PARITY 8u    /* step parity equals the live record's: step already applied */
+#define GDN_DEVERR_CACHE 16u    /* prefix-cache entry out of range, or cached row beyond the replay */
 
 typedef struct gdn_dims {
     int32_t h_k, h_v;      /* key heads, value heads; h_v % h_k == 0 */
@@ -286,6 +291,58 @@ int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* params, int32_t 
                         void* pages, int64_t page_bytes, int32_t n_pages,
                         gdn_conv_pool conv, float* o, int32_t* err, void* stream);
 
+/* ----------------------------------------- prefix cache beside the record */
+
+/* Cached committed prefixes of speculative requests.  The one-page design of
+ * "r9700-stack v0.2.4" (section "What it does") is switched off there when
+ * prefix caching is on; here a cache entry coexists with the record: entry e
+ * holds a committed state at state.base + e*state.page_stride (state dtype,
+ * [h_v][d_k][d_v]) and the conv window that ends with it in rows 0..W-2 of
+ * conv page e (act dtype, oldest row first).  conv.sync is not used.
+ * Entries written by one call must be distinct. */
+typedef struct gdn_prefix_cache {
+    const int32_t* entry;  /* [n_req] entry to write, < 0: none */
+    const int32_t* row;    /* [n_req] the cached prefix ends at replayed record row `row`, 0..num_accepted */
+    gdn_state_pool state;  /* n_pages = entries */
+    gdn_conv_pool conv;    /* rows >= W-1, n_pages = entries */
+} gdn_prefix_cache;
+
+/* gdn_spec_verify, writing cached prefixes during the same step (no extra
+ * launch).  For request r with cache->entry[r] >= 0: when the live record
+ * holds rows, the committed stream grows by the replayed rows 0..a' and the
+ * entry receives the prefix that ends at replayed row j = cache->row[r]
+ * (0 <= j <= a'): the state after row j, rounded to the state dtype exactly
+ * as a checkpoint is (j = a' gives the new checkpoint itself; the slot design
+ * copies slot j, which holds the same bits), and conv buffer rows j..j+W-2.
+ * When the live record holds no rows, the entry receives the checkpoint and
+ * conv rows 0..W-2 as they are (row ignored).  An entry >= the cache's
+ * entries or a row outside 0..a' refuses the request (GDN_DEVERR_CACHE):
+ * nothing of it is written.  Every other argument, result and error is that
+ * of gdn_spec_verify; cache == NULL is gdn_spec_verify. */
+int32_t gdn_spec_verify_cached(const gdn_dims* dims, const gdn_params* params, int32_t layout,
+                               const void* x, int64_t x_stride,
+                               const void* a, const void* b, int64_t ab_stride,
+                               int32_t n_req, int32_t n_cand,
+                               const int32_t* req_page, const int32_t* num_accepted,
+                               const uint8_t* step_parity,
+                               void* pages, int64_t page_bytes, int32_t n_pages,
+                               gdn_conv_pool conv, const gdn_prefix_cache* cache,
+                               float* o, int32_t* err, void* stream);
+
+/* Restore cached prefixes into pages: for request r with entry[r] >= 0 and
+ * req_page[r] >= 0, the page's state region (the one-page checkpoint, or
+ * slot 0 of the slot design) receives entry[r]'s state, its conv rows
+ * 0..W-2 the entry's window, and its header is zeroed: the page is fresh, so
+ * its next verify step replays nothing and starts from the restored state.
+ * cache->entry and cache->row are not read (entry is the argument).  An
+ * entry or page out of range skips the request (GDN_DEVERR_CACHE,
+ * GDN_DEVERR_PAGE).  Pages of one call must be distinct. */
+int32_t gdn_prefix_restore(const gdn_dims* dims, int32_t layout, int32_t n_req,
+                           const int32_t* entry, const int32_t* req_page,
+                           const gdn_prefix_cache* cache,
+                           void* pages, int64_t page_bytes, int32_t n_pages,
+                           gdn_conv_pool conv, int32_t* err, void* stream);
+
 /* ------------------------------------------------------- mixed step */
 
 /* The token-by-token part of a mixed step: the arguments of
@@ -335,9 +392,9 @@ typedef struct gdn_verify_part {
 
 /* One serving step that mixes token-by-token sequences (prefill or decode
  * rows of a ragged batch) with speculative verify requests, in ONE launch
- * ("r9700-stack v0.2.3", section "1. Time to first token": both kernels
- * address the batch's own rows, so a step that mixes prefills with running
- * spec-decode sequences needs no gather).  The result is that of
+ * ("r9700-stack v0.2.3", section "1. Time to first token": the prefill
+ * and verify kernels read their rows where the batch holds them, so such a
+ * step gathers nothing first).  The result is that of
  * gdn_recurrent_seq on `seq` followed by gdn_spec_verify on `verify`, bit
  * for bit; the sequence workgroups come first in the grid (longest sequence
  * first), and the verify workgroups fill the slots shorter sequences free.

@@ -12,18 +12,18 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdn.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_SPEC_ONEPAGE, GDN_SPEC_SLOTS = 0, 1
-GDN_DEVERR_PAGE, GDN_DEVERR_BATCH, GDN_DEVERR_ACCEPTED, GDN_DEVERR_PARITY = 1, 2, 4, 8
+GDN_DEVERR_PAGE, GDN_DEVERR_BATCH, GDN_DEVERR_ACCEPTED, GDN_DEVERR_PARITY, GDN_DEVERR_CACHE = 1, 2, 4, 8, 16
 GDN_PATH_TOKEN, GDN_PATH_CHUNKED = 0, 1
 GDN_PREFILL_MAX_DEFAULT = -1
 
 SYMBOLS = ("gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout", "gdn_chunked_workspace_bytes",
            "gdn_conv_update", "gdn_recurrent_seq", "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill",
-           "gdn_spec_verify", "gdn_mixed_step")
+           "gdn_spec_verify", "gdn_spec_verify_cached", "gdn_prefix_restore", "gdn_mixed_step")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -57,6 +57,10 @@ class GdnSpecLayout(ctypes.Structure):
     _fields_ = [("page_bytes", ctypes.c_size_t), ("header_off", ctypes.c_size_t),
                 ("state_off", ctypes.c_size_t), ("record_off", ctypes.c_size_t),
                 ("record_row_bytes", ctypes.c_size_t)]
+
+
+class GdnPrefixCache(ctypes.Structure):
+    _fields_ = [("entry", _vp), ("row", _vp), ("state", GdnStatePool), ("conv", GdnConvPool)]
 
 
 class GdnSeqPart(ctypes.Structure):
@@ -119,6 +123,13 @@ def load() -> ctypes.CDLL:
     L.gdn_spec_verify.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _i32, _vp, _i64, _vp,
                                   _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, GdnConvPool, _vp,
                                   _vp, _vp]
+    L.gdn_spec_verify_cached.restype = _i32
+    L.gdn_spec_verify_cached.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _i32, _vp, _i64, _vp,
+                                         _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, GdnConvPool,
+                                         ctypes.POINTER(GdnPrefixCache), _vp, _vp, _vp]
+    L.gdn_prefix_restore.restype = _i32
+    L.gdn_prefix_restore.argtypes = [ctypes.POINTER(GdnDims), _i32, _i32, _vp, _vp, ctypes.POINTER(GdnPrefixCache),
+                                     _vp, _i64, _i32, GdnConvPool, _vp, _vp]
     L.gdn_mixed_step.restype = _i32
     L.gdn_mixed_step.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), ctypes.POINTER(GdnSeqPart),
                                  ctypes.POINTER(GdnVerifyPart), _vp, _vp]

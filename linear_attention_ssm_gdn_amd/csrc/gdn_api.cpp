@@ -278,11 +278,23 @@ GDN_EXPORT int32_t gdn_prefill(const gdn_dims* dims, const gdn_params* params, c
     return gdn_recurrent_seq(dims, params, x, x_stride, a, b, ab_stride, batch, conv, state, o, err, stream);
 }
 
-GDN_EXPORT int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* params, int32_t layout, const void* x,
-                                   int64_t x_stride, const void* a, const void* b, int64_t ab_stride, int32_t n_req,
-                                   int32_t n_cand, const int32_t* req_page, const int32_t* num_accepted,
-                                   const uint8_t* step_parity, void* pages, int64_t page_bytes, int32_t n_pages,
-                                   gdn_conv_pool conv, float* o, int32_t* err, void* stream) {
+namespace {
+// A prefix cache's pools: states of the state dtype, windows of W-1 rows.
+int32_t check_prefix_cache(const gdn_dims* dims, const gdn_prefix_cache& c, bool need_index) {
+    int32_t st;
+    if (need_index && (!c.entry || !c.row)) return GDN_ERR_ARG;
+    if ((st = check_state_pool(dims, c.state)) != GDN_OK) return st;
+    if ((st = check_conv_pool(dims, c.conv, dims->conv_w - 1, false)) != GDN_OK) return st;
+    return GDN_OK;
+}
+}  // namespace
+
+GDN_EXPORT int32_t gdn_spec_verify_cached(const gdn_dims* dims, const gdn_params* params, int32_t layout,
+                                          const void* x, int64_t x_stride, const void* a, const void* b,
+                                          int64_t ab_stride, int32_t n_req, int32_t n_cand, const int32_t* req_page,
+                                          const int32_t* num_accepted, const uint8_t* step_parity, void* pages,
+                                          int64_t page_bytes, int32_t n_pages, gdn_conv_pool conv,
+                                          const gdn_prefix_cache* cache, float* o, int32_t* err, void* stream) {
     int32_t st;
     if ((st = check_dims(dims)) != GDN_OK) return st;
     if ((st = check_params(params)) != GDN_OK) return st;
@@ -290,11 +302,56 @@ GDN_EXPORT int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* param
     if ((st = check_verify_call(dims, layout, x, x_stride, a, b, ab_stride, n_req, n_cand, req_page, num_accepted,
                                 step_parity, pages, page_bytes, n_pages, conv, o, &L)) != GDN_OK)
         return st;
+    if (cache && (st = check_prefix_cache(dims, *cache, true)) != GDN_OK) return st;
     if (n_req == 0) return GDN_OK;
-    const gdn::VerifyArgs A = verify_args(dims, params, L, x, x_stride, a, b, ab_stride, n_req, n_cand, req_page,
-                                          num_accepted, step_parity, pages, page_bytes, n_pages, conv, o, err);
+    gdn::VerifyArgs A = verify_args(dims, params, L, x, x_stride, a, b, ab_stride, n_req, n_cand, req_page,
+                                    num_accepted, step_parity, pages, page_bytes, n_pages, conv, o, err);
+    if (cache) {
+        A.cache_entry = cache->entry; A.cache_row = cache->row;
+        A.cache_state = cache->state.base; A.cache_state_stride = cache->state.page_stride;
+        A.cache_state_n = cache->state.n_pages;
+        A.cache_conv = cache->conv.base; A.cache_conv_stride = cache->conv.page_stride;
+        A.cache_conv_n = cache->conv.n_pages;
+    }
     return from_hip(gdn::launch_verify(A, dims->d_k, dims->act_dtype, dims->state_dtype, layout,
                                        (hipStream_t)stream));
+}
+
+GDN_EXPORT int32_t gdn_spec_verify(const gdn_dims* dims, const gdn_params* params, int32_t layout, const void* x,
+                                   int64_t x_stride, const void* a, const void* b, int64_t ab_stride, int32_t n_req,
+                                   int32_t n_cand, const int32_t* req_page, const int32_t* num_accepted,
+                                   const uint8_t* step_parity, void* pages, int64_t page_bytes, int32_t n_pages,
+                                   gdn_conv_pool conv, float* o, int32_t* err, void* stream) {
+    return gdn_spec_verify_cached(dims, params, layout, x, x_stride, a, b, ab_stride, n_req, n_cand, req_page,
+                                  num_accepted, step_parity, pages, page_bytes, n_pages, conv, nullptr, o, err,
+                                  stream);
+}
+
+GDN_EXPORT int32_t gdn_prefix_restore(const gdn_dims* dims, int32_t layout, int32_t n_req, const int32_t* entry,
+                                      const int32_t* req_page, const gdn_prefix_cache* cache, void* pages,
+                                      int64_t page_bytes, int32_t n_pages, gdn_conv_pool conv, int32_t* err,
+                                      void* stream) {
+    int32_t st;
+    if ((st = check_dims(dims)) != GDN_OK) return st;
+    gdn_spec_layout L{};
+    if ((st = gdn_spec_page_layout(dims, layout, &L)) != GDN_OK) return st;
+    if (n_req < 0 || !cache) return GDN_ERR_ARG;
+    if (n_req == 0) return GDN_OK;
+    if (!entry || !req_page || !pages || n_pages < 0) return GDN_ERR_ARG;
+    if (page_bytes < (int64_t)L.page_bytes || page_bytes % 256 != 0 || !aligned(pages, 256)) return GDN_ERR_ARG;
+    if ((st = check_conv_pool(dims, conv, dims->conv_w - 1, false)) != GDN_OK) return st;
+    if ((st = check_prefix_cache(dims, *cache, false)) != GDN_OK) return st;
+    gdn::RestoreArgs A{};
+    A.n_req = n_req; A.entry = entry; A.req_page = req_page;
+    A.cache_state = cache->state.base; A.cache_state_stride = cache->state.page_stride;
+    A.cache_state_n = cache->state.n_pages;
+    A.cache_conv = cache->conv.base; A.cache_conv_stride = cache->conv.page_stride; A.cache_conv_n = cache->conv.n_pages;
+    A.pages = static_cast<uint8_t*>(pages); A.page_bytes = page_bytes; A.n_pages = n_pages;
+    A.header_off = (int64_t)L.header_off; A.state_off = (int64_t)L.state_off;
+    A.conv_base = conv.base; A.conv_page_stride = conv.page_stride; A.conv_n_pages = conv.n_pages;
+    A.err = err; A.h_v = dims->h_v; A.d_k = dims->d_k; A.d_v = dims->d_v; A.conv_rows = dims->conv_w - 1;
+    A.C = (int32_t)c_conv(dims);
+    return from_hip(gdn::launch_restore(A, dims->act_dtype, dims->state_dtype, (hipStream_t)stream));
 }
 
 GDN_EXPORT int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,

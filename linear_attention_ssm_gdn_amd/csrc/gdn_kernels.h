@@ -48,6 +48,23 @@ struct VerifyArgs {
     int32_t* err;
     int32_t h_k, h_v, d_v, n_spec;
     float scale, eps;
+    // optional prefix cache: request r writes the committed prefix that ends
+    // at replayed record row cache_row[r] into entry cache_entry[r]
+    const int32_t* cache_entry; const int32_t* cache_row;
+    void* cache_state; int64_t cache_state_stride; int32_t cache_state_n;
+    void* cache_conv; int64_t cache_conv_stride; int32_t cache_conv_n;
+};
+
+struct RestoreArgs {
+    int32_t n_req;
+    const int32_t* entry; const int32_t* req_page;
+    const void* cache_state; int64_t cache_state_stride; int32_t cache_state_n;
+    const void* cache_conv; int64_t cache_conv_stride; int32_t cache_conv_n;
+    uint8_t* pages; int64_t page_bytes; int32_t n_pages;
+    int64_t header_off, state_off;
+    void* conv_base; int64_t conv_page_stride; int32_t conv_n_pages;
+    int32_t* err;
+    int32_t h_v, d_k, d_v, conv_rows, C;
 };
 
 struct ChunkArgs {
@@ -69,6 +86,7 @@ hipError_t launch_seq(const SeqArgs& a, int d_k, int act_dtype, int state_dtype,
 hipError_t launch_conv(const ConvArgs& a, int act_dtype, int y_dtype, int max_seqlen, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs& a, int d_k, int act_dtype, int state_dtype, int layout,
                          hipStream_t s);
+hipError_t launch_restore(const RestoreArgs& a, int act_dtype, int state_dtype, hipStream_t s);
 hipError_t launch_chunked(const ChunkArgs& a, int d_k, int act_dtype, int state_dtype, hipStream_t s);
 // One launch running the token-by-token workgroups of `s` and the verify
 // workgroups of `v` (either part may be empty: n_seqs or n_req == 0).

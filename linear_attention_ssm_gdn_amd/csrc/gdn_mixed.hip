@@ -1,9 +1,9 @@
 // gdn_mixed.hip -- one launch for a serving step that mixes token-by-token
 // sequences (prefill or decode rows of a ragged batch) with speculative
 // verify requests ("r9700-stack v0.2.3", section "1. Time to first token":
-// both kernels address the batch's own rows, so a step that mixes prefills
-// with running spec-decode sequences needs no gather; "r9700-stack v0.2.4"
-// names the mixed-step path beside the one-page verify).
+// the prefill and verify kernels read their rows in place, so a mixed step
+// gathers nothing; "r9700-stack v0.2.4" names the mixed-step path beside
+// the one-page verify).
 //
 // Grid, in the order workgroups are handed out: the workgroups of the
 // token-by-token part (gdn_seq_block.hpp, 32 columns each, ranked longest

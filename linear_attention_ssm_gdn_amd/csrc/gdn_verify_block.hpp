@@ -15,6 +15,13 @@
 //
 // Grid: one workgroup per (request, value head, block of 32*CPL value
 // columns), the lane layout of gdn_block.hpp.  Candidates per step <= 16.
+//
+// With CACHE, a request may also leave a committed prefix in a cache entry:
+// the state after replayed record row j (the running state of the replay,
+// rounded to the state dtype as a checkpoint is) and the conv window that
+// ends at that row, buffer rows j .. j+W-2.  The slot design holds that
+// state already, in slot j, and copies it; an empty live record caches the
+// checkpoint as it is with window rows 0 .. W-2.
 #pragma once
 
 #include "gdn_block.hpp"
@@ -25,7 +32,7 @@ namespace gdn {
 
 constexpr int VER_TT = 16;
 
-template <typename ActT, typename StT, int DK, int CPL, int LAYOUT>
+template <typename ActT, typename StT, int DK, int CPL, int LAYOUT, bool CACHE = false>
 __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int block) {
     constexpr int TT = VER_TT;
     constexpr int R = DK / 16;
@@ -77,6 +84,20 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
             return;
         }
     }
+    // ---- prefix cache: entry `cache_e` takes the committed prefix that ends
+    // at replayed row `cache_j` (0 .. acc), or the checkpoint itself when the
+    // live record holds no rows
+    int cache_e = -1, cache_j = 0;
+    if constexpr (CACHE) {
+        cache_e = A.cache_entry[req];
+        if (cache_e >= 0) {
+            cache_j = nr > 0 ? A.cache_row[req] : 0;
+            if (cache_e >= A.cache_state_n || cache_e >= A.cache_conv_n || cache_j < 0 || cache_j > acc) {
+                if (reporter) set_err(A.err, GDN_DEVERR_CACHE);
+                return;
+            }
+        }
+    }
     const int n_replay = (LAYOUT == GDN_SPEC_ONEPAGE && nr > 0) ? acc + 1 : 0;
     const int nc = A.n_cand;
 
@@ -109,6 +130,15 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         xw0 = to_f32(cbuf[(int64_t)(acc + 0) * C + gc]);
         xw1 = to_f32(cbuf[(int64_t)(acc + 1) * C + gc]);
         xw2 = to_f32(cbuf[(int64_t)(acc + 2) * C + gc]);
+    }
+    // the cached prefix's window: buffer rows cache_j .. cache_j+2
+    float cw0 = 0.0f, cw1 = 0.0f, cw2 = 0.0f;
+    if constexpr (CACHE) {
+        if (cache_e >= 0 && lc < NLC) {
+            cw0 = to_f32(cbuf[(int64_t)(cache_j + 0) * C + gc]);
+            cw1 = to_f32(cbuf[(int64_t)(cache_j + 1) * C + gc]);
+            cw2 = to_f32(cbuf[(int64_t)(cache_j + 2) * C + gc]);
+        }
     }
     float* ydst = lc < DK ? sq + qk_pos<DK>(lc) : lc < 2 * DK ? sk + qk_pos<DK>(lc - DK) : sv + (lc - 2 * DK);
     const int yld = lc < 2 * DK ? DK : BV;
@@ -202,6 +232,7 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         float exp_pin = exp_alog;
         asm volatile("" : "+v"(exp_pin), "+v"(pa), "+v"(pb), "+v"(ra), "+v"(rb), "+v"(xw0), "+v"(xw1), "+v"(xw2));
         asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+        if constexpr (CACHE) asm volatile("" : "+v"(cw0), "+v"(cw1), "+v"(cw2));
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) asm volatile("" : "+v"(xp[tt]));
         exp_alog_v = exp_pin;
@@ -210,6 +241,25 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
 
     float s[CPL][R];
     load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
+
+    StT* __restrict__ cst = nullptr;  // this workgroup's block of the cache entry's state
+    if constexpr (CACHE) {
+        if (cache_e >= 0) {
+            cst = static_cast<StT*>(A.cache_state) + (int64_t)cache_e * A.cache_state_stride +
+                  (int64_t)h * head_elems + colbase;
+            if (LAYOUT == GDN_SPEC_SLOTS && cache_j != acc) {
+                // slot cache_j holds the prefix's state; this workgroup owns its
+                // columns in every slot, and no slot is written before this copy
+                const StT* src = st_base + ((int64_t)cache_j * A.h_v + h) * head_elems + colbase;
+                for (int i = tid; i < DK * BV; i += BLOCK_THREADS)
+                    cst[(int64_t)(i / BV) * A.d_v + (i % BV)] = src[(int64_t)(i / BV) * A.d_v + (i % BV)];
+            } else if (LAYOUT == GDN_SPEC_SLOTS || n_replay == 0) {
+                // the loaded state is the prefix's state (stored values: exact)
+                store_state<StT, DK, CPL>(cst, A.d_v, s, tid);
+            }
+        }
+    }
+    const int cache_at = (CACHE && LAYOUT == GDN_SPEC_ONEPAGE && cache_e >= 0 && n_replay > 0) ? cache_j : -1;
 
     // ---- candidates: conv (+ record) into rows crow.., then gating
     const bool qk_writer = (h == ki * rr) && (blk == 0);
@@ -294,9 +344,11 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         for (int tt = 0; tt < n_replay; tt += 2) {
             roperands(r1, tt + 1 < n_replay ? tt + 1 : tt);
             delta_update<R, CPL>(s, r0.k, r0.v, r0.eg, r0.beta);
+            if (CACHE && tt == cache_at) store_state<StT, DK, CPL>(cst, A.d_v, s, tid);
             if (tt + 1 < n_replay) {
                 roperands(r0, tt + 2 < n_replay ? tt + 2 : tt + 1);
                 delta_update<R, CPL>(s, r1.k, r1.v, r1.eg, r1.beta);
+                if (CACHE && tt + 1 == cache_at) store_state<StT, DK, CPL>(cst, A.d_v, s, tid);
             }
         }
     }
@@ -393,6 +445,17 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
             cbuf[0 * C + gc] = from_f32<ActT>(xw0);
             cbuf[1 * C + gc] = from_f32<ActT>(xw1);
             cbuf[2 * C + gc] = from_f32<ActT>(xw2);
+        }
+    }
+
+    // ---- the cached prefix's window (v channels by every workgroup, q/k
+    // channels by the key head's recording workgroup)
+    if constexpr (CACHE) {
+        if (cache_e >= 0 && gc >= 0 && (lc >= 2 * DK || qk_writer)) {
+            ActT* __restrict__ cc = static_cast<ActT*>(A.cache_conv) + (int64_t)cache_e * A.cache_conv_stride;
+            cc[0 * C + gc] = from_f32<ActT>(cw0);
+            cc[1 * C + gc] = from_f32<ActT>(cw1);
+            cc[2 * C + gc] = from_f32<ActT>(cw2);
         }
     }
 

@@ -267,24 +267,63 @@ class SpecPages:
             self.buf.shape[0], self.n_slots, d.h_v, d.d_k, d.d_v)
 
 
+@dataclasses.dataclass
+class PrefixCache:
+    """Cached committed prefixes: entry e holds a state (state pool page e)
+    and the conv window that ends with it (conv pool page e, rows 0..W-2)."""
+    state: StatePool
+    conv: ConvPool
+
+    @staticmethod
+    def alloc(dims: Dims, n_entries: int, device) -> "PrefixCache":
+        return PrefixCache(StatePool.alloc(dims, n_entries, device),
+                           ConvPool.alloc(dims, n_entries, dims.conv_w - 1, device))
+
+    def c(self, entry: Optional[torch.Tensor] = None, row: Optional[torch.Tensor] = None) -> L.GdnPrefixCache:
+        return L.GdnPrefixCache(_ptr(entry), _ptr(row), self.state.c(), self.conv.c())
+
+
 def gdn_spec_verify(dims: Dims, params: Params, pages: SpecPages, x: Optional[torch.Tensor],
                     a: Optional[torch.Tensor], b: Optional[torch.Tensor], n_req: int, n_cand: int,
                     req_page: torch.Tensor, num_accepted: torch.Tensor, step_parity: torch.Tensor,
                     conv: ConvPool, o: Optional[torch.Tensor] = None,
-                    err: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+                    err: Optional[torch.Tensor] = None, cache: Optional[PrefixCache] = None,
+                    cache_entry: Optional[torch.Tensor] = None,
+                    cache_row: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """gdn_spec_verify, or gdn_spec_verify_cached when `cache` is given (with
+    int32 device tensors cache_entry and cache_row, one entry per request)."""
     dev = req_page.device
     if o is None and n_cand > 0:
         o = torch.empty((n_req * n_cand, dims.h_v, dims.d_v), dtype=torch.float32, device=dev)
     xs = _rows(x, "x") if x is not None else 0
     abs_ = _rows(a, "a") if a is not None else 0
     d, p = dims.c(), params.c()
-    st = L.load().gdn_spec_verify(ctypes.byref(d), ctypes.byref(p), pages.layout, _ptr(x), xs, _ptr(a),
-                                  _ptr(b), abs_, n_req, n_cand, req_page.data_ptr(), num_accepted.data_ptr(),
-                                  step_parity.data_ptr(), pages.buf.data_ptr(), pages.buf.stride(0),
-                                  pages.buf.shape[0], conv.c(), _ptr(o), _ptr(err),
-                                  torch.cuda.current_stream(dev).cuda_stream)
-    _check("gdn_spec_verify", st)
+    args = (ctypes.byref(d), ctypes.byref(p), pages.layout, _ptr(x), xs, _ptr(a), _ptr(b), abs_, n_req, n_cand,
+            req_page.data_ptr(), num_accepted.data_ptr(), step_parity.data_ptr(), pages.buf.data_ptr(),
+            pages.buf.stride(0), pages.buf.shape[0], conv.c())
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if cache is None:
+        st = L.load().gdn_spec_verify(*args, _ptr(o), _ptr(err), stream)
+        _check("gdn_spec_verify", st)
+    else:
+        if cache_entry is None or cache_row is None:
+            raise ValueError("a prefix cache needs cache_entry and cache_row")
+        pc = cache.c(cache_entry, cache_row)
+        st = L.load().gdn_spec_verify_cached(*args, ctypes.byref(pc), _ptr(o), _ptr(err), stream)
+        _check("gdn_spec_verify_cached", st)
     return o
+
+
+def gdn_prefix_restore(dims: Dims, pages: SpecPages, entry: torch.Tensor, req_page: torch.Tensor,
+                       cache: PrefixCache, conv: ConvPool, err: Optional[torch.Tensor] = None) -> None:
+    """Restore cached prefixes entry[r] into pages req_page[r] (fresh headers)."""
+    d = dims.c()
+    pc = cache.c()
+    st = L.load().gdn_prefix_restore(ctypes.byref(d), pages.layout, int(entry.numel()), entry.data_ptr(),
+                                     req_page.data_ptr(), ctypes.byref(pc), pages.buf.data_ptr(),
+                                     pages.buf.stride(0), pages.buf.shape[0], conv.c(), _ptr(err),
+                                     torch.cuda.current_stream(entry.device).cuda_stream)
+    _check("gdn_prefix_restore", st)
 
 
 def gdn_mixed_step(dims: Dims, params: Params, seq: Optional[dict] = None, verify: Optional[dict] = None,

@@ -117,3 +117,123 @@ def max_slice_rel_S(S, S_ref):
         for h in range(S_ref.shape[1]):
             worst = max(worst, rel(S[s, h], S_ref[s, h]))
     return worst
+
+
+class BookModel:
+    """The oracle's bookkeeping model of verify pages (oracle.book_batch),
+    stepped beside a GPU run: headers (flag, n_rows, acceptance echo), the
+    whole conv buffer of every page and the sticky error bits, compared bit
+    for bit with the GPU's after each step."""
+
+    def __init__(self, dims, n_pages, rows, req_page, window0):
+        import oracle
+        self.ora = oracle
+        self.W, self.n_spec = dims.conv_w, dims.n_spec
+        C = dims.c_conv
+        self.hdr = np.zeros((n_pages, 4), np.uint32)
+        self.cbuf = np.zeros((n_pages, rows, C))
+        for r, p in enumerate(req_page):
+            if 0 <= p < n_pages:
+                self.cbuf[p, :self.W - 1] = window0[r]
+        self.own = sorted(p for p in req_page if 0 <= p < n_pages)  # the pages this run's requests use
+        self.err = 0
+
+    def step(self, req_page, x, accepted, parity):
+        g = gdn()
+        errs, self.hdr, self.cbuf = self.ora.book_batch(self.W, self.n_spec, self.hdr, self.cbuf, req_page, x,
+                                                        accepted, parity)
+        bits = {0: 0, -1: g.GDN_DEVERR_PAGE, self.ora.BOOK_ACCEPTED: g.GDN_DEVERR_ACCEPTED,
+                self.ora.BOOK_PARITY: g.GDN_DEVERR_PARITY}
+        for e in errs:
+            self.err |= bits[e]
+        return errs
+
+    def check(self, pages, conv, err):
+        own = self.own
+        got_hdr = pages.header()[own, :4].cpu().numpy().view(np.uint32)
+        np.testing.assert_array_equal(got_hdr, self.hdr[own])
+        np.testing.assert_array_equal(host(conv.buf[own]), self.cbuf[own])
+        assert int(err.item()) == self.err
+
+
+class VerifyRun:
+    """A request batch stepping through speculative verify on the GPU."""
+
+    def __init__(self, wl, inp, layout, state_dtype, pages_of=None, n_pages=None, pages=None, conv=None):
+        """pages / conv: pools shared with other runs (other layers); by
+        default the run allocates its own."""
+        g = gdn()
+        self.g, self.wl, self.inp = g, wl, inp
+        self.dims = dims_of(wl, state_dtype=state_dtype, n_spec=wl.n_cand - 1)
+        R = wl.n_req
+        self.req_page = list(range(R)) if pages_of is None else list(pages_of)
+        n_pages = n_pages or (max(self.req_page) + 1)
+        self.pages = pages if pages is not None else g.SpecPages.alloc(self.dims, layout, n_pages, DEV)
+        self.conv = conv if conv is not None else g.ConvPool.alloc(self.dims, n_pages, 3 + self.dims.n_spec, DEV)
+        st = self.pages.states()
+        for r, p in enumerate(self.req_page):
+            if p < 0:
+                continue
+            st[p, 0] = dev(inp["S0"][r], self.dims.state_torch)
+            self.conv.buf[p, :3] = dev(inp["window0"][r], self.dims.act_torch)
+        self.params = params_of(inp, wl)
+        self.rp = torch.tensor(self.req_page, dtype=torch.int32, device=DEV)
+        self.err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.step_no = 0
+        # the oracle's page bookkeeping, stepped beside the GPU and compared after every step
+        self.book = BookModel(self.dims, n_pages, 3 + self.dims.n_spec, self.req_page, inp["window0"])
+
+    def step(self, s, accepted_prev, n_cand=None, parity=None, cache=None, cache_entry=None, cache_row=None,
+             refused=()):
+        """Step s with the previous step's acceptance counts.  With `cache`
+        (a PrefixCache) the step also writes cache_entry[r] <- the prefix that
+        ends at replayed row cache_row[r].  `refused`: requests the device is
+        expected to refuse for their cache arguments (their pages untouched,
+        GDN_DEVERR_CACHE)."""
+        wl, inp = self.wl, self.inp
+        R, K = wl.n_req, wl.n_cand if n_cand is None else n_cand
+        C = wl.c_conv
+        acc = torch.tensor(np.asarray(accepted_prev, np.int32), device=DEV)
+        par = (self.step_no + 1) & 1 if parity is None else parity
+        pt = torch.full((R,), par, dtype=torch.uint8, device=DEV)
+        if K > 0:
+            x = dev(inp["x"][s][:, :K].reshape(R * K, C), self.dims.act_torch)
+            a = dev(inp["a"][s][:, :K].reshape(R * K, wl.h_v), self.dims.act_torch)
+            b = dev(inp["b"][s][:, :K].reshape(R * K, wl.h_v), self.dims.act_torch)
+            o = torch.full((R * K, wl.h_v, wl.d_v), float("nan"), device=DEV)
+        else:
+            x = a = b = o = None
+        kw = {}
+        if cache is not None:
+            kw = dict(cache=cache, cache_entry=torch.tensor(np.asarray(cache_entry, np.int32), device=DEV),
+                      cache_row=torch.tensor(np.asarray(cache_row, np.int32), device=DEV))
+        self.g.gdn_spec_verify(self.dims, self.params, self.pages, x, a, b, R, K, self.rp, acc, pt, self.conv,
+                               o=o, err=self.err, **kw)
+        if parity is None:
+            self.step_no += 1
+        torch.cuda.synchronize()
+        stepped = [(-1 if r in refused else p) for r, p in enumerate(self.req_page)]
+        self.book.step(stepped, inp["x"][s][:, :K] if K > 0 else None, accepted_prev, [par] * R)
+        if refused:
+            self.book.err |= self.g.GDN_DEVERR_CACHE
+        self.book.check(self.pages, self.conv, self.err)
+        return None if o is None else o.view(R, K, wl.h_v, wl.d_v)
+
+    def clear_err(self):
+        self.err.zero_()
+        self.book.err = 0
+
+    def run(self):
+        wl, inp = self.wl, self.inp
+        outs = []
+        for s in range(wl.n_steps):
+            prev = inp["accepted"][s - 1] if s > 0 else np.zeros(wl.n_req, np.int32)
+            outs.append(self.step(s, prev))
+        self.step(0, inp["accepted"][wl.n_steps - 1], n_cand=0)  # commit the last acceptance
+        return torch.stack(outs)  # [steps][R][K][h_v][d_v]
+
+    def committed_state(self):
+        return self.pages.states()[self.req_page, 0]
+
+    def committed_window(self):
+        return self.conv.buf[self.req_page, :3]

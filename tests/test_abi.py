@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_header_compiles_as_plain_c(tmp_path):
     src = tmp_path / "h.c"
-    src.write_text('#include "gdn.h"\nint main(void) { return GDN_ABI_VERSION == 1 ? 0 : 1; }\n')
+    src.write_text('#include "gdn.h"\nint main(void) { return GDN_ABI_VERSION == 2 ? 0 : 1; }\n')
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.dirname(HEADER),
                     str(src), "-o", str(tmp_path / "h")], check=True)
     subprocess.run([str(tmp_path / "h")], check=True)
@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(so):
     assert set(names) == {"gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout",
                           "gdn_chunked_workspace_bytes", "gdn_conv_update", "gdn_recurrent_seq",
                           "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill", "gdn_spec_verify",
-                          "gdn_mixed_step"}
+                          "gdn_spec_verify_cached", "gdn_prefix_restore", "gdn_mixed_step"}
     for n in names:
         assert hasattr(so, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "linear_attention_ssm_gdn_amd",
@@ -63,7 +63,7 @@ def test_struct_layouts_match_c(L, tmp_path):
     structs = {"gdn_dims": L.GdnDims, "gdn_params": L.GdnParams, "gdn_batch": L.GdnBatch,
                "gdn_conv_pool": L.GdnConvPool, "gdn_state_pool": L.GdnStatePool,
                "gdn_spec_layout": L.GdnSpecLayout, "gdn_seq_part": L.GdnSeqPart,
-               "gdn_verify_part": L.GdnVerifyPart}
+               "gdn_verify_part": L.GdnVerifyPart, "gdn_prefix_cache": L.GdnPrefixCache}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gdn.h"', 'int main(void) {']
     for cname, py in structs.items():
         lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
@@ -84,7 +84,7 @@ def test_struct_layouts_match_c(L, tmp_path):
 
 
 def test_version_and_status_strings(so, L):
-    assert so.gdn_abi_version() == L.ABI_VERSION == 1
+    assert so.gdn_abi_version() == L.ABI_VERSION == 2
     for code, text in ((0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"kernel launch failed"), (99, b"unknown status")):
         assert so.gdn_status_str(code) == text

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import gdn_workloads as wk
-from gpu_util import DEV, dev, dims_of, gdn, make_batch, params_of
+from gpu_util import DEV, dev, dims_of, gdn, host, make_batch, max_slice_rel_o, params_of
 
 pytestmark = pytest.mark.gpu
 
@@ -274,11 +274,15 @@ def test_mixed_step_small_head_dims(d_k, d_v):
             assert torch.equal(got, ref)
 
 
-def test_mixed_step_at_the_benchmark_shape():
+def test_mixed_step_at_the_benchmark_shape(ora):
     """The benchmark's mix: the full short-prefill batch (8 sequences, 2,159
     rows) with 32 one-page verify requests of 8 candidates, H_k = 16,
     H_v = 32, d = 128, in one launch, equals the two separate launches bit
-    for bit: outputs, states, pages and the shared conv pool."""
+    for bit: outputs, states, pages and the shared conv pool.  Two such
+    steps (the sequences continue with the same rows, the verify requests
+    replay their first step's accepted rows) match the oracle: its layer
+    twice over the batch, and its verify semantics for the requests
+    (1e-4)."""
     g = gdn()
     ws = wk.SHORT_PREFILL
     wv = wk.SPEC_VERIFY
@@ -313,6 +317,7 @@ def test_mixed_step_at_the_benchmark_shape():
         return conv, state, pages, o_s, o_v, err
 
     fused, sep = world(), world()
+    outs = []
     for step in (0, 1):
         vx, va, vb, acc, par = vstep(step)
         conv, state, pages, o_s, o_v, err = fused
@@ -330,3 +335,25 @@ def test_mixed_step_at_the_benchmark_shape():
         assert not torch.isnan(fused[3]).any() and not torch.isnan(fused[4]).any(), step
         assert int(fused[5].item()) == 0, step
         assert int(fused[0].sync.abs().sum()) == 0, step
+        outs.append((host(fused[3]), host(fused[4]).reshape(R, K, ws.h_v, ws.d_v)))
+    # the oracle: the layer twice over the batch, and two verify steps
+    from gpu_util import max_slice_rel_S, oracle_seq
+    dm = ora.dims_of(ws)
+    cu = si["cu_seqlens"]
+    o1, win1, S1 = oracle_seq(ora, ws, si)
+    o2, win2, S2 = ora.layer(dm, si["conv_w"], si["a_log"], si["dt_bias"], si["x"], si["a"], si["b"], cu, win1, S1)
+    for got, ref in ((outs[0][0], o1), (outs[1][0], o2)):
+        assert max_slice_rel_o(got, ref, cu) <= 1e-4
+    conv, state = fused[0], fused[1]
+    assert max_slice_rel_S(host(state.buf), S2) <= 1e-4
+    np.testing.assert_array_equal(host(conv.buf[:NS, :3]), win2)
+    # one layer: both parts run with the sequence workload's conv weights and gates
+    vo, _, _ = ora.verify(dm, si["conv_w"], si["a_log"], si["dt_bias"], vi["x"][:2], vi["a"][:2], vi["b"][:2],
+                          vi["accepted"][:2], vi["window0"], vi["S0"])
+    worst = 0.0
+    for step in (0, 1):
+        for r in range(R):
+            for h in range(ws.h_v):
+                ref = vo[step, r, :, h]
+                worst = max(worst, np.abs(outs[step][1][r, :, h] - ref).max() / np.abs(ref).max())
+    assert worst <= 1e-4, worst

@@ -1,77 +1,18 @@
 """GPU tests of speculative verify (gdn_spec_verify): the one-page record
 design against the per-candidate-slot design (bit-exact, fp32 state first,
 then bf16), both against the oracle's verify semantics, the flag-word and
-record bookkeeping, and the device error paths."""
+record bookkeeping against the oracle's bookkeeping model after every step,
+and the device error paths."""
 import numpy as np
 import pytest
 import torch
 
 import gdn_workloads as wk
-from gpu_util import DEV, dev, dims_of, gdn, host, max_slice_rel_o, params_of, run_seq
+from gpu_util import DEV, VerifyRun, dev, gdn, host, run_seq
 
 pytestmark = pytest.mark.gpu
 
 ONEPAGE, SLOTS = 0, 1
-
-
-class VerifyRun:
-    """A request batch stepping through speculative verify on the GPU."""
-
-    def __init__(self, wl, inp, layout, state_dtype, pages_of=None, n_pages=None):
-        g = gdn()
-        self.g, self.wl, self.inp = g, wl, inp
-        self.dims = dims_of(wl, state_dtype=state_dtype, n_spec=wl.n_cand - 1)
-        R = wl.n_req
-        self.req_page = list(range(R)) if pages_of is None else list(pages_of)
-        n_pages = n_pages or (max(self.req_page) + 1)
-        self.pages = g.SpecPages.alloc(self.dims, layout, n_pages, DEV)
-        self.conv = g.ConvPool.alloc(self.dims, n_pages, 3 + self.dims.n_spec, DEV)
-        st = self.pages.states()
-        for r, p in enumerate(self.req_page):
-            if p < 0:
-                continue
-            st[p, 0] = dev(inp["S0"][r], self.dims.state_torch)
-            self.conv.buf[p, :3] = dev(inp["window0"][r], self.dims.act_torch)
-        self.params = params_of(inp, wl)
-        self.rp = torch.tensor(self.req_page, dtype=torch.int32, device=DEV)
-        self.err = torch.zeros(1, dtype=torch.int32, device=DEV)
-        self.step_no = 0
-
-    def step(self, s, accepted_prev, n_cand=None, parity=None):
-        wl, inp = self.wl, self.inp
-        R, K = wl.n_req, wl.n_cand if n_cand is None else n_cand
-        C = wl.c_conv
-        acc = torch.tensor(np.asarray(accepted_prev, np.int32), device=DEV)
-        par = (self.step_no + 1) & 1 if parity is None else parity
-        pt = torch.full((R,), par, dtype=torch.uint8, device=DEV)
-        if K > 0:
-            x = dev(inp["x"][s][:, :K].reshape(R * K, C), self.dims.act_torch)
-            a = dev(inp["a"][s][:, :K].reshape(R * K, wl.h_v), self.dims.act_torch)
-            b = dev(inp["b"][s][:, :K].reshape(R * K, wl.h_v), self.dims.act_torch)
-            o = torch.full((R * K, wl.h_v, wl.d_v), float("nan"), device=DEV)
-        else:
-            x = a = b = o = None
-        self.g.gdn_spec_verify(self.dims, self.params, self.pages, x, a, b, R, K, self.rp, acc, pt, self.conv,
-                               o=o, err=self.err)
-        if parity is None:
-            self.step_no += 1
-        torch.cuda.synchronize()
-        return None if o is None else o.view(R, K, wl.h_v, wl.d_v)
-
-    def run(self):
-        wl, inp = self.wl, self.inp
-        outs = []
-        for s in range(wl.n_steps):
-            prev = inp["accepted"][s - 1] if s > 0 else np.zeros(wl.n_req, np.int32)
-            outs.append(self.step(s, prev))
-        self.step(0, inp["accepted"][wl.n_steps - 1], n_cand=0)  # commit the last acceptance
-        return torch.stack(outs)  # [steps][R][K][h_v][d_v]
-
-    def committed_state(self):
-        return self.pages.states()[self.req_page, 0]
-
-    def committed_window(self):
-        return self.conv.buf[self.req_page, :3]
 
 
 def _inputs(wl, state_dtype):
@@ -124,29 +65,34 @@ def test_verify_oracle_parity(ora, state_dtype, tol):
     np.testing.assert_array_equal(host(run.committed_window()), win_ref)
 
 
-def test_header_bookkeeping():
+def test_header_bookkeeping(ora):
+    """After every step the headers (flag word, n_rows, acceptance echo) and
+    every page's whole conv buffer equal the oracle's bookkeeping model bit
+    for bit (VerifyRun.step checks them), and the record slot the step wrote
+    holds its candidates: a and b exactly, the post-conv q|k|v within fp32
+    rounding of the oracle's conv + SiLU from the step's window."""
     wl = _small()
     inp = _inputs(wl, wk.F32)
     run = VerifyRun(wl, inp, ONEPAGE, wk.F32)
-    L = 0
+    lay = run.pages.lay
+    row = lay["record_row_bytes"] // 4
+    C, K = wl.c_conv, wl.n_cand
     for s in range(wl.n_steps):
         prev = inp["accepted"][s - 1] if s > 0 else np.zeros(wl.n_req, np.int32)
+        cbuf_before, hdr_before = run.book.cbuf.copy(), run.book.hdr.copy()
         run.step(s, prev)
-        hdr = run.pages.header().cpu().numpy()
-        L = 1 - L
-        par = (s + 1) & 1
-        for r in range(wl.n_req):
-            assert hdr[r, 0] == (L | (par << 1))          # live slot, parity, done counter back at 0
-            assert hdr[r, 1 + L] == wl.n_cand            # rows held by the new live slot
-            assert hdr[r, 3] == (prev[r] if s > 0 else 0)  # acceptance echo
-    # record rows: post-conv values of the last step's candidates (fp32), then a and b
-    lay = run.pages.lay
-    rec = run.pages.buf[0, lay["record_off"]:].view(torch.float32)
-    row = lay["record_row_bytes"] // 4
-    slot = L * wl.n_cand
-    a_last = torch.tensor(inp["a"][wl.n_steps - 1][0], device=DEV)
-    got_a = rec[slot * row: (slot + wl.n_cand) * row].view(wl.n_cand, row)[:, wl.c_conv:wl.c_conv + wl.h_v]
-    assert torch.equal(got_a, a_last)
+        for r, p in enumerate(run.req_page):
+            held = int(hdr_before[p, 1 + (int(hdr_before[p, 0]) & 1)])
+            a_rep = int(prev[r]) if held > 0 else 0
+            y_ref, _ = ora.conv_seq(inp["x"][s][r], inp["conv_w"], cbuf_before[p, a_rep:a_rep + 3])
+            slot = int(run.book.hdr[p, 0]) & 1
+            assert int(run.book.hdr[p, 1 + slot]) == K
+            rec = run.pages.buf[p, lay["record_off"]:].view(torch.float32)
+            got = host(rec[slot * K * row:(slot + 1) * K * row].view(K, row))
+            np.testing.assert_array_equal(got[:, C:C + wl.h_v], inp["a"][s][r])
+            np.testing.assert_array_equal(got[:, C + wl.h_v:C + 2 * wl.h_v], inp["b"][s][r])
+            rel_rows = np.abs(got[:, :C] - y_ref).max(axis=1) / np.abs(y_ref).max(axis=1)
+            assert rel_rows.max() <= 1e-5, (s, r, rel_rows.max())
 
 
 def test_all_accepted_chain_equals_sequence_kernel():
@@ -196,11 +142,12 @@ def test_relaunch_and_bad_acceptance_are_rejected():
     run = VerifyRun(wl, inp, ONEPAGE, wk.F32)
     run.step(0, np.zeros(3, np.int32))
     snap = run.pages.buf.clone(), run.conv.buf.clone()
-    # the same step again (same parity) is refused and changes nothing
+    # the same step again (same parity) is refused and changes nothing (the
+    # bookkeeping model refuses it too: VerifyRun.step compares the two)
     run.step(1, np.zeros(3, np.int32), parity=1)
     assert int(run.err.item()) & g.GDN_DEVERR_PARITY
     assert torch.equal(run.pages.buf, snap[0]) and torch.equal(run.conv.buf, snap[1])
-    run.err.zero_()
+    run.clear_err()
     # an acceptance beyond the record's rows is refused
     run.step(1, np.array([0, wl.n_cand, 1], np.int32))
     assert int(run.err.item()) & g.GDN_DEVERR_ACCEPTED
@@ -220,7 +167,7 @@ def test_padding_requests_are_skipped():
 
 
 @pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
-def test_prefix_snapshot_after_commit_continues_bit_identically(state_dtype):
+def test_prefix_snapshot_after_commit_continues_bit_identically(ora, state_dtype):
     """One page per request with a prefix cache ("r9700-stack v0.2.4" leaves
     prefix caching to the stock pages): after a commit-only step the
     checkpoint and conv rows 0..2 hold the committed prefix and the record is
@@ -237,9 +184,21 @@ def test_prefix_snapshot_after_commit_continues_bit_identically(state_dtype):
     cached_W = A.committed_window().clone()
     hdr = A.pages.header()[A.req_page]
     assert int(hdr[:, 1 + (int(hdr[0, 0]) & 1)].abs().sum()) == 0   # the live record holds no rows
+    # the cached prefix is the oracle's committed state and window after four steps
+    dm = ora.dims_of(wl)
+    _, win_ref, S_ref = ora.verify(dm, inp["conv_w"], inp["a_log"], inp["dt_bias"], inp["x"][:4], inp["a"][:4],
+                                   inp["b"][:4], inp["accepted"][:4], inp["window0"], inp["S0"],
+                                   state_bf16=(state_dtype == wk.BF16))
+    np.testing.assert_array_equal(host(cached_W), win_ref)
+    Sc = host(cached_S)
+    tol = 1e-4 if state_dtype == wk.F32 else 3e-3
+    for r in range(wl.n_req):
+        for h in range(wl.h_v):
+            assert np.abs(Sc[r, h] - S_ref[r, h]).max() <= tol * np.abs(S_ref[r, h]).max(), (r, h)
     B = VerifyRun(wl, inp, ONEPAGE, state_dtype)
     B.pages.states()[B.req_page, 0] = cached_S
     B.conv.buf[B.req_page, :3] = cached_W
+    B.book.cbuf[B.req_page, :3] = host(cached_W)
     for s in range(4, 8):
         prev = inp["accepted"][s - 1] if s > 4 else zero
         oa, ob = A.step(s, prev), B.step(s, prev)
@@ -413,3 +372,49 @@ def test_two_column_blocks_per_head(ora, state_dtype):
     np.testing.assert_array_equal(host(one.committed_window()), win_ref)
     hdr = one.pages.header()
     assert int(one.err.item()) == 0 and int((hdr[:, 0] >> 8).abs().sum()) == 0  # done counters back to zero
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
+def test_several_layers_share_one_pool_without_cross_talk(ora, state_dtype):
+    """Three layers, each with its own conv weights, gates, inputs and
+    initial states, keep their pages in one shared page pool and one shared
+    conv pool and are stepped in turn on one stream (layer 0 step s, layer 1
+    step s, layer 2 step s, ...): each layer's outputs, committed states and
+    windows equal a run of that layer alone bit for bit and the oracle at
+    the gate (the pages' own verify tests run several layers,
+    "r9700-stack v0.2.4", section "What it does")."""
+    g = gdn()
+    n_layers, R = 3, 4
+    wls = [_small(n_req=R, n_steps=4, seed=91 + i) for i in range(n_layers)]
+    inps = [_inputs(w, state_dtype) for w in wls]
+    dims = VerifyRun(wls[0], inps[0], ONEPAGE, state_dtype).dims
+    pages = g.SpecPages.alloc(dims, ONEPAGE, n_layers * R, DEV)
+    conv = g.ConvPool.alloc(dims, n_layers * R, 3 + dims.n_spec, DEV)
+    # pages interleaved across layers: layer i, request r on page r * n_layers + i
+    runs = [VerifyRun(w, x, ONEPAGE, state_dtype, pages_of=[r * n_layers + i for r in range(R)],
+                      n_pages=n_layers * R, pages=pages, conv=conv) for i, (w, x) in enumerate(zip(wls, inps))]
+    outs = [[] for _ in runs]
+    zero = np.zeros(R, np.int32)
+    for s in range(4):
+        for i, run in enumerate(runs):
+            outs[i].append(run.step(s, inps[i]["accepted"][s - 1] if s else zero))
+    for i, run in enumerate(runs):
+        run.step(0, inps[i]["accepted"][3], n_cand=0)
+    tol = 1e-4 if state_dtype == wk.F32 else 3e-3
+    for i, run in enumerate(runs):
+        alone = VerifyRun(wls[i], inps[i], ONEPAGE, state_dtype)
+        o_alone = alone.run()
+        assert torch.equal(torch.stack(outs[i]), o_alone), i
+        assert torch.equal(run.committed_state(), alone.committed_state()), i
+        assert torch.equal(run.committed_window(), alone.committed_window()), i
+        dm = ora.dims_of(wls[i])
+        o_ref, win_ref, S_ref = ora.verify(dm, inps[i]["conv_w"], inps[i]["a_log"], inps[i]["dt_bias"], inps[i]["x"],
+                                           inps[i]["a"], inps[i]["b"], inps[i]["accepted"], inps[i]["window0"],
+                                           inps[i]["S0"], state_bf16=(state_dtype == wk.BF16))
+        o = host(o_alone)
+        for r in range(R):
+            for h in range(wls[i].h_v):
+                ref = o_ref[:, r, :, h]
+                assert np.abs(o[:, r, :, h] - ref).max() <= tol * np.abs(ref).max(), (i, r, h)
+        np.testing.assert_array_equal(host(run.committed_window()), win_ref)
+    assert int(conv.sync.abs().sum()) == 0
