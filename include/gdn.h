@@ -203,6 +203,26 @@ int32_t gdn_recurrent_seq(const gdn_dims* dims, const gdn_params* params,
                           const gdn_batch* batch, gdn_conv_pool conv, gdn_state_pool state,
                           float* o, int32_t* err, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * gdn_recurrent_seq with its sync words kept in the library's own device
+ * array of GDN_NOALLOC_SYNC_WORDS 32-bit words (256 KiB, held by every GPU
+ * the library runs on until the process ends) instead of conv.sync, which
+ * may be NULL here.  The call needs conv.n_pages * h_k + 1 words and
+ * returns GDN_ERR_ARG beyond that maximum (at h_k = 16: up to 4,095 pages);
+ * it zeroes the words it uses with a fill kernel on `stream` before the
+ * layer kernel, so no word of an earlier call is read.  Nothing is
+ * allocated, freed or copied.  Every call on one GPU shares the array:
+ * calls that may overlap on one GPU (different streams, no ordering) race
+ * on it and must be ordered.  Results are those of gdn_recurrent_seq, bit
+ * for bit; every other argument, result and error is the same. */
+#define GDN_NOALLOC_SYNC_WORDS 65536
+int32_t gdn_recurrent_seq_noalloc(const gdn_dims* dims, const gdn_params* params,
+                                  const void* x, int64_t x_stride,
+                                  const void* a, const void* b, int64_t ab_stride,
+                                  const gdn_batch* batch, gdn_conv_pool conv, gdn_state_pool state,
+                                  float* o, int32_t* err, void* stream);
+
 /* ------------------------------------------- (c) chunked WY/UT prefill */
 
 /* The same result as gdn_recurrent_seq computed in the chunked WY/UT form

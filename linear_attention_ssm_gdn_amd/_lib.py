@@ -20,9 +20,10 @@ GDN_SPEC_ONEPAGE, GDN_SPEC_SLOTS = 0, 1
 GDN_DEVERR_PAGE, GDN_DEVERR_BATCH, GDN_DEVERR_ACCEPTED, GDN_DEVERR_PARITY, GDN_DEVERR_CACHE = 1, 2, 4, 8, 16
 GDN_PATH_TOKEN, GDN_PATH_CHUNKED = 0, 1
 GDN_PREFILL_MAX_DEFAULT = -1
+GDN_NOALLOC_SYNC_WORDS = 65536
 
 SYMBOLS = ("gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout", "gdn_chunked_workspace_bytes",
-           "gdn_conv_update", "gdn_recurrent_seq", "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill",
+           "gdn_conv_update", "gdn_recurrent_seq", "gdn_recurrent_seq_noalloc", "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill",
            "gdn_spec_verify", "gdn_spec_verify_cached", "gdn_prefix_restore", "gdn_mixed_step")
 
 _vp = ctypes.c_void_p
@@ -108,6 +109,8 @@ def load() -> ctypes.CDLL:
     L.gdn_recurrent_seq.restype = _i32
     L.gdn_recurrent_seq.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _vp, _i64, _vp, _vp,
                                     _i64, ctypes.POINTER(GdnBatch), GdnConvPool, GdnStatePool, _vp, _vp, _vp]
+    L.gdn_recurrent_seq_noalloc.restype = _i32
+    L.gdn_recurrent_seq_noalloc.argtypes = L.gdn_recurrent_seq.argtypes
     L.gdn_chunked_prefill.restype = _i32
     L.gdn_chunked_prefill.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), _vp, _i64, _vp, _vp,
                                       _i64, ctypes.POINTER(GdnBatch), GdnConvPool, GdnStatePool, _vp, _i32,

@@ -16,7 +16,8 @@ LIB = os.path.join(HERE, "libgdn.so")
 OBJ = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gdn_api.cpp", "gdn_seq.hip", "gdn_conv.hip", "gdn_verify.hip", "gdn_chunked.hip", "gdn_mixed.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_seq.hip", "gdn_conv.hip", "gdn_verify.hip", "gdn_chunked.hip", "gdn_mixed.hip",
+           "gdn_noalloc.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden", "-ffp-contract=off", "-Wall", "-Wno-unused-function",

@@ -70,13 +70,13 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int32_t check_sequence_call(const gdn_dims* dims, const gdn_params* params, const void* x,
                             int64_t x_stride, const void* a, const void* b, int64_t ab_stride,
                             const gdn_batch* batch, const gdn_conv_pool& conv,
-                            const gdn_state_pool& state, const float* o) {
+                            const gdn_state_pool& state, const float* o, bool need_sync = true) {
     int32_t st;
     if ((st = check_dims(dims)) != GDN_OK) return st;
     if ((st = check_params(params)) != GDN_OK) return st;
     if ((st = check_batch(batch)) != GDN_OK) return st;
     if (batch->n_seqs == 0) return GDN_OK;
-    if ((st = check_conv_pool(dims, conv, dims->conv_w - 1, true)) != GDN_OK) return st;
+    if ((st = check_conv_pool(dims, conv, dims->conv_w - 1, need_sync)) != GDN_OK) return st;
     if ((st = check_state_pool(dims, state)) != GDN_OK) return st;
     if (batch->n_rows > 0 && (!x || !a || !b || !o)) return GDN_ERR_ARG;
     if (x_stride < c_conv(dims) || ab_stride < dims->h_v) return GDN_ERR_ARG;
@@ -135,6 +135,21 @@ gdn::VerifyArgs verify_args(const gdn_dims* dims, const gdn_params* params, cons
 }
 
 }  // namespace
+
+namespace gdn {
+// Validation and argument block of a token-by-token call whose sync words
+// the caller does not supply (conv.sync may be NULL): used by the entry
+// point that keeps them in the library's own device array.
+int32_t seq_call_args_nosync(const gdn_dims* dims, const gdn_params* params, const void* x, int64_t x_stride,
+                             const void* a, const void* b, int64_t ab_stride, const gdn_batch* batch,
+                             const gdn_conv_pool& conv, const gdn_state_pool& state, float* o, int32_t* err,
+                             SeqArgs* out) {
+    const int32_t st = check_sequence_call(dims, params, x, x_stride, a, b, ab_stride, batch, conv, state, o, false);
+    if (st != GDN_OK || batch->n_seqs == 0) return st;
+    *out = seq_args(dims, params, x, x_stride, a, b, ab_stride, batch, conv, state, o, err);
+    return GDN_OK;
+}
+}  // namespace gdn
 
 GDN_EXPORT int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
 

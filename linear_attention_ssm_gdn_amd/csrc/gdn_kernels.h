@@ -93,6 +93,13 @@ hipError_t launch_chunked(const ChunkArgs& a, int d_k, int act_dtype, int state_
 hipError_t launch_mixed(const SeqArgs& s, const VerifyArgs& v, int d_k, int act_dtype, int state_dtype, int layout,
                         hipStream_t st);
 
+// Argument checks and block of a token-by-token call with no caller sync
+// words (gdn_api.cpp); GDN_OK with out->n_seqs == 0 for an empty batch.
+int32_t seq_call_args_nosync(const struct gdn_dims* dims, const struct gdn_params* params, const void* x,
+                             int64_t x_stride, const void* a, const void* b, int64_t ab_stride,
+                             const struct gdn_batch* batch, const struct gdn_conv_pool& conv,
+                             const struct gdn_state_pool& state, float* o, int32_t* err, SeqArgs* out);
+
 // Which (d_k, d_v) the kernels are compiled for.
 bool seq_supported(int d_k, int d_v);
 bool chunked_supported(int d_k, int d_v, int chunk);

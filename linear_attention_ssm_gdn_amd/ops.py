@@ -178,6 +178,24 @@ def gdn_recurrent_seq(dims: Dims, params: Params, x: torch.Tensor, a: torch.Tens
     return o
 
 
+def gdn_recurrent_seq_noalloc(dims: Dims, params: Params, x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                              batch: Batch, conv: ConvPool, state: StatePool, o: torch.Tensor,
+                              err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gdn_recurrent_seq with its sync words in the library's own device
+    array: conv.sync is not passed, and o must be given (nothing is
+    allocated on the way)."""
+    if a.stride() != b.stride():
+        raise ValueError("a and b must share their row stride")
+    d, p, bt = dims.c(), params.c(), batch.c()
+    n, rows, C = conv.buf.shape
+    cp = L.GdnConvPool(conv.buf.data_ptr(), conv.buf.stride(0), rows, n, None)
+    st = L.load().gdn_recurrent_seq_noalloc(ctypes.byref(d), ctypes.byref(p), x.data_ptr(), _rows(x, "x"),
+                                            a.data_ptr(), b.data_ptr(), _rows(a, "a"), ctypes.byref(bt), cp,
+                                            state.c(), o.data_ptr(), _ptr(err), _stream(x))
+    _check("gdn_recurrent_seq_noalloc", st)
+    return o
+
+
 def gdn_chunked_prefill(dims: Dims, params: Params, x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
                         batch: Batch, conv: ConvPool, state: StatePool, chunk: int = 64,
                         o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,

@@ -49,7 +49,8 @@ def test_every_declared_symbol_is_exported(so):
     assert set(names) == {"gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout",
                           "gdn_chunked_workspace_bytes", "gdn_conv_update", "gdn_recurrent_seq",
                           "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill", "gdn_spec_verify",
-                          "gdn_spec_verify_cached", "gdn_prefix_restore", "gdn_mixed_step"}
+                          "gdn_spec_verify_cached", "gdn_prefix_restore", "gdn_mixed_step",
+                          "gdn_recurrent_seq_noalloc"}
     for n in names:
         assert hasattr(so, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "linear_attention_ssm_gdn_amd",
@@ -161,6 +162,30 @@ def test_recurrent_seq_validation(so, L):
         assert _call_seq(so, _seq_args(L, d, **over)) == want, over
     # an empty batch is a no-op that returns OK without launching
     assert _call_seq(so, _seq_args(L, d, batch=L.GdnBatch(None, None, None, 0, 0, 0))) == 0
+
+
+def test_recurrent_seq_noalloc_validation(so, L):
+    """The entry point that keeps its sync words in the library's own array
+    validates like gdn_recurrent_seq, needs no conv.sync, and refuses a conv
+    pool whose sync words (n_pages * h_k + 1) exceed its maximum before
+    touching the device."""
+    d = _dims(L)
+    C = 2 * 16 * 128 + 32 * 128
+
+    def call(**over):
+        a = _seq_args(L, d, **over)
+        return so.gdn_recurrent_seq_noalloc(ctypes.byref(a["dims"]), ctypes.byref(a["params"]) if a["params"] else None,
+                                            a["x"], a["x_stride"], a["a"], a["b"], a["ab_stride"],
+                                            ctypes.byref(a["batch"]) if a["batch"] else None, a["conv"], a["state"],
+                                            a["o"], None, None)
+    assert call(x=None) == 1
+    assert call(params=None) == 1
+    assert call(conv=L.GdnConvPool(FAKE, 3 * C, 2, 4, None)) == 1
+    max_pages = (L.GDN_NOALLOC_SYNC_WORDS - 1) // 16
+    assert call(conv=L.GdnConvPool(FAKE, 3 * C, 3, max_pages + 1, None)) == 1
+    assert call(conv=L.GdnConvPool(FAKE, 3 * C, 3, 1 << 20, None)) == 1
+    assert call(batch=L.GdnBatch(None, None, None, 0, 0, 0)) == 0
+    assert "#define GDN_NOALLOC_SYNC_WORDS %d" % L.GDN_NOALLOC_SYNC_WORDS in open(HEADER).read()
 
 
 def test_chunked_validation(so, L):
