@@ -8,9 +8,11 @@ workloads (short ragged prefill, long chunked prefill, speculative verify)
 are reported beside it under "other_workloads".
 
 Inputs are seeded synthetic data (gdn_workloads) already resident in HBM when
-the timed region starts.  State/input pools rotate every step so that the
-working set (>= 512 MiB) cannot sit in the 256 MB last-level cache.  Kernel
-time is taken with HIP events on the stream the kernels are launched on.
+the timed region starts.  Every workload rotates through enough copies of
+its state, page and input buffers that the bytes it touches between two
+uses of one copy are at least 512 MiB, twice the 256 MB last-level cache,
+so no launch reads what an earlier launch left in that cache.  Kernel time
+is taken with HIP events on the stream the kernels are launched on.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,...] [--sweep-dispatch]
 """
@@ -34,7 +36,12 @@ METRIC = "GDN tokens/s/layer (prefill) + decode/verify µs/step at B=64; % HBM/M
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix cores
 FP32_VALU_PEAK_TFLOPS = 157.3    # fp32 vector (256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz)
-POOLS = 4
+# the build disables packed fp32 instructions, so one lane retires at most
+# one fp32 FMA per cycle: half the published figure
+FP32_VALU_REACHABLE_TFLOPS = 78.6
+ROTATION_BYTES = 512 << 20       # bytes touched between two uses of one buffer copy
+MIN_POOLS = 2
+POOLS = 4                        # the dispatch sweep's state copies (its inputs are shared)
 LAST_PERCENTILES = {}  # per-launch kernel time percentiles (us) of the last measure()
 
 
@@ -134,8 +141,19 @@ def _upload(torch, arr, dt):
     return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to("cuda").to(dt)
 
 
+def pools_for(set_bytes: int) -> int:
+    """Copies of a workload's buffers so that one rotation touches at least
+    ROTATION_BYTES."""
+    return max(MIN_POOLS, -(-ROTATION_BYTES // max(int(set_bytes), 1)))
+
+
+def _nbytes(*ts) -> int:
+    return int(sum(t.numel() * t.element_size() for t in ts))
+
+
 class SeqWorkload:
-    """Token-by-token (or chunked) layer over one ragged batch; POOLS copies."""
+    """Token-by-token (or chunked) layer over one ragged batch; enough copies
+    of inputs, windows, states and outputs to rotate through >= 512 MiB."""
 
     def __init__(self, g, torch, wl, chunk=0):
         self.g, self.torch, self.wl, self.chunk = g, torch, wl, chunk
@@ -156,7 +174,10 @@ class SeqWorkload:
         b = _upload(torch, inp["b"], d.act_torch)
         S0 = _upload(torch, inp["S0"], d.state_torch)
         W0 = _upload(torch, inp["window0"], d.act_torch)
-        for _ in range(POOLS):
+        o_bytes = wl.n_tokens * wl.h_v * wl.d_v * 4
+        self.set_bytes = _nbytes(x, a, b, S0, W0) + o_bytes
+        self.pools = pools_for(self.set_bytes)
+        for _ in range(self.pools):
             conv = g.ConvPool.alloc(d, n, wl.conv_w - 1, "cuda")
             conv.buf.copy_(W0)
             state = g.StatePool(S0.clone())
@@ -164,8 +185,11 @@ class SeqWorkload:
             self.sets.append((x.clone(), a.clone(), b.clone(), conv, state, o))
         self.i = 0
 
+    def rotation(self) -> dict:
+        return {"pools": self.pools, "bytes_per_pool": self.set_bytes, "rotation_bytes": self.pools * self.set_bytes}
+
     def launch(self):
-        x, a, b, conv, state, o = self.sets[self.i % POOLS]
+        x, a, b, conv, state, o = self.sets[self.i % self.pools]
         self.i += 1
         if self.chunk:
             self.g.gdn_chunked_prefill(self.dims, self.params, x, a, b, self.batch, conv, state, chunk=self.chunk,
@@ -175,7 +199,8 @@ class SeqWorkload:
 
 
 class VerifyWorkload:
-    """One-page speculative verify steps over n_req requests; POOLS page sets."""
+    """Speculative verify steps over n_req requests; enough page sets (pages,
+    conv buffers, outputs) to rotate through >= 512 MiB."""
 
     def __init__(self, g, torch, wl, state_dtype, layout=0):
         self.g, self.torch, self.wl = g, torch, wl
@@ -193,7 +218,11 @@ class VerifyWorkload:
         self.mean_replay = float(np.mean(inp["accepted"]) + 1.0)
         self.rp = torch.arange(R, dtype=torch.int32, device="cuda")
         self.sets = []
-        for _ in range(POOLS):
+        lay = g.gdn_spec_page_layout(d, layout)
+        act = 2 if wl.act_dtype == wk.BF16 else 4
+        self.set_bytes = R * lay["page_bytes"] + R * (3 + d.n_spec) * C * act + R * K * wl.h_v * wl.d_v * 4
+        self.pools = pools_for(self.set_bytes)
+        for _ in range(self.pools):
             pages = g.SpecPages.alloc(d, layout, R, "cuda")
             pages.states()[:, 0] = _upload(torch, inp["S0"], d.state_torch)
             conv = g.ConvPool.alloc(d, R, 3 + d.n_spec, "cuda")
@@ -203,8 +232,11 @@ class VerifyWorkload:
         self.i = 0
         self.par = [torch.full((R,), p, dtype=torch.uint8, device="cuda") for p in (0, 1)]
 
+    def rotation(self) -> dict:
+        return {"pools": self.pools, "bytes_per_pool": self.set_bytes, "rotation_bytes": self.pools * self.set_bytes}
+
     def launch(self):
-        st = self.sets[self.i % POOLS]
+        st = self.sets[self.i % self.pools]
         self.i += 1
         pages, conv, o, n = st
         s = n % self.wl.n_steps
@@ -229,9 +261,9 @@ class MixedWorkload:
 
     def launch(self):
         g, sw, vw = self.g, self.seq, self.ver
-        x, a, b, conv, state, o = sw.sets[sw.i % POOLS]
+        x, a, b, conv, state, o = sw.sets[sw.i % sw.pools]
         sw.i += 1
-        st = vw.sets[vw.i % POOLS]
+        st = vw.sets[vw.i % vw.pools]
         vw.i += 1
         pages, vconv, vo, n = st
         s = n % vw.wl.n_steps
@@ -291,6 +323,57 @@ def read_traffic(kernel: str, workload: str):
     return None
 
 
+# ---------------------------------------------------------- denominators
+def measured_copy_gbs(torch, nbytes=1 << 30, reps=10):
+    """Bandwidth of a plain device-to-device copy of nbytes (torch's copy
+    kernel), read + write bytes over HIP-event time: the second denominator
+    of every HBM fraction."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for _ in range(reps):
+        t.time(lambda: dst.copy_(src))
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes / (t.mean_ms() * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"value": round(gbs, 1), "unit": "GB/s", "kernel": "torch copy_ (device to device)",
+            "bytes_moved": 2 * nbytes}
+
+
+def measured_gemm_tflops(torch, n=8192, reps=10):
+    """Dense bf16 matrix-core throughput of a library GEMM (torch.matmul on
+    two contiguous n x n bf16 matrices, fp32 accumulation): the measured
+    second denominator of the chunked path's matrix-core fraction."""
+    a = torch.randn((n, n), device="cuda").to(torch.bfloat16).contiguous()
+    b = torch.randn((n, n), device="cuda").to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for _ in range(reps):
+        t.time(lambda: torch.matmul(a, b))
+    torch.cuda.synchronize()
+    tf = 2.0 * n ** 3 / (t.mean_ms() * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"value": round(tf, 1), "unit": "TFLOP/s", "kernel": f"torch.matmul bf16 {n}x{n}x{n}"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 # ---------------------------------------------------------------- cpu leg
 def cpu_baseline(wl, budget_s=12.0):
     """The fp64 oracle on the decode workload, repeated for about budget_s."""
@@ -307,6 +390,7 @@ def cpu_baseline(wl, budget_s=12.0):
     dt = (time.perf_counter() - t0) / n
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"the full decode step ({len(wl.seqlens)} seqs x 1 token, all {wl.h_v} heads), "
                       f"repeated {n} times in {budget_s:.0f} s"}
 
@@ -464,6 +548,19 @@ def main():
         log(f"copy calibration: 5 x {src.numel() * 4} bytes read and written")
         del src, dst
     other = {}
+    log("denominators: device copy and bf16 GEMM")
+    copy = measured_copy_gbs(torch)
+    gemm = measured_gemm_tflops(torch)
+    result["measured_peaks"] = {"copy": copy, "bf16_gemm": gemm,
+                                "fp32_valu_reachable": {"value": FP32_VALU_REACHABLE_TFLOPS, "unit": "TFLOP/s",
+                                                        "derivation": "256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz, "
+                                                                      "packed fp32 off"}}
+    log(f"denominators: copy {copy['value']:.0f} GB/s, bf16 GEMM {gemm['value']:.0f} TFLOP/s")
+
+    def hbm_roofline(achieved_gbs, nbytes, traffic, kernel):
+        return {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                "algorithmic_bytes": nbytes, "frac_of_measured_copy": round(achieved_gbs / copy["value"], 4)}
 
     # ---- headline: decode
     wl = wk.DECODE
@@ -482,10 +579,8 @@ def main():
         "config": {"workload": "decode", "n_seqs": len(wl.seqlens), "tokens_per_seq": 1, "h_k": wl.h_k,
                    "h_v": wl.h_v, "d_k": wl.d_k, "d_v": wl.d_v, "conv_w": wl.conv_w, "act_dtype": wl.act_dtype,
                    "state_dtype": wl.state_dtype, "tokens_per_s_per_layer": round(len(wl.seqlens) / (k_ms * 1e-3)),
-                   "state_pools_rotated": POOLS, "us_per_step_percentiles": dict(LAST_PERCENTILES)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_gdn_seq_stream", "algorithmic_bytes": nbytes},
+                   "rotation": dec.rotation(), "us_per_step_percentiles": dict(LAST_PERCENTILES)},
+        "roofline": hbm_roofline(achieved, nbytes, traffic, "k_gdn_seq_stream"),
     })
     del dec
     torch.cuda.empty_cache()
@@ -504,9 +599,12 @@ def main():
                 "us_per_token_critical_path": round(k_ms * 1e3 / max(wl.seqlens), 4),
                 "us_per_call_percentiles": dict(LAST_PERCENTILES),
                 "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": read_traffic("k_gdn_seq", "short_prefill"),
+                             "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
+                             "peak_reachable": FP32_VALU_REACHABLE_TFLOPS,
+                             "frac_reachable": round(tf / FP32_VALU_REACHABLE_TFLOPS, 4),
+                             "traffic": read_traffic("k_gdn_seq", "short_prefill"),
                              "kernel": "k_gdn_seq", "algorithmic_flops": fl},
-                "config": {"seqlens": list(wl.seqlens)}}
+                "config": {"seqlens": list(wl.seqlens), "rotation": w.rotation()}}
             log(f"short_prefill: {k_ms * 1e3:.1f} us, {tf:.2f} TFLOP/s")
             # the same batch through the chunked kernel, the path gdn_prefill
             # selects for it (its longest sequence is above the token-by-token limit)
@@ -546,10 +644,12 @@ def main():
                     "us_per_call_percentiles": dict(LAST_PERCENTILES),
                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                 "frac_of_measured_gemm": round(tf / gemm["value"], 4),
                                  "traffic": read_traffic("k_gdn_chunk", "long_prefill"), "kernel": "k_gdn_chunk",
                                  "algorithmic_flops": fl,
                                  "hbm_frac": round(chunked_bytes(wl) / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-                    "config": {"n_seqs": len(wl.seqlens), "seqlen": wl.seqlens[0], "chunk": wl.chunk}}
+                    "config": {"n_seqs": len(wl.seqlens), "seqlen": wl.seqlens[0], "chunk": wl.chunk,
+                               "rotation": w.rotation()}}
                 log(f"long_prefill: {k_ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
                 del w
                 torch.cuda.empty_cache()
@@ -570,10 +670,9 @@ def main():
                 nb = verify_bytes(wl, sd, w.mean_replay)
                 gbs = nb / (k_ms * 1e-3) / 1e9
                 res[sd] = {"value": round(k_ms * 1e3, 2), "unit": "us/step", "us_per_step_percentiles": dict(LAST_PERCENTILES),
-                           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                        "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                        "traffic": read_traffic("k_gdn_verify", "spec_verify_" + sd),
-                                        "kernel": "k_gdn_verify", "algorithmic_bytes": nb}}
+                           "roofline": hbm_roofline(gbs, nb, read_traffic("k_gdn_verify", "spec_verify_" + sd),
+                                                    "k_gdn_verify"),
+                           "rotation": w.rotation()}
                 log(f"spec_verify {sd}: {k_ms * 1e3:.2f} us/step, {gbs:.0f} GB/s")
                 del w
                 torch.cuda.empty_cache()
