@@ -617,7 +617,7 @@ def main():
                 other["short_prefill"]["chunked_path"] = {
                     "value": round(wl.n_tokens / (c_ms * 1e-3)), "unit": "tokens/s/layer",
                     "us_per_call": round(c_ms * 1e3, 2), "us_per_call_percentiles": dict(LAST_PERCENTILES),
-                    "kernel": "k_gdn_chunk", "chunk": 64,
+                    "kernel": "k_chunk_prep + k_chunk_state", "chunk": 64,
                     "selected_by_gdn_prefill": path == g.GDN_PATH_CHUNKED}
                 log(f"short_prefill, chunked kernel: {c_ms * 1e3:.1f} us")
                 del w
@@ -645,7 +645,8 @@ def main():
                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                                  "frac_of_measured_gemm": round(tf / gemm["value"], 4),
-                                 "traffic": read_traffic("k_gdn_chunk", "long_prefill"), "kernel": "k_gdn_chunk",
+                                 "traffic": read_traffic("k_chunk_prep+k_chunk_state", "long_prefill"),
+                                 "kernel": "k_chunk_prep + k_chunk_state",
                                  "algorithmic_flops": fl,
                                  "hbm_frac": round(chunked_bytes(wl) / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
                     "config": {"n_seqs": len(wl.seqlens), "seqlen": wl.seqlens[0], "chunk": wl.chunk,

@@ -169,7 +169,9 @@ const char* gdn_status_str(int32_t status);
  * `layout`.  Host-only.  Returns GDN_ERR_ARG on invalid dims or layout. */
 int32_t gdn_spec_page_layout(const gdn_dims* dims, int32_t layout, gdn_spec_layout* out);
 
-/* Workspace bytes gdn_chunked_prefill needs for this batch shape (host-only). */
+/* Workspace bytes gdn_chunked_prefill needs for this batch shape (host-only):
+ * (n_seqs + ceil(n_rows / chunk)) chunk slots of h_k key-head and h_v
+ * value-head records (about 145 KB per slot at h_k = 16, h_v = 32, d = 128). */
 int32_t gdn_chunked_workspace_bytes(const gdn_dims* dims, int32_t n_seqs, int64_t n_rows,
                                     int32_t chunk, size_t* out_bytes);
 
@@ -230,11 +232,19 @@ int32_t gdn_recurrent_seq_noalloc(const gdn_dims* dims, const gdn_params* params
  * T = (I + A)^{-1} of A = tril(diag(beta) K K^T o e^{G_i-G_j}, -1), then
  * W = T diag(beta e^G) K, U = T diag(beta) V and the chunk-state update,
  * with bf16 matrix-core products accumulated in fp32.  chunk == 64 is
- * compiled.  workspace: device bytes >= gdn_chunked_workspace_bytes (may be
- * NULL when that is 0).  x rows and conv-window rows are read, and o rows
- * written, as 16-byte vectors: x, conv.base and o must be 16-byte aligned and
- * x_stride and conv.page_stride multiples of 16 bytes' worth of elements (8
- * bf16 or 4 fp32), else GDN_ERR_ARG. */
+ * compiled.  Two launches on `stream`: the first writes every chunk's
+ * state-independent operands (normalised q/k, T-derived W and (T - I)
+ * diag(beta), the masked decayed Q K^T, gates) into the workspace, the
+ * second runs each sequence's chunk-to-chunk state chain from them.
+ * workspace: caller-owned device memory of at least
+ * gdn_chunked_workspace_bytes bytes, 256-byte aligned, else GDN_ERR_ARG; its
+ * contents on entry are ignored and on return are scratch.  Calls that share
+ * one workspace must be ordered.  batch->max_seqlen, when > 0, must bound
+ * every length: a longer sequence is skipped and raises GDN_DEVERR_BATCH.
+ * x rows and conv-window rows are read, and o rows written, as 16-byte
+ * vectors: x, conv.base and o must be 16-byte aligned and x_stride and
+ * conv.page_stride multiples of 16 bytes' worth of elements (8 bf16 or 4
+ * fp32), else GDN_ERR_ARG. */
 int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* params,
                             const void* x, int64_t x_stride,
                             const void* a, const void* b, int64_t ab_stride,

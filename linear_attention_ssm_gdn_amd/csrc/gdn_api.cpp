@@ -190,7 +190,7 @@ GDN_EXPORT int32_t gdn_chunked_workspace_bytes(const gdn_dims* dims, int32_t n_s
     if (st != GDN_OK) return st;
     if (!out_bytes || n_seqs < 0 || n_rows < 0 || chunk <= 0) return GDN_ERR_ARG;
     if (!gdn::chunked_supported(dims->d_k, dims->d_v, chunk)) return GDN_ERR_UNSUPPORTED;
-    *out_bytes = 0;  // the chunked kernels keep every intermediate on chip
+    *out_bytes = gdn::chunked_workspace_bytes(dims->h_k, dims->h_v, n_seqs, n_rows);
     return GDN_OK;
 }
 
@@ -242,7 +242,7 @@ GDN_EXPORT int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* p
         return GDN_ERR_ARG;
     size_t need = 0;
     if ((st = gdn_chunked_workspace_bytes(dims, batch->n_seqs, batch->n_rows, chunk, &need)) != GDN_OK) return st;
-    if (ws_bytes < need || (need > 0 && !workspace)) return GDN_ERR_ARG;
+    if (ws_bytes < need || (need > 0 && (!workspace || !aligned(workspace, 256)))) return GDN_ERR_ARG;
     if (batch->n_seqs == 0) return GDN_OK;
     gdn::ChunkArgs A{};
     A.x = x; A.x_stride = x_stride; A.a = a; A.b = b; A.ab_stride = ab_stride; A.n_rows = batch->n_rows;
@@ -252,8 +252,11 @@ GDN_EXPORT int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* p
     A.state = state.base; A.state_page_stride = state.page_stride; A.state_n_pages = state.n_pages;
     A.o = o; A.err = err; A.h_k = dims->h_k; A.h_v = dims->h_v; A.d_v = dims->d_v;
     A.scale = dims->scale; A.eps = dims->l2_eps;
-    (void)workspace;
-    return from_hip(gdn::launch_chunked(A, dims->d_k, dims->act_dtype, dims->state_dtype, (hipStream_t)stream));
+    A.workspace = workspace;
+    const int64_t max_len = batch->max_seqlen > 0 ? batch->max_seqlen : batch->n_rows;
+    if (max_len > INT32_MAX) return GDN_ERR_ARG;
+    return from_hip(gdn::launch_chunked(A, dims->d_k, dims->act_dtype, dims->state_dtype, (int)max_len,
+                                        (hipStream_t)stream));
 }
 
 namespace {

@@ -1,31 +1,32 @@
 // gdn_chunked.hip -- chunked WY/UT prefill of the GDN layer core (Gated
 // DeltaNet part (c), chunked form) on bf16 matrix cores with fp32
-// accumulation, conv + SiLU + gating fused in.
+// accumulation, conv + SiLU + gating fused in.  Two launches:
 //
-// Grid: one workgroup of 4 waves per (sequence, value head h, block of 64
-// value columns).  Wave w owns the 16-column tile w of the block; its share
-// of the fp32 state S (128 x 16) lives in MFMA accumulator registers for the
-// whole sequence.  Chunks of C = 64 tokens run in order.  Per chunk, with
-// chunk-local cumulative decay G and start state S0:
-//   P1  conv + SiLU on register tiles (q/k: 8 channels x 8 tokens per thread,
-//       v: 4 x 4), fed by 16-byte row loads issued one chunk ahead.  Raw
-//       post-conv q and k go to LDS as bf16 hi/lo pairs, token-major (for
-//       contractions over d) and k also transposed (for contractions over
-//       tokens); v transposed.  The per-token sums of squares are reduced from
-//       the same registers (16 lanes hold one token group), giving the L2-norm
-//       factors rq (with the output scale) and rk, which stay per-token factors
-//       folded into every product below instead of rescaling the arrays.
-//       Wave 0 also takes the gates and the scan of the cumulative decay G.
-//   P3  Q K^T (three-pass hi/lo) and K K^T on MFMA; P_ts = rq_t rk_s (q_t.k_s)
-//       e^{G_t-G_s} and A_ts = beta_t rk_t rk_s (k_t.k_s) e^{G_t-G_s} for s < t,
-//       masked before the exponential; the diagonal gives k_t.q_t.
-//   P4  UT transform T = (I + A)^{-1}: 16x16 diagonal blocks by the doubling
-//       identity (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8) with both N-powers
-//       and their transposes in registers, then the three block sub-diagonals.
-//   P5  W = T diag(beta e^G rk) K (exact diagonal + MFMA for T - I).
-//   P6  U = T diag(beta) V; D = U - W S; O = diag(e^G rq) Q S + diag(k.q) D +
-//       P D; S <- e^{G_last} S + K^T diag(rk e^{G_last-G}) D, the last row of
-//       the chunk as an exact fp32 outer product.
+// k_chunk_prep: one workgroup of 4 waves per (sequence, chunk of C = 64 rows,
+// key head), every chunk at once.  With the chunk-local cumulative decay G:
+//   conv + SiLU of q and k on register tiles (8 channels x 8 tokens per
+//       thread); hi/lo bf16 rows token-major in LDS, k^T straight into the
+//       record.  Per-token sums of squares reduced from the same registers
+//       give the L2-norm factors rq (with the output scale) and rk, which stay
+//       per-token factors folded into every product instead of rescaling the
+//       arrays.
+//   Q K^T (three-pass hi/lo) and K K^T on MFMA, kept in registers.
+//   Per value head of the key head's group: the gates and the scan of G;
+//       P_ts = rq_t rk_s (q_t.k_s) e^{G_t-G_s} and A_ts = beta_t rk_t rk_s
+//       (k_t.k_s) e^{G_t-G_s} for s < t, masked before the exponential; the
+//       UT transform T = (I + A)^{-1} (16x16 diagonal blocks by the doubling
+//       identity (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8), then the three block
+//       sub-diagonals); W = T diag(beta e^G rk) K (exact diagonal + MFMA for
+//       T - I).  All of it goes to the chunk's workspace records.
+// k_chunk_state: one workgroup of 4 waves per (sequence, value head, 64 value
+// columns); wave w owns columns 16w .. 16w+15 and its share of the fp32 state
+// S (128 x 16) in MFMA accumulator registers for the whole sequence.  Chunks
+// run in order, their records streamed into LDS one step ahead:
+//   v conv + SiLU (4 channels x 4 tokens per thread) into a transposed hi/lo tile;
+//   D = U - W S = diag(beta) V + (T - I) diag(beta) V - W S;
+//   O = diag(e^G rq) Q S + diag(k.q) D + P D;
+//   S <- e^{G_last} S + K^T diag(rk e^{G_last-G}) D, the chunk's last row as
+//   an exact fp32 outer product.
 // Rounding points were chosen by emulating the error against the fp64
 // recurrence: single bf16 roundings that multiply a weight-one term (the
 // diagonal of T and of Q K^T, the last row of the state update) would cost up
@@ -51,28 +52,16 @@ constexpr int LQK = 136;       // bf16 row stride of token-major [64][128] array
 constexpr int LT = 72;         // bf16 row stride of [..][64] arrays
 constexpr int LAF = 68;        // fp32 row stride of A [64][64]
 
-// LDS arena (bytes)
+// LDS of the prep kernel (bytes): token-major q and k hi/lo; after the
+// products the k regions hold T and LTbg, the q-lo region A and then -W.
 constexpr int SZ_TOK = CH * LQK * 2;          // 17408
 constexpr int SZ_REG = 18432;                  // regions that later hold two [64][72] bf16 arrays
 constexpr int OFF_QH = 0;
 constexpr int OFF_KH = OFF_QH + SZ_TOK;        // then T (first half) + LTbg (second half)
-constexpr int OFF_QL = OFF_KH + SZ_REG;        // then A (fp32), then W
-constexpr int OFF_KL = OFF_QL + SZ_REG;        // then LTb
-constexpr int OFF_KTH = OFF_KL + SZ_REG;       // [128][72]
-constexpr int OFF_KTL = OFF_KTH + DK * LT * 2;
-constexpr int OFF_VTH = OFF_KTL + DK * LT * 2; // [64][72]
-constexpr int OFF_VTL = OFF_VTH + BVC * LT * 2;
-constexpr int OFF_PH = OFF_VTL + BVC * LT * 2; // [64][72]
-constexpr int OFF_PL = OFF_PH + CH * LT * 2;
-constexpr int OFF_SC = OFF_PL + CH * LT * 2;   // 8 x [64] fp32 scalars
-constexpr int OFF_KLAST = OFF_SC + 8 * CH * 4; // [128] fp32
-constexpr int OFF_WV = OFF_KLAST + DK * 4;       // [64][4] fp32 v-channel conv taps
-constexpr int OFF_WQK = OFF_WV + BVC * 4 * 4;    // [256][4] fp32 q and k channel conv taps
-constexpr int LDS_BYTES = OFF_WQK + 2 * DK * 4 * 4;
-constexpr int LOS = 68;                          // fp32 row stride of the output staging tile (in P's region)
-static_assert(CH * LOS * 4 <= 2 * CH * LT * 2, "output staging fits P");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-static_assert(CH * LAF * 4 <= SZ_REG && CH * LQK * 2 <= SZ_REG, "region sizes");
+constexpr int OFF_QL = OFF_KH + SZ_REG;        // then A (fp32), then -W
+constexpr int OFF_KL = OFF_QL + SZ_REG;
+constexpr int PREP_LDS = OFF_KL + SZ_REG;
+static_assert(CH * LAF * 4 <= SZ_REG && CH * LQK * 2 <= SZ_REG && 2 * CH * LT * 2 <= SZ_REG, "region sizes");
 
 // scalar rows in the SC block
 enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
@@ -119,6 +108,11 @@ __device__ __forceinline__ bf16x8 ld8(const __bf16* base, int ld, int row, int c
 __device__ __forceinline__ bf16x4 ld4(const __bf16* base, int ld, int row, int col) {
     return *reinterpret_cast<const bf16x4*>(base + row * ld + col);
 }
+// An 8-byte LDS read kept as an instruction of its own: the compiler would
+// pair neighbouring 8-byte reads into one ds_read2_b64, which takes twice the
+// LDS cycles of the two single reads (measured with the LDS counters).
+typedef __attribute__((address_space(3))) const volatile bf16x4 lds_bf16x4_v;
+__device__ __forceinline__ bf16x4 ld4s(const __bf16* p) { return *(lds_bf16x4_v*)(p); }
 __device__ __forceinline__ bf16x4 to_bf4(float a, float b, float c, float d) {
     bf16x4 r;
     r[0] = (__bf16)a; r[1] = (__bf16)b; r[2] = (__bf16)c; r[3] = (__bf16)d;
@@ -149,12 +143,6 @@ __device__ __forceinline__ void split_pk(float a, float b, uint32_t& hi, uint32_
     lo = pack_bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-// K^T [128][LT] is stored with its token columns XOR-swizzled in blocks of 8
-// by bits 3..5 of the row, so that the conv threads' 16-byte column writes
-// (eight channels of one token block per lane group) spread over all banks.
-// Every 4- and 8-token operand read stays inside one block.
-__device__ __forceinline__ int kt_at(int row, int col) { return row * LT + (col ^ (row & 0x38)); }
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -183,54 +171,558 @@ template <int N> struct RowVec<float, N> {
     __device__ __forceinline__ float get(int e) const { return v[e >> 2][e & 3]; }
 };
 
-template <typename ActT, typename StT>
-__global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-    __shared__ int sh_last;
+// ============================================================================
+// Workspace: chunk c of sequence s has slot s + (cu[s] >> 6) + c (distinct
+// for packed sequences, fewer than n_seqs + ceil(n_rows / 64) in all); a slot
+// holds h_k key-head records, then h_v value-head records, in the LDS
+// layouts the state kernel reads.
+constexpr int KR_QH = 0;                         // bf16 [64][LQK]: q hi
+constexpr int KR_KTH = KR_QH + CH * LQK * 2;     // bf16 [128][LT]: k^T hi
+constexpr int KR_KTL = KR_KTH + DK * LT * 2;     // bf16 [128][LT]: k^T lo
+constexpr int KR_KLAST = KR_KTL + DK * LT * 2;   // fp32 [128]: rk k of the chunk's last row
+constexpr int KR_RQ = KR_KLAST + DK * 4;         // fp32 [64]: rq (with the output scale)
+constexpr int KR_KQ = KR_RQ + CH * 4;            // fp32 [64]: rq rk (q.k) of each row
+constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 55296
+constexpr int VR_WM = 0;                         // bf16 [64][LQK]: -W
+constexpr int VR_LTB = VR_WM + CH * LQK * 2;     // bf16 [64][64] (sw64): (T - I) diag(beta)
+constexpr int VR_BETA = VR_LTB + CH * CH * 2;    // fp32 [64]
+constexpr int VR_PH = VR_BETA + CH * 4;          // bf16 [64][LT]: P hi (tiles on or below the diagonal)
+constexpr int VR_PL = VR_PH + CH * LT * 2;       // bf16 [64][LT]: P lo
+constexpr int VR_GAM = VR_PL + CH * LT * 2;      // fp32 [64]: e^G
+constexpr int VR_WDR = VR_GAM + CH * 4;          // fp32 [64]: rk e^{G_last - G}, 0 for the last row
+constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 44800, a multiple of 256
+static_assert(VREC_BYTES % 256 == 0 && KREC_BYTES % 256 == 0, "records keep 256-byte alignment");
+static_assert(VR_WDR + CH * 4 <= VREC_BYTES && KREC_BYTES % 256 == 0 && VREC_BYTES % 256 == 0, "records");
+
+__device__ __forceinline__ int64_t chunk_slot(int seq, int r0, int c) { return (int64_t)seq + (r0 >> 6) + c; }
+
+// LDS layouts of the state kernel's matrix operands.  LDS has 64 four-byte
+// banks; an 8-byte read serves 32 consecutive lanes per cycle and a 16-byte
+// read the lanes {0-7, 24-31} and {8-15, 16-23} of each half wave (measured
+// with the bank-conflict counter).  An MFMA operand read takes row lr = lane
+// & 15 and column group lg = lane >> 4.
+//  - [rows][LT] (k^T, P): 8-byte reads of rows 36 words apart fill all 64
+//    banks for every 32 lanes.
+//  - sw64 ([rows][64], LTb and the v tile): rows 128 bytes apart, the 16-byte
+//    column group XORed with ((row >> 1) & 7) ^ ((row >> 4) & 1); conflict
+//    free for both 8- and 16-byte operand reads (16 rows of one XOR pattern
+//    per read), and at most 2-way for the v tile's 8-byte column writes.
+__device__ __forceinline__ int ktr_at(int row, int col) { return row * LT + col; }
+__device__ __forceinline__ int sw64(int row, int col) {
+    return row * CH + (col ^ ((((row >> 1) & 7) ^ ((row >> 4) & 1)) << 3));
+}
+
+// Copy BYTES (a multiple of 64) from global memory into LDS with direct
+// global->LDS loads, 16 bytes per lane: wave w copies the w-th quarter in
+// copy_instrs(BYTES) instructions (the last one partly masked), so every wave
+// issues the same, compile-time number of loads.  The loads are
+// asynchronous: the reader waits for them (vector-memory counter) and a
+// barrier publishes them.
+constexpr int copy_instrs(int bytes) { return (bytes / 64 + 63) / 64; }
+// One 16-byte direct global->LDS load per lane into LDS byte address
+// lds_base + 16 lane, written as an instruction the compiler does not see as
+// an LDS write: it would otherwise order every later LDS read after every
+// such load in flight (a full vector-memory wait at each read), while the
+// kernel orders them itself with counted waits and barriers.  The load has
+// no result register; M0 takes the LDS base one wait state before the load.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+                 : "memory", "m0");
+}
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(const unsigned char* src, unsigned char* dst, int wv, int lane) {
+    static_assert(BYTES % 64 == 0, "whole 16-byte pieces in four equal shares");
+    constexpr int PW = BYTES / 64;  // pieces per wave
+    const int w0 = wv * PW;
+    const uint32_t base = (uint32_t)(uintptr_t)dst + (uint32_t)w0 * 16u;
+#pragma unroll
+    for (int j = 0; j < copy_instrs(BYTES); ++j) {
+        const int p = 64 * j + lane;
+        if (p < PW) dma16(src + ((int64_t)w0 + p) * 16, __builtin_amdgcn_readfirstlane(base + 1024u * j));
+    }
+}
+// The same copy through registers, LDS to global (16 bytes per thread and pass).
+__device__ __forceinline__ void copy_from_lds(const unsigned char* src, unsigned char* dst, int bytes, int tid) {
+    for (int p = tid; p < (bytes >> 4); p += NTH)
+        *reinterpret_cast<u32x4*>(dst + (int64_t)p * 16) = *reinterpret_cast<const u32x4*>(src + p * 16);
+}
+
+// ---------------------------------------------------------------- prep
+template <typename ActT>
+__global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const int nck) {
+    // Qh, Kh, Ql, Kl (k^T goes to the record only):
+    // under 80 KB with the scalars and taps, so two workgroups share a CU
+    __shared__ __attribute__((aligned(16))) unsigned char lds[PREP_LDS];
+    __shared__ __attribute__((aligned(16))) float sc[8 * CH];
+    __shared__ __attribute__((aligned(16))) float wqk[2 * DK * 4];
     __bf16* Qh = reinterpret_cast<__bf16*>(lds + OFF_QH);
     __bf16* Kh = reinterpret_cast<__bf16*>(lds + OFF_KH);
     __bf16* Ql = reinterpret_cast<__bf16*>(lds + OFF_QL);
     __bf16* Kl = reinterpret_cast<__bf16*>(lds + OFF_KL);
-    __bf16* KTh = reinterpret_cast<__bf16*>(lds + OFF_KTH);
-    __bf16* KTl = reinterpret_cast<__bf16*>(lds + OFF_KTL);
-    __bf16* VTh = reinterpret_cast<__bf16*>(lds + OFF_VTH);
-    __bf16* VTl = reinterpret_cast<__bf16*>(lds + OFF_VTL);
-    __bf16* Ph = reinterpret_cast<__bf16*>(lds + OFF_PH);
-    __bf16* Pl = reinterpret_cast<__bf16*>(lds + OFF_PL);
-    float* Af = reinterpret_cast<float*>(lds + OFF_QL);                    // after P3
-    __bf16* Tm = reinterpret_cast<__bf16*>(lds + OFF_KH);                  // after P3
-    __bf16* LTbg = reinterpret_cast<__bf16*>(lds + OFF_KH + CH * LT * 2);  // after P4
-    __bf16* LTb = reinterpret_cast<__bf16*>(lds + OFF_KL);                 // after P4
-    __bf16* Wm = reinterpret_cast<__bf16*>(lds + OFF_QL);                  // -W, after P5
-    float* Os = reinterpret_cast<float*>(lds + OFF_PH);                    // from P6's end to the next P3
-    float* sc = reinterpret_cast<float*>(lds + OFF_SC);
-    float* klast = reinterpret_cast<float*>(lds + OFF_KLAST);
-    float* wv4 = reinterpret_cast<float*>(lds + OFF_WV);
+    float* Af = reinterpret_cast<float*>(lds + OFF_QL);                    // after Q K^T
+    __bf16* Tm = reinterpret_cast<__bf16*>(lds + OFF_KH);                  // after Q K^T
+    __bf16* LTbg = reinterpret_cast<__bf16*>(lds + OFF_KH + CH * LT * 2);  // after the UT solve
+    __bf16* Wm = reinterpret_cast<__bf16*>(lds + OFF_QL);                  // -W, once A is dead
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;  // MFMA row-in-tile / lane group
-    const int nblk = A.d_v / BVC;
+    // Chunks are handed out last-first, so the records the state kernel reads
+    // first are the last written, the likeliest to be in the last-level cache.
     int bid = blockIdx.x;
-    const int blk = bid % nblk;
-    bid /= nblk;
-    const int h = bid % A.h_v;
-    // Dispatch order: with more workgroups than stay resident (one per CU),
-    // index v takes the v-th longest sequence (ties by position), so the
-    // longest sequences start first.  Batches of up to one sequence per
-    // thread are ranked; larger ones keep their order.
-    int seq = bid / A.h_v;
+    const int ki = bid % A.h_k;
+    bid /= A.h_k;
+    const int c = nck - 1 - bid / A.n_seqs;
+    const int seq = bid % A.n_seqs;
+    const int page = A.page_idx[seq];
+    // invalid pages and batches are reported by the state kernel
+    if (page < 0 || page >= A.conv_n_pages || page >= A.state_n_pages) return;
+    const int r0 = A.cu[seq], r1 = A.cu[seq + 1];
+    if (r0 < 0 || r1 < r0 || (int64_t)r1 > A.n_rows) return;
+    const int T = r1 - r0;
+    const int c0 = c * CH;
+    if (c0 >= T) return;
+    const int n = (T - c0 < CH) ? (T - c0) : CH;
+    const bool init = A.has_init ? (A.has_init[seq] != 0) : true;
+    const int rr = A.h_v / A.h_k;
+    const int64_t C = 2 * (int64_t)A.h_k * DK + (int64_t)A.h_v * A.d_v;
+    unsigned char* slot = static_cast<unsigned char*>(A.workspace) +
+                          chunk_slot(seq, r0, c) * ((int64_t)A.h_k * KREC_BYTES + (int64_t)A.h_v * VREC_BYTES);
+    unsigned char* krec = slot + (int64_t)ki * KREC_BYTES;
+    __bf16* KTh = reinterpret_cast<__bf16*>(krec + KR_KTH);  // written here, read back by the W phase
+    __bf16* KTl = reinterpret_cast<__bf16*>(krec + KR_KTL);
+
+    const ActT* __restrict__ X = static_cast<const ActT*>(A.x);
+    const ActT* __restrict__ win = static_cast<const ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
+    const ActT* Wc = static_cast<const ActT*>(A.conv_w);
+    {
+        const int64_t gq = tid < DK ? (int64_t)ki * DK + tid : (int64_t)A.h_k * DK + (int64_t)ki * DK + (tid - DK);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wqk[4 * tid + e] = LOG2E * to_f32(Wc[gq * 4 + e]);
+    }
+    // this thread's q/k tile: part (q, then k) = tid >> 7, tokens 8 tgp .. +7,
+    // channels 8 cgl .. +7 of the key head
+    const int part = tid >> 7, tgp = (tid >> 4) & 7, cgl = tid & 15;
+    RowVec<ActT, 8> nqk[11];
+    {
+        const int64_t gq8 = (int64_t)part * A.h_k * DK + (int64_t)ki * DK + 8 * cgl;
+#pragma unroll
+        for (int j = 0; j < 11; ++j) {
+            const int t = c0 + 8 * tgp - 3 + j;  // < 0 only in the first chunk
+            if (t >= 0)
+                nqk[j].load(X + (int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gq8);
+            else if (init)
+                nqk[j].load(win + (int64_t)(3 + t) * C + gq8);
+            else
+                nqk[j].zero();
+        }
+    }
+    __syncthreads();
+    // ---- conv + SiLU of q and k (log2(e)-scaled), hi/lo rows, k^T, norms
+    {
+        const float* wrow = wqk + 4 * (part * DK + 8 * cgl);
+        u32x4 ph[8], pl[8];
+        float ss[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss[i] = 0.0f;
+#pragma unroll
+        for (int ep = 0; ep < 4; ++ep) {
+            float y[2][8];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = 2 * ep + u;
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 4 * e);
+                const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
+                float xv[11];
+#pragma unroll
+                for (int j = 0; j < 11; ++j) xv[j] = nqk[j].get(e);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    y[u][i] = silu_log2e(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
+                    ss[i] = fmaf(y[u][i], y[u][i], ss[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t hi, lo;
+                split_pk(y[0][i], y[1][i], hi, lo);
+                ph[i][ep] = hi;
+                pl[i][ep] = lo;
+            }
+            if (part) {
+                u32x4 h0, h1, l0, l1;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t a = ph[2 * m][ep], b = ph[2 * m + 1][ep];
+                    const uint32_t cc = pl[2 * m][ep], d = pl[2 * m + 1][ep];
+                    h0[m] = (a & 0xffffu) | (b << 16);
+                    h1[m] = (a >> 16) | (b & 0xffff0000u);
+                    l0[m] = (cc & 0xffffu) | (d << 16);
+                    l1[m] = (cc >> 16) | (d & 0xffff0000u);
+                }
+                const int ch = 8 * cgl + 2 * ep;
+                *reinterpret_cast<u32x4*>(KTh + ktr_at(ch, 8 * tgp)) = h0;
+                *reinterpret_cast<u32x4*>(KTh + ktr_at(ch + 1, 8 * tgp)) = h1;
+                *reinterpret_cast<u32x4*>(KTl + ktr_at(ch, 8 * tgp)) = l0;
+                *reinterpret_cast<u32x4*>(KTl + ktr_at(ch + 1, 8 * tgp)) = l1;
+            }
+        }
+        {
+            __bf16* rowh = (part ? Kh : Qh) + (8 * tgp) * LQK + 8 * cgl;
+            __bf16* rowl = (part ? Kl : Ql) + (8 * tgp) * LQK + 8 * cgl;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                *reinterpret_cast<u32x4*>(rowh + i * LQK) = ph[i];
+                *reinterpret_cast<u32x4*>(rowl + i * LQK) = pl[i];
+            }
+        }
+        float mine = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float sum = reduce16(ss[i]);
+            if ((cgl & 7) == i) mine = sum;
+        }
+        if (cgl < 8) {
+            const int t = 8 * tgp + cgl;
+            sc[(part ? SC_RK : SC_RQ) * CH + t] =
+                t < n ? (part ? 1.0f : A.scale) / sqrtf(mine + (LOG2E * LOG2E) * A.eps) : 0.0f;
+        }
+    }
+    lds_barrier();
+    // ---- the key head's record: q hi, the last row of rk k (the same bits
+    // as k^T holds), rq; k^T went there from the conv
+    copy_from_lds(lds + OFF_QH, krec + KR_QH, CH * LQK * 2, tid);
+    if (tid < DK) {
+        const int d = tid, tl = n - 1;
+        reinterpret_cast<float*>(krec + KR_KLAST)[d] =
+            sc[SC_RK * CH + tl] * ((float)Kh[tl * LQK + d] + (float)Kl[tl * LQK + d]);
+    } else if (tid < DK + CH) {
+        reinterpret_cast<float*>(krec + KR_RQ)[tid - DK] = sc[SC_RQ * CH + tid - DK];
+    }
+    // ---- Q K^T (three-pass hi/lo) and K K^T: the 10 tiles on or below the
+    // diagonal, round-robin over the waves, kept in registers for every value head
+    const int lr = lane & 15, lg = lane >> 4;
+    const int wvs = __builtin_amdgcn_readfirstlane(wv);
+    f32x4 accq[3], acck[3];
+    int tmt[3], tnt[3];
+    for (int idx = wvs, k = 0; k < 3; ++k, idx += 4) {
+        tmt[k] = -1;
+        tnt[k] = 0;
+        accq[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        acck[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (idx >= 10) continue;
+        int mt = 0, rem = idx;
+        while (rem > mt) { rem -= mt + 1; ++mt; }
+        const int nt = rem;
+        tmt[k] = mt;
+        tnt[k] = nt;
+        f32x4 aq = {0.0f, 0.0f, 0.0f, 0.0f}, ak = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int col = 32 * ks + 8 * lg;
+            const bf16x8 qh = ld8(Qh, LQK, 16 * mt + lr, col);
+            const bf16x8 ql = ld8(Ql, LQK, 16 * mt + lr, col);
+            const bf16x8 khm = ld8(Kh, LQK, 16 * mt + lr, col);
+            const bf16x8 khn = ld8(Kh, LQK, 16 * nt + lr, col);
+            const bf16x8 kln = ld8(Kl, LQK, 16 * nt + lr, col);
+            aq = mma32(khn, qh, aq);
+            aq = mma32(kln, qh, aq);
+            aq = mma32(khn, ql, aq);
+            ak = mma32(khn, khm, ak);
+        }
+        settle(aq, ak);
+        accq[k] = aq;
+        acck[k] = ak;
+    }
+    // k_t.q_t from the diagonal tiles (the same for every value head)
+    for (int k = 0; k < 3; ++k) {
+        if (tmt[k] < 0 || tmt[k] != tnt[k]) continue;
+        const int t = 16 * tmt[k] + lr, s0 = 16 * tnt[k] + 4 * lg;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (s0 + j == t) sc[SC_KQ * CH + t] = sc[SC_RQ * CH + t] * sc[SC_RK * CH + t] * accq[k][j];
+    }
+    lds_barrier();  // every read of Q, K (token-major) is done; KQ is published
+    if (tid < CH) reinterpret_cast<float*>(krec + KR_KQ)[tid] = sc[SC_KQ * CH + tid];
+
+    for (int jv = 0; jv < rr; ++jv) {
+        const int h = ki * rr + jv;
+        unsigned char* vrec = slot + (int64_t)A.h_k * KREC_BYTES + (int64_t)h * VREC_BYTES;
+        // ---- gates and the cumulative decay of this value head: wave 0, lane = token
+        if (wv == 0) {
+            const int t = lane;
+            const int tt = c0 + (t < n ? t : n - 1);
+            const int64_t row = (int64_t)(r0 + tt) * A.ab_stride + h;
+            const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
+            const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
+            const float exp_alog = expf(A.a_log[h]);
+            const float g = t < n ? -exp_alog * softplus(av + A.dt_bias[h]) : 0.0f;
+            const float beta = t < n ? sigmoid(bv) : 0.0f;
+            float G = g;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(G, off, 64);
+                if (lane >= off) G += o;
+            }
+            const float Glast = __shfl(G, 63, 64);
+            const float gam = expf(G);
+            const float rk = sc[SC_RK * CH + t];
+            sc[SC_G * CH + t] = G * LOG2E;
+            sc[SC_BETA * CH + t] = beta;
+            sc[SC_GAM * CH + t] = gam;
+            sc[SC_BGR * CH + t] = beta * gam * rk;
+            // the last row of the chunk enters the state update exactly, not through the MFMA
+            const float wdr = (t == n - 1) ? 0.0f : expf(Glast - G) * rk;
+            sc[SC_WDR * CH + t] = wdr;
+            float* vs = reinterpret_cast<float*>(vrec);
+            vs[VR_BETA / 4 + t] = beta;
+            vs[VR_GAM / 4 + t] = gam;
+            vs[VR_WDR / 4 + t] = wdr;
+        }
+        lds_barrier();
+        // ---- P (to the record) and A (to LDS) from the raw products
+        for (int k = 0; k < 3; ++k) {
+            if (tmt[k] < 0) continue;
+            const int mt = tmt[k], nt = tnt[k];
+            const int t = 16 * mt + lr, s0 = 16 * nt + 4 * lg;
+            const float g2t = sc[SC_G * CH + t], rqt = sc[SC_RQ * CH + t];
+            const float rkt = sc[SC_RK * CH + t], bt = sc[SC_BETA * CH + t];
+            const f32x4 g2s = *reinterpret_cast<const f32x4*>(sc + SC_G * CH + s0);
+            const f32x4 rks = *reinterpret_cast<const f32x4*>(sc + SC_RK * CH + s0);
+            float p[4];
+            f32x4 a;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e = __builtin_amdgcn_exp2f(g2t - g2s[j]);
+                const float pv = rqt * rks[j] * accq[k][j] * e;
+                const float av = bt * rkt * rks[j] * acck[k][j] * e;
+                p[j] = s0 + j < t ? pv : 0.0f;
+                a[j] = s0 + j < t ? av : 0.0f;
+            }
+            uint32_t h0, l0, h1, l1;
+            split_pk(p[0], p[1], h0, l0);
+            split_pk(p[2], p[3], h1, l1);
+            *reinterpret_cast<u32x2*>(vrec + VR_PH + (t * LT + s0) * 2) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(vrec + VR_PL + (t * LT + s0) * 2) = u32x2{l0, l1};
+            *reinterpret_cast<f32x4*>(Af + t * LAF + s0) = a;
+        }
+        lds_barrier();
+        // ---- UT transform: diagonal block b = wave by the doubling identity
+        {
+            const int b = wvs;
+            f32x4 nB, ntB, eye;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * lg + j;
+                nB[j] = Af[(16 * b + r) * LAF + 16 * b + lr];
+                ntB[j] = Af[(16 * b + lr) * LAF + 16 * b + r];
+                eye[j] = (r == lr) ? 1.0f : 0.0f;
+            }
+            const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 Y = nB, Z = ntB;
+            f32x4 R = eye - nB;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                f32x4 Yn = mma16(to_bf4(Z), to_bf4(Y), zero);
+                f32x4 Zn = mma16(to_bf4(Y), to_bf4(Z), zero);
+                Y = Yn;
+                Z = Zn;
+                R = mma16(to_bf4(eye + Z), to_bf4(R), zero);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * b + lr] = (__bf16)R[j];
+        }
+        lds_barrier();
+        for (int lev = 1; lev < 4; ++lev) {
+            if (wvs < 4 - lev) {
+                const int cb = wvs, b = wvs + lev;
+                const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                f32x4 Xacc = zero;
+                for (int d = cb; d < b; ++d) {
+                    const float* ar = Af + (16 * b + lr) * LAF + 16 * d + 4 * lg;
+                    const bf16x4 aop = to_bf4(ar[0], ar[1], ar[2], ar[3]);
+                    const bf16x4 bop = {Tm[(16 * d + 4 * lg + 0) * LT + 16 * cb + lr],
+                                        Tm[(16 * d + 4 * lg + 1) * LT + 16 * cb + lr],
+                                        Tm[(16 * d + 4 * lg + 2) * LT + 16 * cb + lr],
+                                        Tm[(16 * d + 4 * lg + 3) * LT + 16 * cb + lr]};
+                    Xacc = mma16(aop, bop, Xacc);
+                }
+                const bf16x4 tbb = ld4(Tm, LT, 16 * b + lr, 16 * b + 4 * lg);
+                f32x4 Yv = mma16(tbb, to_bf4(Xacc), zero);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * cb + lr] = (__bf16)(-Yv[j]);
+            }
+            lds_barrier();
+        }
+        // LT = T - I (strictly lower), column-scaled by beta and by beta e^G rk
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int e = tid + NTH * pass;
+            const int t = e >> 3, s0 = 8 * (e & 7);
+            const bf16x8 tv = *reinterpret_cast<const bf16x8*>(Tm + t * LT + s0);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0 + 4);
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + s0);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + s0 + 4);
+            float lt[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) lt[k] = s0 + k < t ? (float)tv[k] : 0.0f;
+            const u32x4 ob = {pack_bf2(lt[0] * b0[0], lt[1] * b0[1]), pack_bf2(lt[2] * b0[2], lt[3] * b0[3]),
+                              pack_bf2(lt[4] * b1[0], lt[5] * b1[1]), pack_bf2(lt[6] * b1[2], lt[7] * b1[3])};
+            const u32x4 og = {pack_bf2(lt[0] * g0[0], lt[1] * g0[1]), pack_bf2(lt[2] * g0[2], lt[3] * g0[3]),
+                              pack_bf2(lt[4] * g1[0], lt[5] * g1[1]), pack_bf2(lt[6] * g1[2], lt[7] * g1[3])};
+            *reinterpret_cast<u32x4*>(LTbg + t * LT + s0) = og;
+            *reinterpret_cast<u32x4*>(vrec + VR_LTB + sw64(t, s0) * 2) = ob;
+        }
+        // a full barrier: every thread's k^T stores (long since issued) have
+        // completed, so the W phase may read them back (one CU, one L1)
+        __syncthreads();
+        // ---- W[t][d] = bgr_t K[t][d] + (LTbg K)[t][d]; 32 tiles, 8 per wave
+        {
+            f32x4 wacc[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int idx = wvs + 4 * k, mt = idx >> 3, dt = idx & 7;
+                const int d = 16 * dt + lr;
+                const int ko = ktr_at(d, 16 * mt + 4 * lg);
+                const bf16x4 kh = *reinterpret_cast<const bf16x4*>(KTh + ko);
+                const bf16x4 kl = *reinterpret_cast<const bf16x4*>(KTl + ko);
+                const f32x4 bg = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + 16 * mt + 4 * lg);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wacc[k][j] = bg[j] * ((float)kh[j] + (float)kl[j]);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 aop = ld8(LTbg, LT, 16 * mt + lr, 32 * ks + 8 * lg);
+                    const bf16x8 bop = *reinterpret_cast<const bf16x8*>(KTh + ktr_at(d, 32 * ks + 8 * lg));
+                    wacc[k] = mma32(aop, bop, wacc[k]);
+                }
+            }
+            settle8(wacc);
+            // A (same region) is dead since the LT pass
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int idx = wvs + 4 * k, mt = idx >> 3, dt = idx & 7;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Wm[(16 * mt + 4 * lg + j) * LQK + 16 * dt + lr] = (__bf16)(-wacc[k][j]);
+            }
+        }
+        lds_barrier();
+        copy_from_lds(reinterpret_cast<const unsigned char*>(Wm), vrec + VR_WM, CH * LQK * 2, tid);
+        lds_barrier();  // Wm (A's region) and the scalars are rewritten by the next value head
+    }
+}
+
+// ---------------------------------------------------------------- state
+// LDS of the state kernel: four operand groups, each refilled for the next
+// chunk right after its last read in this one, the v tile, the output
+// staging tile and the v taps.
+//   G1 (D = U - W S): -W, LTb, beta         <- value-head record [0, VR_PH)
+//   G2 (Q S):         q hi                  <- key-head record [0, KR_KTH)
+//   G4 (S update):    k^T hi/lo, klast      <- key-head record [KR_KTH, KR_RQ)
+//   G3 (P D, output): P hi/lo, gam, wdr     <- value-head record [VR_PH, VR_WDR + 256)
+//                     rq, kq                <- key-head record [KR_RQ, KREC_BYTES)
+constexpr int G1_BYTES = VR_PH;                        // 25856
+constexpr int G2_BYTES = KR_KTH;                       // 17408
+constexpr int G4_BYTES = KR_RQ - KR_KTH;               // 37376
+constexpr int G3V_BYTES = VR_WDR + CH * 4 - VR_PH;     // 18944
+constexpr int G3K_BYTES = KREC_BYTES - KR_RQ;          // 512
+constexpr int G3_BYTES = G3V_BYTES + G3K_BYTES;        // 19456
+constexpr int S_G1 = 0;
+constexpr int S_G2 = S_G1 + G1_BYTES;
+constexpr int S_G4 = S_G2 + G2_BYTES;
+constexpr int S_G3 = S_G4 + G4_BYTES;
+constexpr int S_VTH = S_G3 + G3_BYTES;
+constexpr int S_VTL = S_VTH + BVC * CH * 2;
+constexpr int S_OS = S_VTL + BVC * CH * 2;
+constexpr int S_WV = S_OS + CH * BVC * 4;
+constexpr int S_LDS = S_WV + BVC * 4 * 4;
+static_assert(S_LDS <= 160 * 1024, "state kernel LDS");
+// Load instructions every wave issues per refill; a wait for a group counts
+// the loads issued after it (other memory operations issued after it only
+// make the wait stronger).
+// The next chunk's v rows (67 rows of the block's 64 channels) go with G1.
+constexpr int XS_ROWS = CH + 3;
+// Staged row r sits at row r ^ ((r >> 2) & 1): the v conv reads rows 4 apart
+// in the two halves of 32 lanes, which then land in opposite bank halves of
+// a 16-bit row (an involution on 0..66).
+__device__ __forceinline__ int xs_row(int r) { return r ^ ((r >> 2) & 1); }
+// Output staging [64][64] fp32, column XOR 16 ((t >> 2) & 3): conflict free
+// for the tile writes (4-byte, rows 4 lg + j) and the 16-byte row reads.
+__device__ __forceinline__ int os_at(int t, int c) { return t * BVC + (c ^ (((t >> 2) & 3) << 4)); }
+// The v taps of channel c sit at 16-byte slot 16 (c & 3) + c / 4, so the
+// 16-byte reads of channels 4 vc4 + e (vc4 = 0..15) hit 16 different slots.
+__device__ __forceinline__ int tap_at(int c) { return ((c & 3) << 4) | (c >> 2); }
+template <typename ActT> constexpr int xs_bytes() { return XS_ROWS * BVC * (int)sizeof(ActT); }
+template <typename ActT>
+constexpr int N1_of() { return copy_instrs(G1_BYTES) + copy_instrs(xs_bytes<ActT>()); }
+constexpr int N2 = copy_instrs(G2_BYTES), N4 = copy_instrs(G4_BYTES);
+constexpr int N3 = copy_instrs(G3V_BYTES) + copy_instrs(G3K_BYTES);
+// Chunk c issues G1(c+1) after phase 1, G2(c+1) after phase 2, G4(c+1)
+// after the state update and G3(c+1) after the output.  Before phase 1 of
+// chunk c the loads issued after G1(c) are G2(c), G4(c), G3(c); before
+// phase 2, G4(c), G3(c), G1(c+1); before the state update (which reads G4(c)
+// and G3(c)), G1(c+1), G2(c+1).  In-order completion of loads makes "at most
+// that many outstanding" mean "G(c) has landed".
+constexpr int WAIT_G1 = N2 + N4 + N3;
+template <typename ActT> constexpr int wait_g2() { return N4 + N3 + N1_of<ActT>(); }
+template <typename ActT> constexpr int wait_g34() { return N1_of<ActT>() + N2; }
+static_assert(wait_g2<float>() <= 63 && WAIT_G1 <= 63 && wait_g34<float>() <= 63, "vmcnt field");
+
+#define GDN_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory")
+
+template <typename ActT, typename StT>
+__global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const int nck) {
+    // One LDS object per operand group: the compiler's wait insertion tells
+    // direct global->LDS loads into one object from reads of another only
+    // when they are distinct objects (else every LDS read waits for every
+    // load in flight).
+    __shared__ __attribute__((aligned(16))) unsigned char g1s[G1_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char g2s[G2_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char g4s[G4_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char g3s[G3_BYTES];
+    __shared__ __attribute__((aligned(16))) __bf16 VTh[BVC * CH];  // v^T hi, sw64
+    __shared__ __attribute__((aligned(16))) __bf16 VTl[BVC * CH];  // v^T lo, sw64
+    __shared__ __attribute__((aligned(16))) float Os[CH * BVC];     // output staging, os_at
+    __shared__ __attribute__((aligned(16))) float wv4[BVC * 4];
+    __shared__ __attribute__((aligned(16))) unsigned char xs[xs_bytes<ActT>()];
+    __shared__ int sh_last;
+    const __bf16* Wm = reinterpret_cast<const __bf16*>(g1s + VR_WM);
+    const __bf16* LTb = reinterpret_cast<const __bf16*>(g1s + VR_LTB);
+    const float* sbeta = reinterpret_cast<const float*>(g1s + VR_BETA);
+    const __bf16* Qh = reinterpret_cast<const __bf16*>(g2s);
+    const __bf16* KTh = reinterpret_cast<const __bf16*>(g4s);
+    const __bf16* KTl = reinterpret_cast<const __bf16*>(g4s + DK * LT * 2);
+    const float* klast = reinterpret_cast<const float*>(g4s + 2 * DK * LT * 2);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nblk = A.d_v / BVC;
+    const int rr = A.h_v / A.h_k;
+    // The M = rr * nblk workgroups of one (sequence, key head) group read the
+    // same key-head record and, in pairs, the same value-head records, chunk
+    // by chunk in lockstep.  Consecutive workgroup indices go to the 8 XCDs
+    // in turn, so group g's members take indices 8 M (g / 8) + 8 m + (g % 8):
+    // one XCD, one L2, dispatched together.
+    const int M = rr * nblk;
+    const int bx = blockIdx.x;
+    const int grp = 8 * (bx / (8 * M)) + (bx % 8);
+    const int mem = (bx / 8) % M;
+    if (grp >= A.n_seqs * A.h_k) return;
+    const int ki = grp % A.h_k;
+    const int blk = mem % nblk;
+    const int h = ki * rr + mem / nblk;
+    // the v-th group row takes the v-th longest sequence (ties by position)
+    int seq = grp / A.h_k;
     if (A.n_seqs > 1 && A.n_seqs <= NTH) {
-        int* len = reinterpret_cast<int*>(lds + OFF_SC);  // free until the first chunk's gates
-        const int n = A.n_seqs;
+        int* len = reinterpret_cast<int*>(Os);
+        const int ns = A.n_seqs;
         int my = 0;
-        if (tid < n) {
+        if (tid < ns) {
             my = A.cu[tid + 1] - A.cu[tid];
             len[tid] = my;
         }
         __syncthreads();
-        if (tid < n) {
+        if (tid < ns) {
             int rank = 0;
-            for (int j = 0; j < n; ++j) {
+            for (int j = 0; j < ns; ++j) {
                 const int lj = len[j];
                 rank += (lj > my || (lj == my && j < tid)) ? 1 : 0;
             }
@@ -238,10 +730,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
         }
         __syncthreads();
         seq = sh_last;
-        __syncthreads();  // sh_last is reused at the end
+        __syncthreads();
     }
-    const int rr = A.h_v / A.h_k;
-    const int ki = h / rr;
     const int colbase = blk * BVC;
     const int64_t C = 2 * (int64_t)A.h_k * DK + (int64_t)A.h_v * A.d_v;
 
@@ -258,7 +748,50 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
     }
     const int T = r1 - r0;
     if (T == 0) return;
+    const int nch = (T + CH - 1) / CH;
+    if (nch > nck) {  // longer than the bound the records were made for
+        if (tid == 0 && h == 0 && blk == 0) set_err(A.err, GDN_DEVERR_BATCH);
+        return;
+    }
     const bool init = A.has_init ? (A.has_init[seq] != 0) : true;
+    const int64_t slot_bytes = (int64_t)A.h_k * KREC_BYTES + (int64_t)A.h_v * VREC_BYTES;
+    const unsigned char* ws = static_cast<const unsigned char*>(A.workspace);
+    auto krec = [&](int c) { return ws + chunk_slot(seq, r0, c) * slot_bytes + (int64_t)ki * KREC_BYTES; };
+    auto vrec = [&](int c) {
+        return ws + chunk_slot(seq, r0, c) * slot_bytes + (int64_t)A.h_k * KREC_BYTES + (int64_t)h * VREC_BYTES;
+    };
+    const int wvs = __builtin_amdgcn_readfirstlane(wv);
+    // Refills for chunk c; past the last chunk they reload the last chunk's
+    // records (nothing reads them) so that every chunk issues the same loads.
+    const ActT* __restrict__ Xv = static_cast<const ActT*>(A.x) + 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase;
+    // G1 of chunk c, then chunk c's v rows c0-3 .. c0+63 (c >= 1, so all from x;
+    // rows past the sequence clamped to its last), 16-byte pieces, a quarter per wave
+    auto fill_g1 = [&](int c) {
+        copy_to_lds<G1_BYTES>(vrec(c < nch ? c : nch - 1), g1s, wvs, lane);
+        constexpr int PPR = BVC * (int)sizeof(ActT) / 16;   // pieces per row
+        constexpr int PW = xs_bytes<ActT>() / 64;           // pieces per wave
+        const int w0 = wvs * PW;
+        const uint32_t base = (uint32_t)(uintptr_t)xs + (uint32_t)w0 * 16u;
+        const int cs = (c < nch ? c : nch - 1) * CH - 3;
+#pragma unroll
+        for (int j = 0; j < copy_instrs(xs_bytes<ActT>()); ++j) {
+            const int p = w0 + 64 * j + lane;
+            if (64 * j + lane < PW) {
+                const int r = xs_row(p / PPR), q = p % PPR;
+                int t = cs + r;
+                t = t < 0 ? 0 : (t < T ? t : T - 1);
+                dma16(Xv + (int64_t)(r0 + t) * A.x_stride + q * (16 / (int)sizeof(ActT)),
+                      __builtin_amdgcn_readfirstlane(base + 1024u * j));
+            }
+        }
+    };
+    auto fill_g2 = [&](int c) { copy_to_lds<G2_BYTES>(krec(c < nch ? c : nch - 1), g2s, wvs, lane); };
+    auto fill_g4 = [&](int c) { copy_to_lds<G4_BYTES>(krec(c < nch ? c : nch - 1) + KR_KTH, g4s, wvs, lane); };
+    auto fill_g3 = [&](int c) {
+        const int cc = c < nch ? c : nch - 1;
+        copy_to_lds<G3V_BYTES>(vrec(cc) + VR_PH, g3s, wvs, lane);
+        copy_to_lds<G3K_BYTES>(krec(cc) + KR_RQ, g3s + G3V_BYTES, wvs, lane);
+    };
 
     // ---- state: wave w holds S[16 dt + 4 lg + j][16 w + lr], dt = 0..7
     StT* __restrict__ Sg = static_cast<StT*>(A.state) + (int64_t)page * A.state_page_stride +
@@ -267,75 +800,34 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            s[dt][j] = init ? to_f32(Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v]) : 0.0f;
+        for (int j = 0; j < 4; ++j) s[dt][j] = init ? to_f32(Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v]) : 0.0f;
 
-    // ---- conv taps to LDS: q/k channel `tid` (q for tid < 128), v channel `tid`
+    // the first chunk's operands, in the order a chunk issues them
+    fill_g1(0);
+    fill_g2(0);
+    fill_g4(0);
+    fill_g3(0);
+
+    // ---- v taps: channel tid of the block
     const ActT* __restrict__ X = static_cast<const ActT*>(A.x);
     ActT* __restrict__ win = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
     const ActT* Wc = static_cast<const ActT*>(A.conv_w);
-    const int64_t gq = tid < DK ? (int64_t)ki * DK + tid : (int64_t)A.h_k * DK + (int64_t)ki * DK + (tid - DK);
     const bool has_v = tid < BVC;
     const int64_t gv = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + tid;
-    float* wqk = reinterpret_cast<float*>(lds + OFF_WQK);
-    // q and k are only ever used through their L2-norm factors, so they are
-    // carried scaled by log2(e) (conv taps scaled here, eps by log2(e)^2 in
-    // the norms), which puts the SiLU's exponential on exp2 directly
-#pragma unroll
-    for (int e = 0; e < 4; ++e) wqk[4 * tid + e] = LOG2E * to_f32(Wc[gq * 4 + e]);
     if (has_v) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wv4[4 * tid + e] = to_f32(Wc[gv * 4 + e]);
+        for (int e = 0; e < 4; ++e) wv4[4 * tap_at(tid) + e] = to_f32(Wc[gv * 4 + e]);
     }
-    __syncthreads();
-    const float exp_alog = expf(A.a_log[h]);
-    const float dtb = A.dt_bias[h];
-    bool my_last = false;
     float* __restrict__ Og = A.o + (int64_t)r0 * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase;
     const int64_t o_stride = (int64_t)A.h_v * A.d_v;
 
-    // ---- conv tiles.  q/k: part (q, then k) = tid >> 7, tokens 8 tgp .. +7,
-    // channels 8 cgl .. +7 of the key head, so the 16 lanes of a DPP row hold
-    // one token group over all 128 channels.  v: tokens 4 tq4 .. +3, channels
-    // 4 vc4 .. +3 of the block.  The lane-derived offsets are recomputed at
-    // each use from an opaque copy of tid (cheap integer work) rather than
-    // hoisted out of the chunk loop, where they would hold registers for its
-    // whole length.
-    auto fresh_tid = [&]() {
-        int t = tid;
-        asm volatile("" : "+v"(t));
-        return t;
-    };
-    // the same for the MFMA phases' lane indices (the wave index made scalar)
-#define PHASE_IDS                                                                      \
-    const int tid = fresh_tid(), lane = tid & 63, lr = lane & 15, lg = lane >> 4;     \
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);                          \
-    (void)lane; (void)lr; (void)lg; (void)wv
-
-    // ---- a chunk's raw inputs, loaded one chunk ahead into spare registers
-    // (issued once the current chunk's own loads are consumed, so no wait in
-    // a chunk ever covers them): each tile's rows with the three before them
-    // (from x, or the window before the first token), and the gate inputs of
-    // token `lane` (wave 0).  Rows past the end are clamped into the sequence
-    // (their outputs are masked), so every load is unconditional.
-    RowVec<ActT, 8> nqk[11];
+    // a thread's v rows of a chunk: channels 4 vc4 .. +3 (vc4 = tid & 15, so
+    // the 16 lanes of a row group read one contiguous row), tokens 4 tq4 ..
+    // +3 (tq4 = tid >> 4) and the three before them
     RowVec<ActT, 4> nvv[7];
-    ActT na = ActT(0), nb = ActT(0);
-    auto prefetch = [&](int cs) {
-        const int ft = fresh_tid();
-        const int tgp = (ft >> 4) & 7, tq4 = ft & 15;
-        const int64_t gq8 = (int64_t)(ft >> 7) * A.h_k * DK + (int64_t)ki * DK + 8 * (ft & 15);
-        const int64_t gv4 = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + 4 * (ft >> 4);
-#pragma unroll
-        for (int j = 0; j < 11; ++j) {
-            const int t = cs + 8 * tgp - 3 + j;  // sequence-relative row; < 0 only in the first chunk
-            if (t >= 0)
-                nqk[j].load(X + (int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gq8);
-            else if (init)
-                nqk[j].load(win + (int64_t)(3 + t) * C + gq8);
-            else
-                nqk[j].zero();
-        }
+    auto prefetch_v = [&](int cs) {
+        const int tq4 = tid >> 4;
+        const int64_t gv4 = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + 4 * (tid & 15);
 #pragma unroll
         for (int j = 0; j < 7; ++j) {
             const int t = cs + 4 * tq4 - 3 + j;
@@ -346,436 +838,132 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
             else
                 nvv[j].zero();
         }
-        if (wv == 0) {
-            const int t = cs + lane < T ? cs + lane : T - 1;
-            const int64_t row = (int64_t)(r0 + t) * A.ab_stride + h;
-            na = static_cast<const ActT*>(A.a)[row];
-            nb = static_cast<const ActT*>(A.b)[row];
+    };
+    // v conv of a chunk from its rows (prefetched into registers for the
+    // first chunk, staged in LDS for the others): 4 channels x 4 tokens per
+    // thread, stored transposed (hi/lo)
+    auto conv_v = [&](bool from_lds) {
+        const int tq4 = tid >> 4, vc4 = tid & 15;
+        if (from_lds) {
+#pragma unroll
+            for (int j = 0; j < 7; ++j)
+                nvv[j].load(reinterpret_cast<const ActT*>(xs) + xs_row(4 * tq4 + j) * BVC + 4 * vc4);
+        }
+        u32x2 th[4], tl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int col = 4 * vc4 + e;
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(wv4 + 4 * tap_at(col));
+            const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
+            float xv[7];
+#pragma unroll
+            for (int j = 0; j < 7; ++j) xv[j] = nvv[j].get(e);
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
+            uint32_t h0, l0, h1, l1;
+            split_pk(y[0], y[1], h0, l0);
+            split_pk(y[2], y[3], h1, l1);
+            th[e] = u32x2{h0, h1};
+            tl[e] = u32x2{l0, l1};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int at = sw64(4 * vc4 + e, 4 * tq4);
+            *reinterpret_cast<u32x2*>(VTh + at) = th[e];
+            *reinterpret_cast<u32x2*>(VTl + at) = tl[e];
         }
     };
-    prefetch(0);
-
-    // A chunk's output tile (wave w: columns 16 w .. +15, in MFMA accumulator
-    // layout) goes to LDS once the chunk's last read of P is done, and to
-    // memory as 16-byte row pieces during the next chunk, right after that
-    // chunk's prefetch is issued.
-    f32x4 o_tile[4];
+    prefetch_v(0);
     int o_c0 = 0, o_n = 0;
-    auto stage_o = [&]() {
-        PHASE_IDS;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Os[(16 * mt + 4 * lg + j) * LOS + 16 * wv + lr] = o_tile[mt][j];
-    };
     auto store_o = [&]() {
-        const int ft = fresh_tid();
-        const int c4 = ft & 15, r = ft >> 4;
+        const int c4 = tid & 15, r = tid >> 4;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int t = r + 16 * it;
             if (t < o_n)
                 *reinterpret_cast<f32x4*>(Og + (int64_t)(o_c0 + t) * o_stride + 4 * c4) =
-                    *reinterpret_cast<const f32x4*>(Os + t * LOS + 4 * c4);
+                    *reinterpret_cast<const f32x4*>(Os + os_at(t, 4 * c4));
         }
         o_n = 0;
     };
+    __syncthreads();  // taps
+    conv_v(false);     // the first chunk's v tile (published by the barrier before phase 1)
 
-    for (int c0 = 0; c0 < T; c0 += CH) {
+    for (int ci = 0; ci < nch; ++ci) {
+        const int c0 = ci * CH;
         const int n = (T - c0 < CH) ? (T - c0) : CH;
-        // ================================================================ P1
-        {
-            // q/k tile, two channels at a time over the 8 tokens: each pair packs
-            // into one dword of every token-major row.  Outputs of tokens past
-            // the end are left unmasked: their inputs are clamped real rows, so
-            // they are finite, and every product that reads them is scaled by a
-            // zero factor (rq, rk or beta of the padded token).
-            const int ft = fresh_tid();
-            const int part = ft >> 7, tgp = (ft >> 4) & 7, cgl = ft & 15;
-            const int tq4 = ft & 15, vc4 = ft >> 4;
-            const float* wrow = wqk + 4 * (part * DK + 8 * cgl);
-            u32x4 ph[8], pl[8];
-            float ss[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss[i] = 0.0f;
-#pragma unroll
-            for (int ep = 0; ep < 4; ++ep) {
-                float y[2][8];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int e = 2 * ep + u;
-                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 4 * e);
-                    const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
-                    float xv[11];
-#pragma unroll
-                    for (int j = 0; j < 11; ++j) xv[j] = nqk[j].get(e);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        y[u][i] = silu_log2e(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
-                        ss[i] = fmaf(y[u][i], y[u][i], ss[i]);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    uint32_t hi, lo;
-                    split_pk(y[0][i], y[1][i], hi, lo);
-                    ph[i][ep] = hi;
-                    pl[i][ep] = lo;
-                }
-                if (part) {  // k also transposed: rows 2 ep (low halves) and 2 ep + 1 (high halves)
-                    u32x4 h0, h1, l0, l1;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const uint32_t a = ph[2 * m][ep], b = ph[2 * m + 1][ep];
-                        const uint32_t c = pl[2 * m][ep], d = pl[2 * m + 1][ep];
-                        h0[m] = (a & 0xffffu) | (b << 16);
-                        h1[m] = (a >> 16) | (b & 0xffff0000u);
-                        l0[m] = (c & 0xffffu) | (d << 16);
-                        l1[m] = (c >> 16) | (d & 0xffff0000u);
-                    }
-                    const int c = 8 * cgl + 2 * ep;
-                    *reinterpret_cast<u32x4*>(KTh + kt_at(c, 8 * tgp)) = h0;
-                    *reinterpret_cast<u32x4*>(KTh + kt_at(c + 1, 8 * tgp)) = h1;
-                    *reinterpret_cast<u32x4*>(KTl + kt_at(c, 8 * tgp)) = l0;
-                    *reinterpret_cast<u32x4*>(KTl + kt_at(c + 1, 8 * tgp)) = l1;
-                }
-            }
-            {
-                __bf16* rowh = (part ? Kh : Qh) + (8 * tgp) * LQK + 8 * cgl;
-                __bf16* rowl = (part ? Kl : Ql) + (8 * tgp) * LQK + 8 * cgl;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    *reinterpret_cast<u32x4*>(rowh + i * LQK) = ph[i];
-                    *reinterpret_cast<u32x4*>(rowl + i * LQK) = pl[i];
-                }
-            }
-            // L2-norm factors: lane cgl (< 8) of the row writes token 8 tgp + cgl
-            float mine = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float sum = reduce16(ss[i]);
-                if ((cgl & 7) == i) mine = sum;
-            }
-            if (cgl < 8) {
-                const int t = 8 * tgp + cgl;
-                sc[(part ? SC_RK : SC_RQ) * CH + t] =
-                    t < n ? (part ? 1.0f : A.scale) / sqrtf(mine + (LOG2E * LOG2E) * A.eps) : 0.0f;
-            }
-
-            // v tile: channel by channel, 4 tokens each, stored transposed
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int col = 4 * vc4 + e;
-                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wv4 + 4 * col);
-                const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
-                float xv[7];
-#pragma unroll
-                for (int j = 0; j < 7; ++j) xv[j] = nvv[j].get(e);
-                float y[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = silu_fast(conv4(w, xv[i], xv[i + 1], xv[i + 2], xv[i + 3]));
-                uint32_t h0, l0, h1, l1;
-                split_pk(y[0], y[1], h0, l0);
-                split_pk(y[2], y[3], h1, l1);
-                const u32x2 th = {h0, h1}, tl = {l0, l1};
-                *reinterpret_cast<u32x2*>(VTh + col * LT + 4 * tq4) = th;
-                *reinterpret_cast<u32x2*>(VTl + col * LT + 4 * tq4) = tl;
-            }
-
-            // gates and the cumulative decay: wave 0, lane = token
-            if (wv == 0) {
-                const int t = lane;
-                const float av = to_f32(na);
-                const float bv = to_f32(nb);
-                const float g = t < n ? -exp_alog * softplus(av + dtb) : 0.0f;
-                const float beta = t < n ? sigmoid(bv) : 0.0f;
-                float G = g;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float o = __shfl_up(G, off, 64);
-                    if (lane >= off) G += o;
-                }
-                const float Glast = __shfl(G, 63, 64);
-                sc[SC_G * CH + t] = G * LOG2E;  // P3 takes exp2 of differences
-                sc[SC_BETA * CH + t] = beta;
-                sc[SC_GAM * CH + t] = expf(G);
-                sc[SC_WDR * CH + t] = expf(Glast - G);  // rk folded in below
-            }
-        }
-        lds_barrier();
-        if (c0 == 0 && tid == 0)  // every window read of this workgroup has been consumed
-            my_last = arrive_last(A.sync + (int64_t)page * A.h_k + ki, (uint32_t)(rr * nblk));
-        // the next chunk's inputs: every load of this chunk has been consumed
-        if (c0 + CH < T) prefetch(c0 + CH);
-        // then the previous chunk's outputs: a wait for the prefetch above (in
-        // order) never covers stores issued after it
+        const unsigned char* g3 = g3s;
+        const __bf16* Ph = reinterpret_cast<const __bf16*>(g3);
+        const __bf16* Pl = reinterpret_cast<const __bf16*>(g3 + VR_PL - VR_PH);
+        const float* sgam = reinterpret_cast<const float*>(g3 + VR_GAM - VR_PH);
+        const float* swdr = reinterpret_cast<const float*>(g3 + VR_WDR - VR_PH);
+        const float* srq = reinterpret_cast<const float*>(g3 + G3V_BYTES);
+        const float* skq = reinterpret_cast<const float*>(g3 + G3V_BYTES + CH * 4);
+        // the previous chunk's outputs (staged before the barrier that ended it)
         store_o();
-        // ================================================================ P3
-        {
-            PHASE_IDS;
-            // the 10 tiles on or below the diagonal, round-robin over the waves
-            f32x4 accq[3], acck[3];
-            int tmt[3], tnt[3];
-            int cnt = 0;
-            for (int idx = wv, k = 0; k < 3; ++k, idx += 4) {
-                tmt[k] = -1;
-                if (idx >= 10) continue;
-                int mt = 0, rem = idx;
-                while (rem > mt) { rem -= mt + 1; ++mt; }
-                const int nt = rem;
-                tmt[k] = mt; tnt[k] = nt;
-                f32x4 aq = {0.0f, 0.0f, 0.0f, 0.0f}, ak = {0.0f, 0.0f, 0.0f, 0.0f};
+        const int colv = 16 * wv + lr;
+        bf16x8 sb[4];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int col = 32 * ks + 8 * lg;
-                    const bf16x8 qh = ld8(Qh, LQK, 16 * mt + lr, col);
-                    const bf16x8 ql = ld8(Ql, LQK, 16 * mt + lr, col);
-                    const bf16x8 khm = ld8(Kh, LQK, 16 * mt + lr, col);
-                    const bf16x8 khn = ld8(Kh, LQK, 16 * nt + lr, col);
-                    const bf16x8 kln = ld8(Kl, LQK, 16 * nt + lr, col);
-                    // transposed tiles (rows s, columns t), so that each lane holds
-                    // four consecutive s of one t and writes them as one vector
-                    aq = mma32(khn, qh, aq);
-                    aq = mma32(kln, qh, aq);
-                    aq = mma32(khn, ql, aq);
-                    ak = mma32(khn, khm, ak);
-                }
-                settle(aq, ak);
-                accq[k] = aq; acck[k] = ak;
-                ++cnt;
-            }
-            lds_barrier();  // Ql is about to be overwritten by A
-            if (tid < CH) {
-                const int t = tid;
-                const float rk = sc[SC_RK * CH + t];
-                sc[SC_BGR * CH + t] = sc[SC_BETA * CH + t] * sc[SC_GAM * CH + t] * rk;
-                // the last row of the chunk enters the state update exactly, not through the MFMA
-                sc[SC_WDR * CH + t] = (t == n - 1) ? 0.0f : sc[SC_WDR * CH + t] * rk;
-            } else if (tid < CH + DK) {
-                const int d = tid - CH, tl = n - 1;
-                klast[d] = sc[SC_RK * CH + tl] * ((float)KTh[kt_at(d, tl)] + (float)KTl[kt_at(d, tl)]);
-            }
-            for (int k = 0; k < 3; ++k) {
-                if (tmt[k] < 0) continue;
-                const int mt = tmt[k], nt = tnt[k];
-                const int t = 16 * mt + lr, s0 = 16 * nt + 4 * lg;
-                const float g2t = sc[SC_G * CH + t], rqt = sc[SC_RQ * CH + t];
-                const float rkt = sc[SC_RK * CH + t], bt = sc[SC_BETA * CH + t];
-                const f32x4 g2s = *reinterpret_cast<const f32x4*>(sc + SC_G * CH + s0);
-                const f32x4 rks = *reinterpret_cast<const f32x4*>(sc + SC_RK * CH + s0);
-                float p[4];
-                f32x4 a;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // computed for every s and selected: for s >= t the exponential
-                    // may overflow, and is discarded
-                    const float e = __builtin_amdgcn_exp2f(g2t - g2s[j]);
-                    const float pv = rqt * rks[j] * accq[k][j] * e;
-                    const float av = bt * rkt * rks[j] * acck[k][j] * e;
-                    p[j] = s0 + j < t ? pv : 0.0f;
-                    a[j] = s0 + j < t ? av : 0.0f;
-                    if (s0 + j == t) sc[SC_KQ * CH + t] = rqt * rkt * accq[k][j];
-                }
-                uint32_t h0, l0, h1, l1;
-                split_pk(p[0], p[1], h0, l0);
-                split_pk(p[2], p[3], h1, l1);
-                *reinterpret_cast<u32x2*>(Ph + t * LT + s0) = u32x2{h0, h1};
-                *reinterpret_cast<u32x2*>(Pl + t * LT + s0) = u32x2{l0, l1};
-                *reinterpret_cast<f32x4*>(Af + t * LAF + s0) = a;
-            }
-            (void)cnt;
-        }
+        for (int kk = 0; kk < 4; ++kk) sb[kk] = cat8(to_bf4(s[2 * kk]), to_bf4(s[2 * kk + 1]));
+        // ================================ phase 1: D = U - W S = beta V + LTb V + (-W) S
+        GDN_WAIT_VM(WAIT_G1);
         lds_barrier();
-        // ================================================================ P4
-        {
-            PHASE_IDS;
-            // diagonal block b = wv: T_bb = (I - N)(I + N^2)(I + N^4)(I + N^8)
-            const int b = wv;
-            f32x4 nB, ntB, eye;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * lg + j;
-                nB[j] = Af[(16 * b + r) * LAF + 16 * b + lr];   // N[r][lr]
-                ntB[j] = Af[(16 * b + lr) * LAF + 16 * b + r];  // N^T[r][lr]
-                eye[j] = (r == lr) ? 1.0f : 0.0f;
-            }
-            const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            f32x4 Y = nB, Z = ntB;                 // N^(2^k) and its transpose, accumulator layout
-            f32x4 R = eye - nB;                    // running product, starts at I - N
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                f32x4 Yn = mma16(to_bf4(Z), to_bf4(Y), zero);  // Y <- Y Y (A operand = layout of Y^T = Z)
-                f32x4 Zn = mma16(to_bf4(Y), to_bf4(Z), zero);  // Z <- Z Z
-                Y = Yn; Z = Zn;
-                R = mma16(to_bf4(eye + Z), to_bf4(R), zero);         // R <- (I + Y) R
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * b + lr] = (__bf16)R[j];
-        }
-        lds_barrier();
-        // off-diagonal blocks by sub-diagonal level: T_bc = -T_bb sum_{d=c}^{b-1} A_bd T_dc
-        for (int lev = 1; lev < 4; ++lev) {
-            PHASE_IDS;
-            if (wv < 4 - lev) {
-                const int c = wv, b = wv + lev;
-                const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                f32x4 Xacc = zero;
-                for (int d = c; d < b; ++d) {
-                    // A operand: A_bd[lr][4 lg + i]; B operand: T_dc[4 lg + i][lr]
-                    const float* ar = Af + (16 * b + lr) * LAF + 16 * d + 4 * lg;
-                    const bf16x4 aop = to_bf4(ar[0], ar[1], ar[2], ar[3]);
-                    const bf16x4 bop = {Tm[(16 * d + 4 * lg + 0) * LT + 16 * c + lr],
-                                        Tm[(16 * d + 4 * lg + 1) * LT + 16 * c + lr],
-                                        Tm[(16 * d + 4 * lg + 2) * LT + 16 * c + lr],
-                                        Tm[(16 * d + 4 * lg + 3) * LT + 16 * c + lr]};
-                    Xacc = mma16(aop, bop, Xacc);
-                }
-                const bf16x4 tbb = ld4(Tm, LT, 16 * b + lr, 16 * b + 4 * lg);
-                f32x4 Yv = mma16(tbb, to_bf4(Xacc), zero);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Tm[(16 * b + 4 * lg + j) * LT + 16 * c + lr] = (__bf16)(-Yv[j]);
-            }
+        if (ci > 0) {  // this chunk's v tile from its staged rows (the previous tile was last read in phase 1)
+            conv_v(true);
             lds_barrier();
         }
-        // LT = T - I (strictly lower), column-scaled by beta and by beta e^G rk
-        // (8 columns of one row per thread and pass)
+        f32x4 D[4];
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int e = fresh_tid() + NTH * pass;
-            const int t = e >> 3, s0 = 8 * (e & 7);
-            const bf16x8 tv = *reinterpret_cast<const bf16x8*>(Tm + t * LT + s0);
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0);
-            const f32x4 b1 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0 + 4);
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + s0);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + s0 + 4);
-            float lt[8];
+        for (int mt = 0; mt < 4; ++mt) {
+            const int t0 = 16 * mt + 4 * lg;
+            const bf16x4 vh = *reinterpret_cast<const bf16x4*>(VTh + sw64(colv, t0));
+            const bf16x4 vl = *reinterpret_cast<const bf16x4*>(VTl + sw64(colv, t0));
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(sbeta + t0);
+            f32x4 u;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) lt[k] = s0 + k < t ? (float)tv[k] : 0.0f;
-            const u32x4 ob = {pack_bf2(lt[0] * b0[0], lt[1] * b0[1]), pack_bf2(lt[2] * b0[2], lt[3] * b0[3]),
-                              pack_bf2(lt[4] * b1[0], lt[5] * b1[1]), pack_bf2(lt[6] * b1[2], lt[7] * b1[3])};
-            const u32x4 og = {pack_bf2(lt[0] * g0[0], lt[1] * g0[1]), pack_bf2(lt[2] * g0[2], lt[3] * g0[3]),
-                              pack_bf2(lt[4] * g1[0], lt[5] * g1[1]), pack_bf2(lt[6] * g1[2], lt[7] * g1[3])};
-            *reinterpret_cast<u32x4*>(LTb + t * LT + s0) = ob;
-            *reinterpret_cast<u32x4*>(LTbg + t * LT + s0) = og;
+            for (int j = 0; j < 4; ++j) u[j] = bt[j] * ((float)vh[j] + (float)vl[j]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                u = mma32(*reinterpret_cast<const bf16x8*>(LTb + sw64(16 * mt + lr, 32 * ks + 8 * lg)),
+                          *reinterpret_cast<const bf16x8*>(VTh + sw64(colv, 32 * ks + 8 * lg)), u);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                u = mma32(cat8(ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 4 * lg),
+                               ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 16 + 4 * lg)),
+                          sb[kk], u);
+            D[mt] = u;
         }
+        settle4(D);
+        bf16x4 dh[4], dl[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) split4(D[mt], dh[mt], dl[mt]);
+        lds_barrier();  // every read of G1 and of the v tile is done
+        fill_g1(ci + 1);
+        // ================================ phase 2: Q S
+        GDN_WAIT_VM(wait_g2<ActT>());
         lds_barrier();
-        // ================================================================ P5
-        {
-            PHASE_IDS;
-            // W[t][d] = bgr_t K[t][d] + (LTbg K)[t][d]; 32 tiles, 8 per wave
-            f32x4 wacc[8];
+        f32x4 qs[4];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int idx = wv + 4 * k, mt = idx >> 3, dt = idx & 7;
-                const int d = 16 * dt + lr;
-                const int ko = kt_at(d, 16 * mt + 4 * lg);
-                const bf16x4 kh = *reinterpret_cast<const bf16x4*>(KTh + ko);
-                const bf16x4 kl = *reinterpret_cast<const bf16x4*>(KTl + ko);
-                const f32x4 bg = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + 16 * mt + 4 * lg);
+        for (int mt = 0; mt < 4; ++mt) {
+            const int row = 16 * mt + lr;
+            qs[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wacc[k][j] = bg[j] * ((float)kh[j] + (float)kl[j]);
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 aop = ld8(LTbg, LT, 16 * mt + lr, 32 * ks + 8 * lg);
-                    const bf16x8 bop = *reinterpret_cast<const bf16x8*>(KTh + kt_at(d, 32 * ks + 8 * lg));
-                    wacc[k] = mma32(aop, bop, wacc[k]);
-                }
-            }
-            settle8(wacc);
-            // A (in the same region) is dead since the LT pass; W takes its place
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int idx = wv + 4 * k, mt = idx >> 3, dt = idx & 7;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Wm[(16 * mt + 4 * lg + j) * LQK + 16 * dt + lr] = (__bf16)(-wacc[k][j]);
-            }
+            for (int kk = 0; kk < 4; ++kk)
+                qs[mt] = mma32(cat8(ld4s(Qh + row * LQK + 32 * kk + 4 * lg), ld4s(Qh + row * LQK + 32 * kk + 16 + 4 * lg)),
+                               sb[kk], qs[mt]);
         }
+        settle4(qs);
         lds_barrier();
-        // ================================================================ P6
+        fill_g2(ci + 1);
+        // ================================ phase 3: S <- e^{G_last} S + K^T diag(rk e^{G_last - G}) D (+ last row)
+        GDN_WAIT_VM(wait_g34<ActT>());
+        lds_barrier();
         {
-            PHASE_IDS;
-            const int colv = 16 * wv + lr;  // this lane's column within the block
-            // Contractions over d and over tokens run as 16x16x32 products on
-            // accumulator-layout operands: lane group lg supplies K indices
-            // 16 k + 4 lg + (0..3) of two consecutive 16-blocks k, which is a
-            // permutation of the 32 K indices shared by both operands.
-            bf16x8 sb[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) sb[kk] = cat8(to_bf4(s[2 * kk]), to_bf4(s[2 * kk + 1]));
-            f32x4 D[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                // D = U - W S = beta V + LTb V + (-W) S, one accumulator chain
-                const int t0 = 16 * mt + 4 * lg;
-                const bf16x4 vh = ld4(VTh, LT, colv, t0), vl = ld4(VTl, LT, colv, t0);
-                const f32x4 bt = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + t0);
-                f32x4 u;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) u[j] = bt[j] * ((float)vh[j] + (float)vl[j]);
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    u = mma32(ld8(LTb, LT, 16 * mt + lr, 32 * ks + 8 * lg), ld8(VTh, LT, colv, 32 * ks + 8 * lg), u);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    u = mma32(cat8(ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 4 * lg), ld4(Wm, LQK, 16 * mt + lr, 32 * kk + 16 + 4 * lg)),
-                              sb[kk], u);
-                D[mt] = u;
-            }
-            settle4(D);
-            bf16x4 dh[4], dl[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) split4(D[mt], dh[mt], dl[mt]);
-            // O = diag(e^G rq) Q S + diag(k.q) D + P D  (P is lower triangular by
-            // 16-blocks: block pairs below the diagonal, then the diagonal block
-            // alone where it starts a pair)
-            f32x4 qs[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int row = 16 * mt + lr;
-                qs[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    qs[mt] = mma32(cat8(ld4(Qh, LQK, row, 32 * kk + 4 * lg), ld4(Qh, LQK, row, 32 * kk + 16 + 4 * lg)),
-                                   sb[kk], qs[mt]);
-            }
-            settle4(qs);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int row = 16 * mt + lr;
-                const int t0 = 16 * mt + 4 * lg;
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(sc + SC_GAM * CH + t0);
-                const f32x4 rq = *reinterpret_cast<const f32x4*>(sc + SC_RQ * CH + t0);
-                const f32x4 kq = *reinterpret_cast<const f32x4*>(sc + SC_KQ * CH + t0);
-                f32x4 o;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) o[j] = gm[j] * rq[j] * qs[mt][j] + kq[j] * D[mt][j];
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (2 * kk + 1 > mt) continue;
-                    const bf16x8 ph = cat8(ld4(Ph, LT, row, 32 * kk + 4 * lg), ld4(Ph, LT, row, 32 * kk + 16 + 4 * lg));
-                    const bf16x8 pl = cat8(ld4(Pl, LT, row, 32 * kk + 4 * lg), ld4(Pl, LT, row, 32 * kk + 16 + 4 * lg));
-                    const bf16x8 bh = cat8(dh[2 * kk], dh[2 * kk + 1]), bl = cat8(dl[2 * kk], dl[2 * kk + 1]);
-                    o = mma32(ph, bh, o);
-                    o = mma32(ph, bl, o);
-                    o = mma32(pl, bh, o);
-                }
-                if ((mt & 1) == 0) {
-                    if (mt > 0) settle(o);
-                    const bf16x4 ph = ld4(Ph, LT, row, 16 * mt + 4 * lg);
-                    const bf16x4 pl = ld4(Pl, LT, row, 16 * mt + 4 * lg);
-                    o = mma16(ph, dh[mt], o);
-                    o = mma16(ph, dl[mt], o);
-                    o = mma16(pl, dh[mt], o);
-                }
-                o_tile[mt] = o;
-            }
-            o_c0 = c0;
-            o_n = n;
-            // S <- e^{G_last} S + K^T diag(rk e^{G_last - G}) D  (+ the last row exactly)
             bf16x4 wh[4], wl[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                const f32x4 wd = *reinterpret_cast<const f32x4*>(sc + SC_WDR * CH + 16 * kt + 4 * lg);
+                const f32x4 wd = *reinterpret_cast<const f32x4*>(swdr + 16 * kt + 4 * lg);
                 split4(D[kt] * wd, wh[kt], wl[kt]);
             }
             const int tl = n - 1;
@@ -785,9 +973,8 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (16 * kt + 4 * lg + j == tl) dsel = D[kt][j];
-            // the lane of group (tl % 16) / 4 holds D[tl][colv]
             const float dlast = __shfl(dsel, ((tl & 15) >> 2) * 16 + lr, 64);
-            const float glast = sc[SC_GAM * CH + tl];
+            const float glast = sgam[tl];
             bf16x8 wh2[2], wl2[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -800,9 +987,9 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 f32x4 acc = s[dt] * glast;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int k0 = kt_at(row, 32 * kk + 4 * lg), k1 = kt_at(row, 32 * kk + 16 + 4 * lg);
-                    const bf16x8 kh = cat8(*reinterpret_cast<const bf16x4*>(KTh + k0), *reinterpret_cast<const bf16x4*>(KTh + k1));
-                    const bf16x8 kl = cat8(*reinterpret_cast<const bf16x4*>(KTl + k0), *reinterpret_cast<const bf16x4*>(KTl + k1));
+                    const int k0 = ktr_at(row, 32 * kk + 4 * lg), k1 = ktr_at(row, 32 * kk + 16 + 4 * lg);
+                    const bf16x8 kh = cat8(ld4s(KTh + k0), ld4s(KTh + k1));
+                    const bf16x8 kl = cat8(ld4s(KTl + k0), ld4s(KTl + k1));
                     acc = mma32(kh, wh2[kk], acc);
                     acc = mma32(kh, wl2[kk], acc);
                     acc = mma32(kl, wh2[kk], acc);
@@ -817,25 +1004,62 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
                 for (int j = 0; j < 4; ++j) s[dt][j] = fmaf(kv[j], dlast, s[dt][j]);
             }
         }
-        lds_barrier();
-        stage_o();  // P is dead until the next chunk's P3
+        lds_barrier();  // every read of G4 is done
+        fill_g4(ci + 1);
+        // ================================ phase 4: O = diag(e^G rq) Q S + diag(k.q) D + P D
+        f32x4 o_tile[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int row = 16 * mt + lr;
+            const int t0 = 16 * mt + 4 * lg;
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(sgam + t0);
+            const f32x4 rq = *reinterpret_cast<const f32x4*>(srq + t0);
+            const f32x4 kq = *reinterpret_cast<const f32x4*>(skq + t0);
+            f32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = gm[j] * rq[j] * qs[mt][j] + kq[j] * D[mt][j];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (2 * kk + 1 > mt) continue;
+                const bf16x8 ph = cat8(ld4s(Ph + row * LT + 32 * kk + 4 * lg), ld4s(Ph + row * LT + 32 * kk + 16 + 4 * lg));
+                const bf16x8 pl = cat8(ld4s(Pl + row * LT + 32 * kk + 4 * lg), ld4s(Pl + row * LT + 32 * kk + 16 + 4 * lg));
+                const bf16x8 bh = cat8(dh[2 * kk], dh[2 * kk + 1]), bl = cat8(dl[2 * kk], dl[2 * kk + 1]);
+                o = mma32(ph, bh, o);
+                o = mma32(ph, bl, o);
+                o = mma32(pl, bh, o);
+            }
+            if ((mt & 1) == 0) {
+                if (mt > 0) settle(o);
+                const bf16x4 ph = ld4s(Ph + row * LT + 16 * mt + 4 * lg);
+                const bf16x4 pl = ld4s(Pl + row * LT + 16 * mt + 4 * lg);
+                o = mma16(ph, dh[mt], o);
+                o = mma16(ph, dl[mt], o);
+                o = mma16(pl, dh[mt], o);
+            }
+            o_tile[mt] = o;
+        }
+        settle4(o_tile);  // tiles 1 and 3 end with a 16x16x32 product
+        // stage the outputs (the staging tile's last reads, by store_o above,
+        // are ordered before this by the barriers since)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Os[os_at(16 * mt + 4 * lg + j, 16 * wv + lr)] = o_tile[mt][j];
+        o_c0 = c0;
+        o_n = n;
+        lds_barrier();  // the staged outputs; every read of this chunk's P group
+        fill_g3(ci + 1);
     }
-
-    lds_barrier();
     store_o();  // the last chunk's outputs
+    wait_vmem();  // the refills issued past the last chunk have landed before the workgroup ends
 
-    // ---- epilogue: state, then the rolled windows
+    // ---- epilogue: state, then the rolled windows (this block's v channels;
+    // the key head's q/k channels by its first value head's first block: the
+    // prep kernel, the only reader of the old q/k window, has finished)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v] = from_f32<StT>(s[dt][j]);
-    if (tid == 0) sh_last = my_last ? 1 : 0;
-    lds_barrier();
-    // rolled windows: the last three rows of (window ++ sequence) per channel,
-    // each read before its thread writes.  The v channels belong to this
-    // workgroup alone; the q/k channels are shared by the workgroups of the
-    // key head and written by the last of them to arrive, after every other
-    // has consumed its window reads.
     auto roll = [&](int64_t ch) {
         float vw[3];
 #pragma unroll
@@ -848,19 +1072,26 @@ __global__ __launch_bounds__(NTH) void k_gdn_chunk(const ChunkArgs A) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) win[(int64_t)j * C + ch] = from_f32<ActT>(vw[j]);
     };
-    if (sh_last) roll(gq);
     if (has_v) roll(gv);
+    if (h == ki * rr && blk == 0) {
+        const int64_t gq = tid < DK ? (int64_t)ki * DK + tid : (int64_t)A.h_k * DK + (int64_t)ki * DK + (tid - DK);
+        roll(gq);
+    }
 }
 
-#undef PHASE_IDS
-
 template <typename ActT, typename StT>
-hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t s) {
+hipError_t launch_chunk2_t(const ChunkArgs& a, int max_len, hipStream_t s) {
     const int nblk = a.d_v / BVC;
-    const int64_t grid = (int64_t)a.n_seqs * a.h_v * nblk;
-    if (grid == 0) return hipSuccess;
-    if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gdn_chunk<ActT, StT>), dim3((unsigned)grid), dim3(NTH), 0, s, a);
+    const int nck = (max_len + CH - 1) / CH;
+    const int64_t gprep = (int64_t)a.n_seqs * nck * a.h_k;
+    const int64_t groups = (int64_t)a.n_seqs * a.h_k;
+    const int64_t gstate = ((groups + 7) / 8) * 8 * ((int64_t)(a.h_v / a.h_k) * nblk);
+    if (gstate == 0 || nck == 0) return hipSuccess;
+    if (gprep > 0x7fffffff || gstate > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_chunk_prep<ActT>), dim3((unsigned)gprep), dim3(NTH), 0, s, a, nck);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_chunk_state<ActT, StT>), dim3((unsigned)gstate), dim3(NTH), 0, s, a, nck);
     return hipGetLastError();
 }
 
@@ -868,11 +1099,18 @@ hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t s) {
 
 bool chunked_supported(int d_k, int d_v, int chunk) { return d_k == DK && d_v > 0 && d_v % BVC == 0 && chunk == CH; }
 
-hipError_t launch_chunked(const ChunkArgs& a, int d_k, int act_dtype, int state_dtype, hipStream_t s) {
+size_t chunked_workspace_bytes(int h_k, int h_v, int n_seqs, int64_t n_rows) {
+    const int64_t slots = (int64_t)n_seqs + (n_rows + CH - 1) / CH;
+    return (size_t)slots * ((size_t)h_k * KREC_BYTES + (size_t)h_v * VREC_BYTES);
+}
+
+hipError_t launch_chunked(const ChunkArgs& a, int d_k, int act_dtype, int state_dtype, int max_len, hipStream_t s) {
     if (!chunked_supported(d_k, a.d_v, CH)) return hipErrorInvalidValue;
     if (act_dtype == GDN_BF16)
-        return state_dtype == GDN_BF16 ? launch_chunk_t<bf16_t, bf16_t>(a, s) : launch_chunk_t<bf16_t, float>(a, s);
-    return state_dtype == GDN_BF16 ? launch_chunk_t<float, bf16_t>(a, s) : launch_chunk_t<float, float>(a, s);
+        return state_dtype == GDN_BF16 ? launch_chunk2_t<bf16_t, bf16_t>(a, max_len, s)
+                                       : launch_chunk2_t<bf16_t, float>(a, max_len, s);
+    return state_dtype == GDN_BF16 ? launch_chunk2_t<float, bf16_t>(a, max_len, s)
+                                   : launch_chunk2_t<float, float>(a, max_len, s);
 }
 
 }  // namespace gdn

@@ -79,6 +79,7 @@ struct ChunkArgs {
     int32_t* err;
     int32_t h_k, h_v, d_v;
     float scale, eps;
+    void* workspace;  // chunk records (chunked_workspace_bytes), 256-byte aligned
 };
 
 // Each returns hipSuccess or the launch error.
@@ -87,7 +88,8 @@ hipError_t launch_conv(const ConvArgs& a, int act_dtype, int y_dtype, int max_se
 hipError_t launch_verify(const VerifyArgs& a, int d_k, int act_dtype, int state_dtype, int layout,
                          hipStream_t s);
 hipError_t launch_restore(const RestoreArgs& a, int act_dtype, int state_dtype, hipStream_t s);
-hipError_t launch_chunked(const ChunkArgs& a, int d_k, int act_dtype, int state_dtype, hipStream_t s);
+hipError_t launch_chunked(const ChunkArgs& a, int d_k, int act_dtype, int state_dtype, int max_len, hipStream_t s);
+size_t chunked_workspace_bytes(int h_k, int h_v, int n_seqs, int64_t n_rows);
 // One launch running the token-by-token workgroups of `s` and the verify
 // workgroups of `v` (either part may be empty: n_seqs or n_req == 0).
 hipError_t launch_mixed(const SeqArgs& s, const VerifyArgs& v, int d_k, int act_dtype, int state_dtype, int layout,

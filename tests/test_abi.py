@@ -192,10 +192,10 @@ def test_chunked_validation(so, L):
     d = _dims(L)
     a = _seq_args(L, d)
 
-    def call(chunk=64, ws_bytes=0, dims=d, x=a["x"], x_stride=a["x_stride"], conv=a["conv"], o=a["o"]):
+    def call(chunk=64, ws=None, ws_bytes=0, dims=d, x=a["x"], x_stride=a["x_stride"], conv=a["conv"], o=a["o"]):
         return so.gdn_chunked_prefill(ctypes.byref(dims), ctypes.byref(a["params"]), x, x_stride, a["a"],
                                       a["b"], a["ab_stride"], ctypes.byref(a["batch"]), conv, a["state"],
-                                      o, chunk, None, ws_bytes, None, None)
+                                      o, chunk, ws, ws_bytes, None, None)
     assert call(chunk=0) == 1
     assert call(chunk=32) == 2
     assert call(dims=_dims(L, d_k=64)) == 2
@@ -206,9 +206,26 @@ def test_chunked_validation(so, L):
     assert call(conv=L.GdnConvPool(FAKE + 8, 3 * C, 3, 4, FAKE)) == 1
     assert call(conv=L.GdnConvPool(FAKE, 3 * C + 4, 3, 4, FAKE)) == 1
     assert call(o=FAKE + 4) == 1
-    out = ctypes.c_size_t(123)
-    assert so.gdn_chunked_workspace_bytes(ctypes.byref(d), 4, 32768, 64, ctypes.byref(out)) == 0
-    assert out.value == 0
+    # the workspace: one slot of records per sequence plus one per 64 rows
+    def ws(n_seqs, n_rows, dims=d):
+        out = ctypes.c_size_t(123)
+        assert so.gdn_chunked_workspace_bytes(ctypes.byref(dims), n_seqs, n_rows, 64, ctypes.byref(out)) == 0
+        return out.value
+    slot = ws(1, 0)
+    assert slot > 0 and slot % 256 == 0
+    assert ws(4, 32768) == (4 + 512) * slot
+    assert ws(2, 16) == 3 * slot and ws(2, 129) == 5 * slot and ws(0, 0) == 0
+    # key-head and value-head records both count
+    assert ws(1, 0, _dims(L, h_v=16)) < slot and ws(1, 0, _dims(L, h_k=8)) < slot
+    out = ctypes.c_size_t(0)
+    assert so.gdn_chunked_workspace_bytes(ctypes.byref(d), -1, 16, 64, ctypes.byref(out)) == 1
+    assert so.gdn_chunked_workspace_bytes(ctypes.byref(d), 2, 16, 32, ctypes.byref(out)) == 2
+    # the batch of _seq_args (2 sequences, 16 rows) needs three slots: short,
+    # missing or misaligned workspaces are argument errors
+    need = ws(2, 16)
+    assert call(ws=None, ws_bytes=need) == 1
+    assert call(ws=FAKE, ws_bytes=need - 1) == 1
+    assert call(ws=FAKE + 16, ws_bytes=need) == 1
 
 
 def test_prefill_path_selection(so, L):

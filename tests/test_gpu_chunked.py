@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import gdn_workloads as wk
-from gpu_util import DEV, gdn, host, max_slice_rel_S, max_slice_rel_o, oracle_seq, run_seq
+from gpu_util import DEV, dev, gdn, host, max_slice_rel_S, max_slice_rel_o, oracle_seq, run_seq
 
 pytestmark = pytest.mark.gpu
 
@@ -162,6 +162,29 @@ def test_chunked_padding_and_bad_page(ora):
     for p in (1, 3):
         assert float(state.buf[p].abs().sum()) == 0.0 and float(conv.buf[p].float().abs().sum()) == 0.0
     assert int(conv.sync.abs().sum()) == 0
+
+
+def test_chunked_max_seqlen_bounds_the_records(ora):
+    """batch.max_seqlen sizes the record pass (ceil(max_seqlen / 64) chunks per
+    sequence): a sequence longer than it is skipped, leaves its page and rows
+    untouched and raises GDN_DEVERR_BATCH; the others match the oracle."""
+    g = gdn()
+    wl = _small((130, 64, 70), seed=50)
+    inp = wk.make_sequence_inputs(wl)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o, conv, state = run_seq(wl, inp, chunk=64, err=err, max_seqlen=100)
+    assert int(err.item()) == g.GDN_DEVERR_BATCH
+    o_ref, win_ref, S_ref = oracle_seq(ora, wl, inp)
+    cu = inp["cu_seqlens"]
+    oh, Sh, Ch = host(o), host(state.buf), host(conv.buf)
+    assert np.isnan(oh[:130]).all()
+    np.testing.assert_array_equal(Sh[0], host(dev(inp["S0"][0], state.buf.dtype)))
+    np.testing.assert_array_equal(Ch[0][:wl.conv_w - 1], host(dev(inp["window0"][0], conv.buf.dtype)))
+    for s in (1, 2):
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        assert max_slice_rel_o(oh[rows], o_ref[rows], [0, cu[s + 1] - cu[s]]) <= TOL, s
+        assert max_slice_rel_S(Sh[s:s + 1], S_ref[s:s + 1]) <= TOL, s
+        np.testing.assert_array_equal(Ch[s][:wl.conv_w - 1], win_ref[s])
 
 
 @pytest.mark.parametrize("h_k,h_v", [(4, 4), (2, 8)])
