@@ -244,7 +244,7 @@ int32_t gdn_recurrent_seq_noalloc(const gdn_dims* dims, const gdn_params* params
  * x rows and conv-window rows are read, and o rows written, as 16-byte
  * vectors: x, conv.base and o must be 16-byte aligned and x_stride and
  * conv.page_stride multiples of 16 bytes' worth of elements (8 bf16 or 4
- * fp32), else GDN_ERR_ARG. */
+ * fp32), and x_stride and h_v * d_v at most 2^24 elements, else GDN_ERR_ARG. */
 int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* params,
                             const void* x, int64_t x_stride,
                             const void* a, const void* b, int64_t ab_stride,

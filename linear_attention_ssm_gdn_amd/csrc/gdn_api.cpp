@@ -240,6 +240,8 @@ GDN_EXPORT int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* p
     if (batch->n_seqs > 0 && (!aligned(x, 16) || x_stride % vec != 0 || !aligned(conv.base, 16) ||
                               conv.page_stride % vec != 0 || !aligned(o, 16)))
         return GDN_ERR_ARG;
+    // one chunk's x rows and output rows are addressed with 32-bit offsets
+    if (x_stride > (int64_t)1 << 24 || (int64_t)dims->h_v * dims->d_v > (int64_t)1 << 24) return GDN_ERR_ARG;
     size_t need = 0;
     if ((st = gdn_chunked_workspace_bytes(dims, batch->n_seqs, batch->n_rows, chunk, &need)) != GDN_OK) return st;
     if (ws_bytes < need || (need > 0 && (!workspace || !aligned(workspace, 256)))) return GDN_ERR_ARG;

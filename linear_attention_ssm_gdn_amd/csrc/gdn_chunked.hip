@@ -51,6 +51,7 @@ constexpr int NTH = 256;       // threads per workgroup
 constexpr int LQK = 136;       // bf16 row stride of token-major [64][128] arrays
 constexpr int LT = 72;         // bf16 row stride of [..][64] arrays
 constexpr int LAF = 68;        // fp32 row stride of A [64][64]
+constexpr int L80 = 80;        // bf16 row stride of the swizzled [64][80] arrays (sw80)
 
 // LDS of the prep kernel (bytes): token-major q and k hi/lo; after the
 // products the k regions hold T and LTbg, the q-lo region A and then -W.
@@ -83,14 +84,21 @@ enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
 // wait states: while 16x16x32 reads failed in nearly every launch, the
 // states, which depend on every UT solve, never differed.
 #define GDN_SETTLE_NOPS "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-__device__ __forceinline__ void settle(f32x4& a) { asm volatile(GDN_SETTLE_NOPS : "+a"(a)); }
 __device__ __forceinline__ void settle(f32x4& a, f32x4& b) { asm volatile(GDN_SETTLE_NOPS : "+a"(a), "+a"(b)); }
-__device__ __forceinline__ void settle4(f32x4 (&a)[4]) {
-    asm volatile(GDN_SETTLE_NOPS : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
-}
 __device__ __forceinline__ void settle8(f32x4 (&a)[8]) {
     asm volatile(GDN_SETTLE_NOPS : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]),
                  "+a"(a[6]), "+a"(a[7]));
+}
+// The same wait on accumulators held in architectural registers (kernels
+// whose register budget is shared by two waves per SIMD keep MFMA results
+// there rather than split the budget with accumulator registers).
+__device__ __forceinline__ void settle_v(f32x4& a) { asm volatile(GDN_SETTLE_NOPS : "+v"(a)); }
+__device__ __forceinline__ void settle4_v(f32x4 (&a)[4]) {
+    asm volatile(GDN_SETTLE_NOPS : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+}
+__device__ __forceinline__ void settle8_v(f32x4 (&a)[8]) {
+    asm volatile(GDN_SETTLE_NOPS : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                 "+v"(a[6]), "+v"(a[7]));
 }
 
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
@@ -184,13 +192,14 @@ constexpr int KR_RQ = KR_KLAST + DK * 4;         // fp32 [64]: rq (with the outp
 constexpr int KR_KQ = KR_RQ + CH * 4;            // fp32 [64]: rq rk (q.k) of each row
 constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 55296
 constexpr int VR_WM = 0;                         // bf16 [64][LQK]: -W
-constexpr int VR_LTB = VR_WM + CH * LQK * 2;     // bf16 [64][64] (sw64): (T - I) diag(beta)
-constexpr int VR_BETA = VR_LTB + CH * CH * 2;    // fp32 [64]
+constexpr int VR_LTB = VR_WM + CH * LQK * 2;     // bf16 [64][80] (sw80): (T - I) diag(beta)
+constexpr int VR_BETA = VR_LTB + CH * L80 * 2;   // fp32 [64]
 constexpr int VR_PH = VR_BETA + CH * 4;          // bf16 [64][LT]: P hi (tiles on or below the diagonal)
 constexpr int VR_PL = VR_PH + CH * LT * 2;       // bf16 [64][LT]: P lo
-constexpr int VR_GAM = VR_PL + CH * LT * 2;      // fp32 [64]: e^G
+constexpr int VR_GRQ = VR_PL + CH * LT * 2;      // fp32 [64]: e^G rq
+constexpr int VR_GAM = VR_GRQ + CH * 4;          // fp32 [64]: e^G
 constexpr int VR_WDR = VR_GAM + CH * 4;          // fp32 [64]: rk e^{G_last - G}, 0 for the last row
-constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 44800, a multiple of 256
+constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 47104, a multiple of 256
 static_assert(VREC_BYTES % 256 == 0 && KREC_BYTES % 256 == 0, "records keep 256-byte alignment");
 static_assert(VR_WDR + CH * 4 <= VREC_BYTES && KREC_BYTES % 256 == 0 && VREC_BYTES % 256 == 0, "records");
 
@@ -201,15 +210,16 @@ __device__ __forceinline__ int64_t chunk_slot(int seq, int r0, int c) { return (
 // read the lanes {0-7, 24-31} and {8-15, 16-23} of each half wave (measured
 // with the bank-conflict counter).  An MFMA operand read takes row lr = lane
 // & 15 and column group lg = lane >> 4.
-//  - [rows][LT] (k^T, P): 8-byte reads of rows 36 words apart fill all 64
-//    banks for every 32 lanes.
-//  - sw64 ([rows][64], LTb and the v tile): rows 128 bytes apart, the 16-byte
-//    column group XORed with ((row >> 1) & 7) ^ ((row >> 4) & 1); conflict
-//    free for both 8- and 16-byte operand reads (16 rows of one XOR pattern
-//    per read), and at most 2-way for the v tile's 8-byte column writes.
+//  - [rows][LT] (k^T, P) and [rows][LQK] (q, -W): 8-byte reads of rows 36
+//    (68) words apart fill all 64 banks for every 32 lanes.
+//  - sw80 ([rows][80], LTb and the v tile, read both 8 and 16 bytes wide):
+//    rows 160 bytes apart, the 16-byte column group XORed with a 2-bit
+//    function of row & 15 (3 (row & 1) ^ 2 ((row >> 3) & 1)); conflict free
+//    for both read widths, and the XOR leaves the column bits that the
+//    unrolled tiles step through alone, so their offsets stay immediates.
 __device__ __forceinline__ int ktr_at(int row, int col) { return row * LT + col; }
-__device__ __forceinline__ int sw64(int row, int col) {
-    return row * CH + (col ^ ((((row >> 1) & 7) ^ ((row >> 4) & 1)) << 3));
+__device__ __forceinline__ int sw80(int row, int col) {
+    return row * L80 + (col ^ (((3 * (row & 1)) ^ (((row >> 3) & 1) << 1)) << 3));
 }
 
 // Copy BYTES (a multiple of 64) from global memory into LDS with direct
@@ -219,15 +229,25 @@ __device__ __forceinline__ int sw64(int row, int col) {
 // asynchronous: the reader waits for them (vector-memory counter) and a
 // barrier publishes them.
 constexpr int copy_instrs(int bytes) { return (bytes / 64 + 63) / 64; }
-// One 16-byte direct global->LDS load per lane into LDS byte address
+// One 16-byte direct global->LDS load per lane from sbase + voff (sbase
+// wave-uniform, in scalar registers; voff per lane) into LDS byte address
 // lds_base + 16 lane, written as an instruction the compiler does not see as
 // an LDS write: it would otherwise order every later LDS read after every
 // such load in flight (a full vector-memory wait at each read), while the
 // kernel orders them itself with counted waits and barriers.  The load has
 // no result register; M0 takes the LDS base one wait state before the load.
-__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_base)
                  : "memory", "m0");
+}
+// A wave-uniform pointer moved to scalar registers (the builtin returns a
+// signed 32-bit value: each half is taken back as unsigned before widening).
+template <typename T> __device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>((uintptr_t)((hi << 32) | lo));
 }
 template <int BYTES>
 __device__ __forceinline__ void copy_to_lds(const unsigned char* src, unsigned char* dst, int wv, int lane) {
@@ -235,10 +255,11 @@ __device__ __forceinline__ void copy_to_lds(const unsigned char* src, unsigned c
     constexpr int PW = BYTES / 64;  // pieces per wave
     const int w0 = wv * PW;
     const uint32_t base = (uint32_t)(uintptr_t)dst + (uint32_t)w0 * 16u;
+    const unsigned char* sw = src + (int64_t)w0 * 16;
 #pragma unroll
     for (int j = 0; j < copy_instrs(BYTES); ++j) {
-        const int p = 64 * j + lane;
-        if (p < PW) dma16(src + ((int64_t)w0 + p) * 16, __builtin_amdgcn_readfirstlane(base + 1024u * j));
+        if (64 * j + lane < PW)
+            dma16(uniform_ptr(sw + 1024 * j), 16u * (uint32_t)lane, __builtin_amdgcn_readfirstlane(base + 1024u * j));
     }
 }
 // The same copy through registers, LDS to global (16 bytes per thread and pass).
@@ -474,6 +495,7 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             sc[SC_WDR * CH + t] = wdr;
             float* vs = reinterpret_cast<float*>(vrec);
             vs[VR_BETA / 4 + t] = beta;
+            vs[VR_GRQ / 4 + t] = gam * sc[SC_RQ * CH + t];
             vs[VR_GAM / 4 + t] = gam;
             vs[VR_WDR / 4 + t] = wdr;
         }
@@ -570,7 +592,7 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             const u32x4 og = {pack_bf2(lt[0] * g0[0], lt[1] * g0[1]), pack_bf2(lt[2] * g0[2], lt[3] * g0[3]),
                               pack_bf2(lt[4] * g1[0], lt[5] * g1[1]), pack_bf2(lt[6] * g1[2], lt[7] * g1[3])};
             *reinterpret_cast<u32x4*>(LTbg + t * LT + s0) = og;
-            *reinterpret_cast<u32x4*>(vrec + VR_LTB + sw64(t, s0) * 2) = ob;
+            *reinterpret_cast<u32x4*>(vrec + VR_LTB + sw80(t, s0) * 2) = ob;
         }
         // a full barrier: every thread's k^T stores (long since issued) have
         // completed, so the W phase may read them back (one CU, one L1)
@@ -611,78 +633,56 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
 }
 
 // ---------------------------------------------------------------- state
-// LDS of the state kernel: four operand groups, each refilled for the next
-// chunk right after its last read in this one, the v tile, the output
-// staging tile and the v taps.
+// k_chunk_state runs 8 waves per workgroup, two per SIMD.  Waves 0-3 (the
+// chain) hold the state and do only what the next chunk's state depends on;
+// waves 4-7 (the output side) run the v conv, Q S and the outputs from the
+// state and D that the chain hands over in LDS, so the two interleave on
+// every SIMD.  Wave w of either side owns value columns 16 (w & 3) .. +15 of
+// the block.  A chunk takes two steps, each closed by a barrier:
+//   step A(c)  chain:  refill G4 <- chunk c;  D(c) = U - W S(c)
+//              output: x rows of chunk c+1 -> registers;  Q S(c);  O(c-1)
+//   step B(c)  chain:  refill G1 <- chunk c+1;  D(c) -> LDS;  S(c+1);
+//                      hi(S(c+1)) -> LDS
+//              output: v conv of chunk c+1 -> LDS;  refill G2 <- c+1, G3 <- c
+// and O of the last chunk after the loop.  Each refill is issued after the
+// barrier that ends the last read of its buffer and is awaited (vector
+// memory count 0 in the waves that issued it) before the barrier that
+// precedes its first read.
 //   G1 (D = U - W S): -W, LTb, beta         <- value-head record [0, VR_PH)
 //   G2 (Q S):         q hi                  <- key-head record [0, KR_KTH)
 //   G4 (S update):    k^T hi/lo, klast      <- key-head record [KR_KTH, KR_RQ)
-//   G3 (P D, output): P hi/lo, gam, wdr     <- value-head record [VR_PH, VR_WDR + 256)
-//                     rq, kq                <- key-head record [KR_RQ, KREC_BYTES)
-constexpr int G1_BYTES = VR_PH;                        // 25856
+//                     gam, wdr              <- value-head record [VR_GAM, VR_WDR + 256)
+//   G3 (P D, output): P hi/lo, e^G rq       <- value-head record [VR_PH, VR_GAM)
+//                     kq                    <- key-head record [KR_KQ, KREC_BYTES)
+constexpr int SNTH = 512;                              // threads of the state kernel
+constexpr int G1_BYTES = VR_PH;                        // 27904
 constexpr int G2_BYTES = KR_KTH;                       // 17408
-constexpr int G4_BYTES = KR_RQ - KR_KTH;               // 37376
-constexpr int G3V_BYTES = VR_WDR + CH * 4 - VR_PH;     // 18944
-constexpr int G3K_BYTES = KREC_BYTES - KR_RQ;          // 512
-constexpr int G3_BYTES = G3V_BYTES + G3K_BYTES;        // 19456
-constexpr int S_G1 = 0;
-constexpr int S_G2 = S_G1 + G1_BYTES;
-constexpr int S_G4 = S_G2 + G2_BYTES;
-constexpr int S_G3 = S_G4 + G4_BYTES;
-constexpr int S_VTH = S_G3 + G3_BYTES;
-constexpr int S_VTL = S_VTH + BVC * CH * 2;
-constexpr int S_OS = S_VTL + BVC * CH * 2;
-constexpr int S_WV = S_OS + CH * BVC * 4;
-constexpr int S_LDS = S_WV + BVC * 4 * 4;
+constexpr int G4K_BYTES = KR_RQ - KR_KTH;              // 37376
+constexpr int G4V_BYTES = VR_WDR + CH * 4 - VR_GAM;    // 512
+constexpr int G3V_BYTES = VR_GAM - VR_PH;              // 18688
+constexpr int G3K_BYTES = KREC_BYTES - KR_KQ;          // 256
+constexpr int XCH_BYTES = 4 * 4 * 64 * 16;             // one 16-byte vector per (chain wave, tile, lane)
+constexpr int S_LDS = G1_BYTES + G2_BYTES + G4K_BYTES + G4V_BYTES + G3V_BYTES + G3K_BYTES + 2 * BVC * L80 * 2 +
+                      2 * XCH_BYTES + BVC * 4 * 4;
 static_assert(S_LDS <= 160 * 1024, "state kernel LDS");
-// Load instructions every wave issues per refill; a wait for a group counts
-// the loads issued after it (other memory operations issued after it only
-// make the wait stronger).
-// The next chunk's v rows (67 rows of the block's 64 channels) go with G1.
-constexpr int XS_ROWS = CH + 3;
-// Staged row r sits at row r ^ ((r >> 2) & 1): the v conv reads rows 4 apart
-// in the two halves of 32 lanes, which then land in opposite bank halves of
-// a 16-bit row (an involution on 0..66).
-__device__ __forceinline__ int xs_row(int r) { return r ^ ((r >> 2) & 1); }
-// Output staging [64][64] fp32, column XOR 16 ((t >> 2) & 3): conflict free
-// for the tile writes (4-byte, rows 4 lg + j) and the 16-byte row reads.
-__device__ __forceinline__ int os_at(int t, int c) { return t * BVC + (c ^ (((t >> 2) & 3) << 4)); }
 // The v taps of channel c sit at 16-byte slot 16 (c & 3) + c / 4, so the
 // 16-byte reads of channels 4 vc4 + e (vc4 = 0..15) hit 16 different slots.
 __device__ __forceinline__ int tap_at(int c) { return ((c & 3) << 4) | (c >> 2); }
-template <typename ActT> constexpr int xs_bytes() { return XS_ROWS * BVC * (int)sizeof(ActT); }
-template <typename ActT>
-constexpr int N1_of() { return copy_instrs(G1_BYTES) + copy_instrs(xs_bytes<ActT>()); }
-constexpr int N2 = copy_instrs(G2_BYTES), N4 = copy_instrs(G4_BYTES);
-constexpr int N3 = copy_instrs(G3V_BYTES) + copy_instrs(G3K_BYTES);
-// Chunk c issues G1(c+1) after phase 1, G2(c+1) after phase 2, G4(c+1)
-// after the state update and G3(c+1) after the output.  Before phase 1 of
-// chunk c the loads issued after G1(c) are G2(c), G4(c), G3(c); before
-// phase 2, G4(c), G3(c), G1(c+1); before the state update (which reads G4(c)
-// and G3(c)), G1(c+1), G2(c+1).  In-order completion of loads makes "at most
-// that many outstanding" mean "G(c) has landed".
-constexpr int WAIT_G1 = N2 + N4 + N3;
-template <typename ActT> constexpr int wait_g2() { return N4 + N3 + N1_of<ActT>(); }
-template <typename ActT> constexpr int wait_g34() { return N1_of<ActT>() + N2; }
-static_assert(wait_g2<float>() <= 63 && WAIT_G1 <= 63 && wait_g34<float>() <= 63, "vmcnt field");
 
 #define GDN_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory")
 
 template <typename ActT, typename StT>
-__global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const int nck) {
-    // One LDS object per operand group: the compiler's wait insertion tells
-    // direct global->LDS loads into one object from reads of another only
-    // when they are distinct objects (else every LDS read waits for every
-    // load in flight).
+__global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_chunk_state(const ChunkArgs A, const int nck) {
+    // One LDS object per operand group and hand-over buffer.
     __shared__ __attribute__((aligned(16))) unsigned char g1s[G1_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char g2s[G2_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char g4s[G4_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char g3s[G3_BYTES];
-    __shared__ __attribute__((aligned(16))) __bf16 VTh[BVC * CH];  // v^T hi, sw64
-    __shared__ __attribute__((aligned(16))) __bf16 VTl[BVC * CH];  // v^T lo, sw64
-    __shared__ __attribute__((aligned(16))) float Os[CH * BVC];     // output staging, os_at
+    __shared__ __attribute__((aligned(16))) unsigned char g4s[G4K_BYTES + G4V_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char g3s[G3V_BYTES + G3K_BYTES];
+    __shared__ __attribute__((aligned(16))) __bf16 VTh[BVC * L80];  // v^T hi, sw80
+    __shared__ __attribute__((aligned(16))) __bf16 VTl[BVC * L80];  // v^T lo, sw80
+    __shared__ __attribute__((aligned(16))) f32x4 Dx[4 * 4 * 64];   // D: (chain wave, row tile, lane)
+    __shared__ __attribute__((aligned(16))) bf16x8 Sx[4 * 4 * 64];  // hi(S) operand: (chain wave, k step, lane)
     __shared__ __attribute__((aligned(16))) float wv4[BVC * 4];
-    __shared__ __attribute__((aligned(16))) unsigned char xs[xs_bytes<ActT>()];
     __shared__ int sh_last;
     const __bf16* Wm = reinterpret_cast<const __bf16*>(g1s + VR_WM);
     const __bf16* LTb = reinterpret_cast<const __bf16*>(g1s + VR_LTB);
@@ -691,8 +691,18 @@ __global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const in
     const __bf16* KTh = reinterpret_cast<const __bf16*>(g4s);
     const __bf16* KTl = reinterpret_cast<const __bf16*>(g4s + DK * LT * 2);
     const float* klast = reinterpret_cast<const float*>(g4s + 2 * DK * LT * 2);
+    const float* sgam4 = reinterpret_cast<const float*>(g4s + G4K_BYTES);
+    const float* swdr = reinterpret_cast<const float*>(g4s + G4K_BYTES + CH * 4);
+    const __bf16* Ph = reinterpret_cast<const __bf16*>(g3s);
+    const __bf16* Pl = reinterpret_cast<const __bf16*>(g3s + VR_PL - VR_PH);
+    const float* sgrq = reinterpret_cast<const float*>(g3s + VR_GRQ - VR_PH);
+    const float* skq = reinterpret_cast<const float*>(g3s + G3V_BYTES);
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wvs = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool chain = wvs < 4;
+    const int w4 = wvs & 3;    // column tile of this wave, either side
+    const int t4 = tid & 255;  // thread index within its side
     const int lr = lane & 15, lg = lane >> 4;
     const int nblk = A.d_v / BVC;
     const int rr = A.h_v / A.h_k;
@@ -711,8 +721,8 @@ __global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const in
     const int h = ki * rr + mem / nblk;
     // the v-th group row takes the v-th longest sequence (ties by position)
     int seq = grp / A.h_k;
-    if (A.n_seqs > 1 && A.n_seqs <= NTH) {
-        int* len = reinterpret_cast<int*>(Os);
+    if (A.n_seqs > 1 && A.n_seqs <= 256) {
+        int* len = reinterpret_cast<int*>(Dx);
         const int ns = A.n_seqs;
         int my = 0;
         if (tid < ns) {
@@ -732,6 +742,7 @@ __global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const in
         seq = sh_last;
         __syncthreads();
     }
+    seq = __builtin_amdgcn_readfirstlane(seq);
     const int colbase = blk * BVC;
     const int64_t C = 2 * (int64_t)A.h_k * DK + (int64_t)A.h_v * A.d_v;
 
@@ -760,101 +771,67 @@ __global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const in
     auto vrec = [&](int c) {
         return ws + chunk_slot(seq, r0, c) * slot_bytes + (int64_t)A.h_k * KREC_BYTES + (int64_t)h * VREC_BYTES;
     };
-    const int wvs = __builtin_amdgcn_readfirstlane(wv);
-    // Refills for chunk c; past the last chunk they reload the last chunk's
-    // records (nothing reads them) so that every chunk issues the same loads.
-    const ActT* __restrict__ Xv = static_cast<const ActT*>(A.x) + 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase;
-    // G1 of chunk c, then chunk c's v rows c0-3 .. c0+63 (c >= 1, so all from x;
-    // rows past the sequence clamped to its last), 16-byte pieces, a quarter per wave
-    auto fill_g1 = [&](int c) {
-        copy_to_lds<G1_BYTES>(vrec(c < nch ? c : nch - 1), g1s, wvs, lane);
-        constexpr int PPR = BVC * (int)sizeof(ActT) / 16;   // pieces per row
-        constexpr int PW = xs_bytes<ActT>() / 64;           // pieces per wave
-        const int w0 = wvs * PW;
-        const uint32_t base = (uint32_t)(uintptr_t)xs + (uint32_t)w0 * 16u;
-        const int cs = (c < nch ? c : nch - 1) * CH - 3;
-#pragma unroll
-        for (int j = 0; j < copy_instrs(xs_bytes<ActT>()); ++j) {
-            const int p = w0 + 64 * j + lane;
-            if (64 * j + lane < PW) {
-                const int r = xs_row(p / PPR), q = p % PPR;
-                int t = cs + r;
-                t = t < 0 ? 0 : (t < T ? t : T - 1);
-                dma16(Xv + (int64_t)(r0 + t) * A.x_stride + q * (16 / (int)sizeof(ActT)),
-                      __builtin_amdgcn_readfirstlane(base + 1024u * j));
-            }
-        }
+    // refills, each split over the four waves of the side that reads it
+    auto fill_g1 = [&](int c) { copy_to_lds<G1_BYTES>(vrec(c), g1s, w4, lane); };
+    auto fill_g4 = [&](int c) {
+        copy_to_lds<G4K_BYTES>(krec(c) + KR_KTH, g4s, w4, lane);
+        copy_to_lds<G4V_BYTES>(vrec(c) + VR_GAM, g4s + G4K_BYTES, w4, lane);
     };
-    auto fill_g2 = [&](int c) { copy_to_lds<G2_BYTES>(krec(c < nch ? c : nch - 1), g2s, wvs, lane); };
-    auto fill_g4 = [&](int c) { copy_to_lds<G4_BYTES>(krec(c < nch ? c : nch - 1) + KR_KTH, g4s, wvs, lane); };
+    auto fill_g2 = [&](int c) { copy_to_lds<G2_BYTES>(krec(c), g2s, w4, lane); };
     auto fill_g3 = [&](int c) {
-        const int cc = c < nch ? c : nch - 1;
-        copy_to_lds<G3V_BYTES>(vrec(cc) + VR_PH, g3s, wvs, lane);
-        copy_to_lds<G3K_BYTES>(krec(cc) + KR_RQ, g3s + G3V_BYTES, wvs, lane);
+        copy_to_lds<G3V_BYTES>(vrec(c) + VR_PH, g3s, w4, lane);
+        copy_to_lds<G3K_BYTES>(krec(c) + KR_KQ, g3s + G3V_BYTES, w4, lane);
     };
 
-    // ---- state: wave w holds S[16 dt + 4 lg + j][16 w + lr], dt = 0..7
-    StT* __restrict__ Sg = static_cast<StT*>(A.state) + (int64_t)page * A.state_page_stride +
-                           (int64_t)h * DK * A.d_v + colbase + 16 * wv + lr;
-    f32x4 s[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s[dt][j] = init ? to_f32(Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v]) : 0.0f;
-
-    // the first chunk's operands, in the order a chunk issues them
-    fill_g1(0);
-    fill_g2(0);
-    fill_g4(0);
-    fill_g3(0);
-
-    // ---- v taps: channel tid of the block
     const ActT* __restrict__ X = static_cast<const ActT*>(A.x);
     ActT* __restrict__ win = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
     const ActT* Wc = static_cast<const ActT*>(A.conv_w);
-    const bool has_v = tid < BVC;
-    const int64_t gv = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + tid;
-    if (has_v) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wv4[4 * tap_at(tid) + e] = to_f32(Wc[gv * 4 + e]);
-    }
-    float* __restrict__ Og = A.o + (int64_t)r0 * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase;
-    const int64_t o_stride = (int64_t)A.h_v * A.d_v;
 
-    // a thread's v rows of a chunk: channels 4 vc4 .. +3 (vc4 = tid & 15, so
-    // the 16 lanes of a row group read one contiguous row), tokens 4 tq4 ..
-    // +3 (tq4 = tid >> 4) and the three before them
+    // ---- chain: wave w holds S[16 dt + 4 lg + j][16 w + lr], dt = 0..7
+    StT* __restrict__ Sg = static_cast<StT*>(A.state) + (int64_t)page * A.state_page_stride +
+                           (int64_t)h * DK * A.d_v + colbase + 16 * w4 + lr;
+    f32x4 s[8];
+    // the hi(S) operand of the chain's products and of the output side's Q S
+    auto publish_s = [&](bf16x8 (&sb)[4]) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            sb[kk] = cat8(to_bf4(s[2 * kk]), to_bf4(s[2 * kk + 1]));
+            Sx[(w4 * 4 + kk) * 64 + lane] = sb[kk];
+        }
+    };
+    bf16x8 sb[4];
+
+    // ---- output side: v rows and taps; thread t4 takes channels 4 vc4 .. +3
+    // (vc4 = t4 & 15) and tokens 4 tq4 .. +3 (tq4 = t4 >> 4) of a chunk
+    const int vc4 = t4 & 15, tq4 = t4 >> 4;
+    const int64_t gv = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + t4;  // channel t4 (< 64)
     RowVec<ActT, 4> nvv[7];
-    auto prefetch_v = [&](int cs) {
-        const int tq4 = tid >> 4;
-        const int64_t gv4 = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + 4 * (tid & 15);
+    auto load_v = [&](int cs) {
+        const int64_t gv4 = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + 4 * vc4;
+        // rows cs - 3 .. cs + 63 (clamped to the sequence) as 32-bit offsets
+        // from a wave-uniform base row
+        const int tb = cs >= 3 ? cs - 3 : 0;
+        const ActT* xb = uniform_ptr(X + (int64_t)(r0 + tb) * A.x_stride + 2 * (int64_t)A.h_k * DK +
+                                     (int64_t)h * A.d_v + colbase);
 #pragma unroll
         for (int j = 0; j < 7; ++j) {
             const int t = cs + 4 * tq4 - 3 + j;
             if (t >= 0)
-                nvv[j].load(X + (int64_t)(r0 + (t < T ? t : T - 1)) * A.x_stride + gv4);
+                nvv[j].load(xb + (uint32_t)(((t < T ? t : T - 1) - tb) * (int)A.x_stride + 4 * vc4));
             else if (init)
                 nvv[j].load(win + (int64_t)(3 + t) * C + gv4);
             else
                 nvv[j].zero();
         }
     };
-    // v conv of a chunk from its rows (prefetched into registers for the
-    // first chunk, staged in LDS for the others): 4 channels x 4 tokens per
-    // thread, stored transposed (hi/lo)
-    auto conv_v = [&](bool from_lds) {
-        const int tq4 = tid >> 4, vc4 = tid & 15;
-        if (from_lds) {
-#pragma unroll
-            for (int j = 0; j < 7; ++j)
-                nvv[j].load(reinterpret_cast<const ActT*>(xs) + xs_row(4 * tq4 + j) * BVC + 4 * vc4);
-        }
+    // v conv + SiLU of a chunk from its rows, stored transposed (hi/lo)
+    auto conv_v = [&]() {
         u32x2 th[4], tl[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int col = 4 * vc4 + e;
-            const f32x4 w4 = *reinterpret_cast<const f32x4*>(wv4 + 4 * tap_at(col));
-            const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
+            const f32x4 w4v = *reinterpret_cast<const f32x4*>(wv4 + 4 * tap_at(col));
+            const float w[4] = {w4v[0], w4v[1], w4v[2], w4v[3]};
             float xv[7];
 #pragma unroll
             for (int j = 0; j < 7; ++j) xv[j] = nvv[j].get(e);
@@ -869,97 +846,148 @@ __global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const in
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int at = sw64(4 * vc4 + e, 4 * tq4);
+            const int at = sw80(4 * vc4 + e, 4 * tq4);
             *reinterpret_cast<u32x2*>(VTh + at) = th[e];
             *reinterpret_cast<u32x2*>(VTl + at) = tl[e];
         }
     };
-    prefetch_v(0);
-    int o_c0 = 0, o_n = 0;
-    auto store_o = [&]() {
-        const int c4 = tid & 15, r = tid >> 4;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int t = r + 16 * it;
-            if (t < o_n)
-                *reinterpret_cast<f32x4*>(Og + (int64_t)(o_c0 + t) * o_stride + 4 * c4) =
-                    *reinterpret_cast<const f32x4*>(Os + os_at(t, 4 * c4));
-        }
-        o_n = 0;
-    };
-    __syncthreads();  // taps
-    conv_v(false);     // the first chunk's v tile (published by the barrier before phase 1)
-
-    for (int ci = 0; ci < nch; ++ci) {
-        const int c0 = ci * CH;
-        const int n = (T - c0 < CH) ? (T - c0) : CH;
-        const unsigned char* g3 = g3s;
-        const __bf16* Ph = reinterpret_cast<const __bf16*>(g3);
-        const __bf16* Pl = reinterpret_cast<const __bf16*>(g3 + VR_PL - VR_PH);
-        const float* sgam = reinterpret_cast<const float*>(g3 + VR_GAM - VR_PH);
-        const float* swdr = reinterpret_cast<const float*>(g3 + VR_WDR - VR_PH);
-        const float* srq = reinterpret_cast<const float*>(g3 + G3V_BYTES);
-        const float* skq = reinterpret_cast<const float*>(g3 + G3V_BYTES + CH * 4);
-        // the previous chunk's outputs (staged before the barrier that ended it)
-        store_o();
-        const int colv = 16 * wv + lr;
-        bf16x8 sb[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) sb[kk] = cat8(to_bf4(s[2 * kk]), to_bf4(s[2 * kk + 1]));
-        // ================================ phase 1: D = U - W S = beta V + LTb V + (-W) S
-        GDN_WAIT_VM(WAIT_G1);
-        lds_barrier();
-        if (ci > 0) {  // this chunk's v tile from its staged rows (the previous tile was last read in phase 1)
-            conv_v(true);
-            lds_barrier();
-        }
-        f32x4 D[4];
+    float* __restrict__ Og0 = A.o + (int64_t)r0 * A.h_v * A.d_v + (int64_t)h * A.d_v + colbase;
+    const int64_t o_stride = (int64_t)A.h_v * A.d_v;
+    const int ocol = 16 * w4 + lr;
+    f32x4 qs[4], Dp[4];
+    bf16x4 dh[4], dl[4];
+    // D of a chunk from the chain (LDS) into registers, with its hi/lo split
+    auto take_d = [&]() {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int t0 = 16 * mt + 4 * lg;
-            const bf16x4 vh = *reinterpret_cast<const bf16x4*>(VTh + sw64(colv, t0));
-            const bf16x4 vl = *reinterpret_cast<const bf16x4*>(VTl + sw64(colv, t0));
-            const f32x4 bt = *reinterpret_cast<const f32x4*>(sbeta + t0);
-            f32x4 u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) u[j] = bt[j] * ((float)vh[j] + (float)vl[j]);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                u = mma32(*reinterpret_cast<const bf16x8*>(LTb + sw64(16 * mt + lr, 32 * ks + 8 * lg)),
-                          *reinterpret_cast<const bf16x8*>(VTh + sw64(colv, 32 * ks + 8 * lg)), u);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                u = mma32(cat8(ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 4 * lg),
-                               ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 16 + 4 * lg)),
-                          sb[kk], u);
-            D[mt] = u;
+            Dp[mt] = Dx[(w4 * 4 + mt) * 64 + lane];
+            split4(Dp[mt], dh[mt], dl[mt]);
         }
-        settle4(D);
-        bf16x4 dh[4], dl[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) split4(D[mt], dh[mt], dl[mt]);
-        lds_barrier();  // every read of G1 and of the v tile is done
-        fill_g1(ci + 1);
-        // ================================ phase 2: Q S
-        GDN_WAIT_VM(wait_g2<ActT>());
-        lds_barrier();
-        f32x4 qs[4];
+    };
+    // O of chunk pc (n_p rows) from its Q S (qs), D (Dp, dh, dl) and G3: wave
+    // w's column tile, written straight from the accumulator layout (16 lanes
+    // = 64 contiguous bytes of one row)
+    auto output = [&](int pc, int n_p) {
+        // every operand read first (P tiles on and below the diagonal), then the products
+        bf16x8 pa[4][2][2];  // [row tile][k step][hi, lo] for the 16x16x32 products
+        bf16x4 pd[2][2];     // [even row tile / 2][hi, lo] for the diagonal 16x16x16 products
+        f32x4 grq[4], kq[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int row = 16 * mt + lr;
-            qs[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int t0 = 16 * mt + 4 * lg;
+            grq[mt] = *reinterpret_cast<const f32x4*>(sgrq + t0);
+            kq[mt] = *reinterpret_cast<const f32x4*>(skq + t0);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                qs[mt] = mma32(cat8(ld4s(Qh + row * LQK + 32 * kk + 4 * lg), ld4s(Qh + row * LQK + 32 * kk + 16 + 4 * lg)),
-                               sb[kk], qs[mt]);
+            for (int kk = 0; kk < 2; ++kk) {
+                if (2 * kk + 1 > mt) continue;
+                pa[mt][kk][0] = cat8(ld4s(Ph + row * LT + 32 * kk + 4 * lg), ld4s(Ph + row * LT + 32 * kk + 16 + 4 * lg));
+                pa[mt][kk][1] = cat8(ld4s(Pl + row * LT + 32 * kk + 4 * lg), ld4s(Pl + row * LT + 32 * kk + 16 + 4 * lg));
+            }
+            if ((mt & 1) == 0) {
+                pd[mt >> 1][0] = ld4s(Ph + row * LT + 16 * mt + 4 * lg);
+                pd[mt >> 1][1] = ld4s(Pl + row * LT + 16 * mt + 4 * lg);
+            }
         }
-        settle4(qs);
-        lds_barrier();
-        fill_g2(ci + 1);
-        // ================================ phase 3: S <- e^{G_last} S + K^T diag(rk e^{G_last - G}) D (+ last row)
-        GDN_WAIT_VM(wait_g34<ActT>());
-        lds_barrier();
-        {
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+        f32x4 o_tile[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = grq[mt][j] * qs[mt][j] + kq[mt][j] * Dp[mt][j];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (2 * kk + 1 > mt) continue;
+                const bf16x8 bh = cat8(dh[2 * kk], dh[2 * kk + 1]), bl = cat8(dl[2 * kk], dl[2 * kk + 1]);
+                o = mma32(pa[mt][kk][0], bh, o);
+                o = mma32(pa[mt][kk][0], bl, o);
+                o = mma32(pa[mt][kk][1], bh, o);
+            }
+            if ((mt & 1) == 0) {
+                if (mt > 0) settle_v(o);
+                o = mma16(pd[mt >> 1][0], dh[mt], o);
+                o = mma16(pd[mt >> 1][0], dl[mt], o);
+                o = mma16(pd[mt >> 1][1], dh[mt], o);
+            }
+            o_tile[mt] = o;
+        }
+        settle4_v(o_tile);  // tiles 1 and 3 end with a 16x16x32 product
+        // rows of this chunk as 32-bit offsets from a wave-uniform base
+        float* ob = uniform_ptr(Og0 + (int64_t)pc * CH * o_stride);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * mt + 4 * lg + j;
+                if (t < n_p) ob[(uint32_t)(t * (int)o_stride + ocol)] = o_tile[mt][j];
+            }
+    };
+
+    // The two sides run separate copies of the chunk loop (their registers
+    // never overlap); every barrier of one has its counterpart in the other,
+    // in the same order.
+    if (chain) {
+        // ---- prologue: the state and its hi operand, G1 of the first chunk
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                s[dt][j] = init ? to_f32(Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v]) : 0.0f;
+        publish_s(sb);
+        fill_g1(0);
+        lds_barrier();  // (the output side's taps)
+        GDN_WAIT_VM(0);
+        lds_barrier();  // v tile, hi(S), G1 and G2 of chunk 0
+        const int colv = 16 * w4 + lr;
+        for (int ci = 0; ci < nch; ++ci) {
+            const int n = (T - ci * CH < CH) ? (T - ci * CH) : CH;
+            // ================================ step A: D = U - W S = beta V + LTb V + (-W) S
+            fill_g4(ci);
+            f32x4 D[4];
+            bf16x8 vb[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) vb[ks] = *reinterpret_cast<const bf16x8*>(VTh + sw80(colv, 32 * ks + 8 * lg));
+            // two row tiles at a time: their operands are read before their products
+#pragma unroll
+            for (int mp = 0; mp < 4; mp += 2) {
+                bf16x4 vh[2], vl[2];
+                f32x4 bt[2];
+                bf16x8 la[2][2], wa[2][4];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    const int mt = mp + m2, t0 = 16 * mt + 4 * lg;
+                    vh[m2] = *reinterpret_cast<const bf16x4*>(VTh + sw80(colv, t0));
+                    vl[m2] = *reinterpret_cast<const bf16x4*>(VTl + sw80(colv, t0));
+                    bt[m2] = *reinterpret_cast<const f32x4*>(sbeta + t0);
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        la[m2][ks] = *reinterpret_cast<const bf16x8*>(LTb + sw80(16 * mt + lr, 32 * ks + 8 * lg));
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        wa[m2][kk] = cat8(ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 4 * lg),
+                                          ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 16 + 4 * lg));
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    f32x4 u;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) u[j] = bt[m2][j] * ((float)vh[m2][j] + (float)vl[m2][j]);
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) u = mma32(la[m2][ks], vb[ks], u);
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) u = mma32(wa[m2][kk], sb[kk], u);
+                    D[mp + m2] = u;
+                }
+            }
+            settle4_v(D);
+            GDN_WAIT_VM(0);  // G4 of this chunk
+            lds_barrier();
+            // ================================ step B: hand D over; S <- e^{G_last} S + K^T diag(rk e^{G_last - G}) D
+            if (ci + 1 < nch) fill_g1(ci + 1);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) Dx[(w4 * 4 + mt) * 64 + lane] = D[mt];
             bf16x4 wh[4], wl[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
@@ -967,99 +995,127 @@ __global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const in
                 split4(D[kt] * wd, wh[kt], wl[kt]);
             }
             const int tl = n - 1;
-            float dsel = 0.0f;
+            float dsel = D[3][3];  // row 63 of a full chunk (lanes with lg = 3)
+            if (n < CH) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (16 * kt + 4 * lg + j == tl) dsel = D[kt][j];
+                    for (int j = 0; j < 4; ++j)
+                        if (16 * kt + 4 * lg + j == tl) dsel = D[kt][j];
+            }
             const float dlast = __shfl(dsel, ((tl & 15) >> 2) * 16 + lr, 64);
-            const float glast = sgam[tl];
+            const float glast = sgam4[tl];
             bf16x8 wh2[2], wl2[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 wh2[kk] = cat8(wh[2 * kk], wh[2 * kk + 1]);
                 wl2[kk] = cat8(wl[2 * kk], wl[2 * kk + 1]);
             }
+            // k^T operands of four row tiles at a time, read before their products
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const int row = 16 * dt + lr;
-                f32x4 acc = s[dt] * glast;
+            for (int dh = 0; dh < 8; dh += 4) {
+                bf16x8 kh[4][2], kl[4][2];
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int k0 = ktr_at(row, 32 * kk + 4 * lg), k1 = ktr_at(row, 32 * kk + 16 + 4 * lg);
-                    const bf16x8 kh = cat8(ld4s(KTh + k0), ld4s(KTh + k1));
-                    const bf16x8 kl = cat8(ld4s(KTl + k0), ld4s(KTl + k1));
-                    acc = mma32(kh, wh2[kk], acc);
-                    acc = mma32(kh, wl2[kk], acc);
-                    acc = mma32(kl, wh2[kk], acc);
+                for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const int row = 16 * (dh + d4) + lr;
+                        const int k0 = ktr_at(row, 32 * kk + 4 * lg), k1 = ktr_at(row, 32 * kk + 16 + 4 * lg);
+                        kh[d4][kk] = cat8(ld4s(KTh + k0), ld4s(KTh + k1));
+                        kl[d4][kk] = cat8(ld4s(KTl + k0), ld4s(KTl + k1));
+                    }
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+                for (int d4 = 0; d4 < 4; ++d4) {
+                    f32x4 acc = s[dh + d4] * glast;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        acc = mma32(kh[d4][kk], wh2[kk], acc);
+                        acc = mma32(kh[d4][kk], wl2[kk], acc);
+                        acc = mma32(kl[d4][kk], wh2[kk], acc);
+                    }
+                    s[dh + d4] = acc;
                 }
-                s[dt] = acc;
             }
-            settle8(s);
+            settle8_v(s);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 const f32x4 kv = *reinterpret_cast<const f32x4*>(klast + 16 * dt + 4 * lg);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) s[dt][j] = fmaf(kv[j], dlast, s[dt][j]);
             }
+            publish_s(sb);
+            GDN_WAIT_VM(0);  // G1 of the next chunk
+            lds_barrier();
         }
-        lds_barrier();  // every read of G4 is done
-        fill_g4(ci + 1);
-        // ================================ phase 4: O = diag(e^G rq) Q S + diag(k.q) D + P D
-        f32x4 o_tile[4];
+        // ---- the final state
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int row = 16 * mt + lr;
-            const int t0 = 16 * mt + 4 * lg;
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(sgam + t0);
-            const f32x4 rq = *reinterpret_cast<const f32x4*>(srq + t0);
-            const f32x4 kq = *reinterpret_cast<const f32x4*>(skq + t0);
-            f32x4 o;
+        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = gm[j] * rq[j] * qs[mt][j] + kq[j] * D[mt][j];
+            for (int j = 0; j < 4; ++j) Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v] = from_f32<StT>(s[dt][j]);
+    } else {
+        // ---- prologue: taps, the first chunk's v tile, G2 of the first chunk
+        if (t4 < BVC) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (2 * kk + 1 > mt) continue;
-                const bf16x8 ph = cat8(ld4s(Ph + row * LT + 32 * kk + 4 * lg), ld4s(Ph + row * LT + 32 * kk + 16 + 4 * lg));
-                const bf16x8 pl = cat8(ld4s(Pl + row * LT + 32 * kk + 4 * lg), ld4s(Pl + row * LT + 32 * kk + 16 + 4 * lg));
-                const bf16x8 bh = cat8(dh[2 * kk], dh[2 * kk + 1]), bl = cat8(dl[2 * kk], dl[2 * kk + 1]);
-                o = mma32(ph, bh, o);
-                o = mma32(ph, bl, o);
-                o = mma32(pl, bh, o);
-            }
-            if ((mt & 1) == 0) {
-                if (mt > 0) settle(o);
-                const bf16x4 ph = ld4s(Ph + row * LT + 16 * mt + 4 * lg);
-                const bf16x4 pl = ld4s(Pl + row * LT + 16 * mt + 4 * lg);
-                o = mma16(ph, dh[mt], o);
-                o = mma16(ph, dl[mt], o);
-                o = mma16(pl, dh[mt], o);
-            }
-            o_tile[mt] = o;
+            for (int e = 0; e < 4; ++e) wv4[4 * tap_at(t4) + e] = to_f32(Wc[gv * 4 + e]);
         }
-        settle4(o_tile);  // tiles 1 and 3 end with a 16x16x32 product
-        // stage the outputs (the staging tile's last reads, by store_o above,
-        // are ordered before this by the barriers since)
+        load_v(0);
+        fill_g2(0);
+        lds_barrier();  // taps
+        conv_v();
+        GDN_WAIT_VM(0);
+        lds_barrier();  // v tile, hi(S), G1 and G2 of chunk 0
+        for (int ci = 0; ci < nch; ++ci) {
+            // ================================ step A: Q S of this chunk, O of the previous one
+            if (ci + 1 < nch) load_v((ci + 1) * CH);
+            f32x4 qn[4];
+            bf16x8 sbo[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int kk = 0; kk < 4; ++kk) sbo[kk] = Sx[(w4 * 4 + kk) * 64 + lane];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Os[os_at(16 * mt + 4 * lg + j, 16 * wv + lr)] = o_tile[mt][j];
-        o_c0 = c0;
-        o_n = n;
-        lds_barrier();  // the staged outputs; every read of this chunk's P group
-        fill_g3(ci + 1);
+            for (int mp = 0; mp < 4; mp += 2) {
+                bf16x8 qa[2][4];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    const int row = 16 * (mp + m2) + lr;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        qa[m2][kk] = cat8(ld4s(Qh + row * LQK + 32 * kk + 4 * lg), ld4s(Qh + row * LQK + 32 * kk + 16 + 4 * lg));
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    f32x4 q = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) q = mma32(qa[m2][kk], sbo[kk], q);
+                    qn[mp + m2] = q;
+                }
+            }
+            if (ci > 0) {
+                take_d();
+                output(ci - 1, CH);
+            }
+            settle4_v(qn);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) qs[mt] = qn[mt];
+            lds_barrier();
+            // ================================ step B: the next chunk's v tile; refills
+            if (ci + 1 < nch) {
+                conv_v();
+                fill_g2(ci + 1);
+            }
+            fill_g3(ci);
+            GDN_WAIT_VM(0);  // G2 of the next chunk, G3 of this one
+            lds_barrier();
+        }
+        // ---- the last chunk's outputs (its D and G3 arrived in the last step)
+        take_d();
+        output(nch - 1, T - (nch - 1) * CH);
     }
-    store_o();  // the last chunk's outputs
-    wait_vmem();  // the refills issued past the last chunk have landed before the workgroup ends
 
-    // ---- epilogue: state, then the rolled windows (this block's v channels;
-    // the key head's q/k channels by its first value head's first block: the
-    // prep kernel, the only reader of the old q/k window, has finished)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Sg[(int64_t)(16 * dt + 4 * lg + j) * A.d_v] = from_f32<StT>(s[dt][j]);
+    // ---- the rolled windows (this block's v channels; the key head's q/k
+    // channels by its first value head's first block: the prep kernel, the
+    // only reader of the old q/k window, has finished)
     auto roll = [&](int64_t ch) {
         float vw[3];
 #pragma unroll
@@ -1072,9 +1128,9 @@ __global__ __launch_bounds__(NTH) void k_chunk_state(const ChunkArgs A, const in
 #pragma unroll
         for (int j = 0; j < 3; ++j) win[(int64_t)j * C + ch] = from_f32<ActT>(vw[j]);
     };
-    if (has_v) roll(gv);
-    if (h == ki * rr && blk == 0) {
-        const int64_t gq = tid < DK ? (int64_t)ki * DK + tid : (int64_t)A.h_k * DK + (int64_t)ki * DK + (tid - DK);
+    if (!chain && t4 < BVC) roll(gv);
+    if (chain && h == ki * rr && blk == 0) {
+        const int64_t gq = t4 < DK ? (int64_t)ki * DK + t4 : (int64_t)A.h_k * DK + (int64_t)ki * DK + (t4 - DK);
         roll(gq);
     }
 }
@@ -1091,7 +1147,7 @@ hipError_t launch_chunk2_t(const ChunkArgs& a, int max_len, hipStream_t s) {
     hipLaunchKernelGGL((k_chunk_prep<ActT>), dim3((unsigned)gprep), dim3(NTH), 0, s, a, nck);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_chunk_state<ActT, StT>), dim3((unsigned)gstate), dim3(NTH), 0, s, a, nck);
+    hipLaunchKernelGGL((k_chunk_state<ActT, StT>), dim3((unsigned)gstate), dim3(SNTH), 0, s, a, nck);
     return hipGetLastError();
 }
 

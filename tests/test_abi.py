@@ -206,6 +206,7 @@ def test_chunked_validation(so, L):
     assert call(conv=L.GdnConvPool(FAKE + 8, 3 * C, 3, 4, FAKE)) == 1
     assert call(conv=L.GdnConvPool(FAKE, 3 * C + 4, 3, 4, FAKE)) == 1
     assert call(o=FAKE + 4) == 1
+    assert call(x_stride=(1 << 24) + 8) == 1  # a chunk's rows are addressed with 32-bit offsets
     # the workspace: one slot of records per sequence plus one per 64 rows
     def ws(n_seqs, n_rows, dims=d):
         out = ctypes.c_size_t(123)
