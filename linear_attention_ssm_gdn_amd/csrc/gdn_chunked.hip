@@ -600,21 +600,33 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
         // ---- W[t][d] = bgr_t K[t][d] + (LTbg K)[t][d]; 32 tiles, 8 per wave
         {
             f32x4 wacc[8];
+            // four tiles at a time: their k^T reads (the record, in L2) are
+            // issued together, ahead of the products
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int idx = wvs + 4 * k, mt = idx >> 3, dt = idx & 7;
-                const int d = 16 * dt + lr;
-                const int ko = ktr_at(d, 16 * mt + 4 * lg);
-                const bf16x4 kh = *reinterpret_cast<const bf16x4*>(KTh + ko);
-                const bf16x4 kl = *reinterpret_cast<const bf16x4*>(KTl + ko);
-                const f32x4 bg = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + 16 * mt + 4 * lg);
+            for (int kb = 0; kb < 8; kb += 4) {
+                bf16x4 kh[4], kl[4];
+                bf16x8 bop[4][2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wacc[k][j] = bg[j] * ((float)kh[j] + (float)kl[j]);
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const int idx = wvs + 4 * (kb + k4), mt = idx >> 3, dt = idx & 7;
+                    const int d = 16 * dt + lr;
+                    const int ko = ktr_at(d, 16 * mt + 4 * lg);
+                    kh[k4] = *reinterpret_cast<const bf16x4*>(KTh + ko);
+                    kl[k4] = *reinterpret_cast<const bf16x4*>(KTl + ko);
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 aop = ld8(LTbg, LT, 16 * mt + lr, 32 * ks + 8 * lg);
-                    const bf16x8 bop = *reinterpret_cast<const bf16x8*>(KTh + ktr_at(d, 32 * ks + 8 * lg));
-                    wacc[k] = mma32(aop, bop, wacc[k]);
+                    for (int ks = 0; ks < 2; ++ks)
+                        bop[k4][ks] = *reinterpret_cast<const bf16x8*>(KTh + ktr_at(d, 32 * ks + 8 * lg));
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const int k = kb + k4, idx = wvs + 4 * k, mt = idx >> 3;
+                    const f32x4 bg = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + 16 * mt + 4 * lg);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) wacc[k][j] = bg[j] * ((float)kh[k4][j] + (float)kl[k4][j]);
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        wacc[k] = mma32(ld8(LTbg, LT, 16 * mt + lr, 32 * ks + 8 * lg), bop[k4][ks], wacc[k]);
                 }
             }
             settle8(wacc);
