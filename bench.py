@@ -298,9 +298,14 @@ def measure(torch, wload, steps, warmup):
 
 # --------------------------------------------------------------- traffic file
 def kernel_source_hash() -> str:
+    """Hash of the device sources (kernels, their launchers and headers; the
+    host-side argument checks and path selection do not change a kernel's
+    traffic)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_ssm_gdn_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not f.endswith((".hip", ".hpp", ".h")):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -231,7 +231,7 @@ def test_chunked_validation(so, L):
 
 def test_prefill_path_selection(so, L):
     """Host-side choice between the token-by-token and chunked paths: the
-    measured default break-even (32 rows for one or two sequences, 16 for
+    measured default break-even (32 rows for 1-4 sequences, 16 for 5-8, 8 for
     more), an explicit token_max, max_seqlen unknown (n_rows stands in), and
     head dims the chunked kernel is not compiled for."""
     def path(dims, n_seqs, max_seqlen, token_max=-1, n_rows=None):
@@ -241,10 +241,12 @@ def test_prefill_path_selection(so, L):
         return out.value
     d = _dims(L)
     T, K = L.GDN_PATH_TOKEN, L.GDN_PATH_CHUNKED
-    for n in (1, 2):
+    for n in (1, 2, 4):
         assert path(d, n, 1) == T and path(d, n, 32) == T and path(d, n, 33) == K
-    for n in (3, 8, 64):
+    for n in (5, 8):
         assert path(d, n, 16) == T and path(d, n, 17) == K and path(d, n, 8192) == K
+    for n in (9, 16, 64):
+        assert path(d, n, 8) == T and path(d, n, 9) == K and path(d, n, 8192) == K
     assert path(d, 8, 4096, token_max=2 ** 31 - 1) == T
     assert path(d, 1, 1, token_max=0) == K
     assert path(d, 1, 100, token_max=100) == T and path(d, 1, 101, token_max=100) == K
