@@ -51,7 +51,6 @@ constexpr int NTH = 256;       // threads per workgroup
 constexpr int LQK = 136;       // bf16 row stride of token-major [64][128] arrays
 constexpr int LT = 72;         // bf16 row stride of [..][64] arrays
 constexpr int LAF = 68;        // fp32 row stride of A [64][64]
-constexpr int L80 = 80;        // bf16 row stride of the swizzled [64][80] arrays (sw80)
 
 // LDS of the prep kernel (bytes): token-major q and k hi/lo; after the
 // products the k regions hold T and LTbg, the q-lo region A and then -W.
@@ -63,6 +62,7 @@ constexpr int OFF_QL = OFF_KH + SZ_REG;        // then A (fp32), then -W
 constexpr int OFF_KL = OFF_QL + SZ_REG;
 constexpr int PREP_LDS = OFF_KL + SZ_REG;
 static_assert(CH * LAF * 4 <= SZ_REG && CH * LQK * 2 <= SZ_REG && 2 * CH * LT * 2 <= SZ_REG, "region sizes");
+static_assert(DK * CH * 2 <= SZ_TOK && DK * CH * 2 <= SZ_REG, "k^T hi/lo fit the q hi and k lo regions");
 
 // scalar rows in the SC block
 enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
@@ -192,14 +192,14 @@ constexpr int KR_RQ = KR_KLAST + DK * 4;         // fp32 [64]: rq (with the outp
 constexpr int KR_KQ = KR_RQ + CH * 4;            // fp32 [64]: rq rk (q.k) of each row
 constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 55296
 constexpr int VR_WM = 0;                         // bf16 [64][LQK]: -W
-constexpr int VR_LTB = VR_WM + CH * LQK * 2;     // bf16 [64][80] (sw80): (T - I) diag(beta)
-constexpr int VR_BETA = VR_LTB + CH * L80 * 2;   // fp32 [64]
+constexpr int VR_LTB = VR_WM + CH * LQK * 2;     // bf16 [64][64] (sw64): (T - I) diag(beta)
+constexpr int VR_BETA = VR_LTB + CH * CH * 2;    // fp32 [64]
 constexpr int VR_PH = VR_BETA + CH * 4;          // bf16 [64][LT]: P hi (tiles on or below the diagonal)
 constexpr int VR_PL = VR_PH + CH * LT * 2;       // bf16 [64][LT]: P lo
 constexpr int VR_GRQ = VR_PL + CH * LT * 2;      // fp32 [64]: e^G rq
 constexpr int VR_GAM = VR_GRQ + CH * 4;          // fp32 [64]: e^G
 constexpr int VR_WDR = VR_GAM + CH * 4;          // fp32 [64]: rk e^{G_last - G}, 0 for the last row
-constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 47104, a multiple of 256
+constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 45056, a multiple of 256
 static_assert(VREC_BYTES % 256 == 0 && KREC_BYTES % 256 == 0, "records keep 256-byte alignment");
 static_assert(VR_WDR + CH * 4 <= VREC_BYTES && KREC_BYTES % 256 == 0 && VREC_BYTES % 256 == 0, "records");
 
@@ -212,15 +212,12 @@ __device__ __forceinline__ int64_t chunk_slot(int seq, int r0, int c) { return (
 // & 15 and column group lg = lane >> 4.
 //  - [rows][LT] (k^T, P) and [rows][LQK] (q, -W): 8-byte reads of rows 36
 //    (68) words apart fill all 64 banks for every 32 lanes.
-//  - sw80 ([rows][80], LTb and the v tile, read both 8 and 16 bytes wide):
-//    rows 160 bytes apart, the 16-byte column group XORed with a 2-bit
-//    function of row & 15 (3 (row & 1) ^ 2 ((row >> 3) & 1)); conflict free
-//    for both read widths, and the XOR leaves the column bits that the
-//    unrolled tiles step through alone, so their offsets stay immediates.
+//  - sw64 ([rows][64], LTb and the v tile, read both 8 and 16 bytes wide):
+//    rows 128 bytes apart, the 16-byte column group XORed with (row >> 1) & 7;
+//    conflict free for both read widths, and for the v conv's 8-byte writes
+//    when four consecutive lanes share a channel group (all measured).
 __device__ __forceinline__ int ktr_at(int row, int col) { return row * LT + col; }
-__device__ __forceinline__ int sw80(int row, int col) {
-    return row * L80 + (col ^ (((3 * (row & 1)) ^ (((row >> 3) & 1) << 1)) << 3));
-}
+__device__ __forceinline__ int sw64(int row, int col) { return row * CH + (col ^ (((row >> 1) & 7) << 3)); }
 
 // Copy BYTES (a multiple of 64) from global memory into LDS with direct
 // global->LDS loads, 16 bytes per lane: wave w copies the w-th quarter in
@@ -308,7 +305,7 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
     unsigned char* slot = static_cast<unsigned char*>(A.workspace) +
                           chunk_slot(seq, r0, c) * ((int64_t)A.h_k * KREC_BYTES + (int64_t)A.h_v * VREC_BYTES);
     unsigned char* krec = slot + (int64_t)ki * KREC_BYTES;
-    __bf16* KTh = reinterpret_cast<__bf16*>(krec + KR_KTH);  // written here, read back by the W phase
+    __bf16* KTh = reinterpret_cast<__bf16*>(krec + KR_KTH);  // the record's k^T (the state kernel's)
     __bf16* KTl = reinterpret_cast<__bf16*>(krec + KR_KTL);
 
     const ActT* __restrict__ X = static_cast<const ActT*>(A.x);
@@ -461,8 +458,39 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
         for (int j = 0; j < 4; ++j)
             if (s0 + j == t) sc[SC_KQ * CH + t] = sc[SC_RQ * CH + t] * sc[SC_RK * CH + t] * accq[k][j];
     }
-    lds_barrier();  // every read of Q, K (token-major) is done; KQ is published
+    lds_barrier();  // every product read of Q, K (token-major) is done; KQ is published
     if (tid < CH) reinterpret_cast<float*>(krec + KR_KQ)[tid] = sc[SC_KQ * CH + tid];
+    // ---- k^T hi/lo into LDS for the W phases ([128][64], sw64), transposed
+    // from the token-major k rows: hi into q hi's region (q hi is in the
+    // record), lo over k lo's own region once every lane has read it.  Item
+    // i = tid + 256 p: channel i & 127, tokens 8 (i >> 7) .. +7.
+    __bf16* KTsh = reinterpret_cast<__bf16*>(lds + OFF_QH);
+    __bf16* KTsl = reinterpret_cast<__bf16*>(lds + OFF_KL);
+    {
+        u32x4 lo_items[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int i = tid + NTH * p, d = i & (DK - 1), t0 = 8 * (i >> 7);
+            u32x4 hv, lv;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const __bf16* h0 = Kh + (t0 + 2 * m) * LQK + d;
+                const __bf16* l0 = Kl + (t0 + 2 * m) * LQK + d;
+                hv[m] = (uint32_t)__builtin_bit_cast(uint16_t, h0[0]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, h0[LQK]) << 16);
+                lv[m] = (uint32_t)__builtin_bit_cast(uint16_t, l0[0]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, l0[LQK]) << 16);
+            }
+            *reinterpret_cast<u32x4*>(KTsh + sw64(d, t0)) = hv;
+            lo_items[p] = lv;
+        }
+        lds_barrier();  // every read of k lo is done
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int i = tid + NTH * p, d = i & (DK - 1), t0 = 8 * (i >> 7);
+            *reinterpret_cast<u32x4*>(KTsl + sw64(d, t0)) = lo_items[p];
+        }
+    }
 
     for (int jv = 0; jv < rr; ++jv) {
         const int h = ki * rr + jv;
@@ -592,16 +620,14 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             const u32x4 og = {pack_bf2(lt[0] * g0[0], lt[1] * g0[1]), pack_bf2(lt[2] * g0[2], lt[3] * g0[3]),
                               pack_bf2(lt[4] * g1[0], lt[5] * g1[1]), pack_bf2(lt[6] * g1[2], lt[7] * g1[3])};
             *reinterpret_cast<u32x4*>(LTbg + t * LT + s0) = og;
-            *reinterpret_cast<u32x4*>(vrec + VR_LTB + sw80(t, s0) * 2) = ob;
+            *reinterpret_cast<u32x4*>(vrec + VR_LTB + sw64(t, s0) * 2) = ob;
         }
-        // a full barrier: every thread's k^T stores (long since issued) have
-        // completed, so the W phase may read them back (one CU, one L1)
-        __syncthreads();
+        lds_barrier();  // LTbg, and (first value head) k^T in LDS
         // ---- W[t][d] = bgr_t K[t][d] + (LTbg K)[t][d]; 32 tiles, 8 per wave
         {
             f32x4 wacc[8];
-            // four tiles at a time: their k^T reads (the record, in L2) are
-            // issued together, ahead of the products
+            // four tiles at a time: their k^T reads are issued together, ahead
+            // of the products
 #pragma unroll
             for (int kb = 0; kb < 8; kb += 4) {
                 bf16x4 kh[4], kl[4];
@@ -610,12 +636,12 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
                 for (int k4 = 0; k4 < 4; ++k4) {
                     const int idx = wvs + 4 * (kb + k4), mt = idx >> 3, dt = idx & 7;
                     const int d = 16 * dt + lr;
-                    const int ko = ktr_at(d, 16 * mt + 4 * lg);
-                    kh[k4] = *reinterpret_cast<const bf16x4*>(KTh + ko);
-                    kl[k4] = *reinterpret_cast<const bf16x4*>(KTl + ko);
+                    const int ko = sw64(d, 16 * mt + 4 * lg);
+                    kh[k4] = *reinterpret_cast<const bf16x4*>(KTsh + ko);
+                    kl[k4] = *reinterpret_cast<const bf16x4*>(KTsl + ko);
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
-                        bop[k4][ks] = *reinterpret_cast<const bf16x8*>(KTh + ktr_at(d, 32 * ks + 8 * lg));
+                        bop[k4][ks] = *reinterpret_cast<const bf16x8*>(KTsh + sw64(d, 32 * ks + 8 * lg));
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
@@ -667,14 +693,14 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
 //   G3 (P D, output): P hi/lo, e^G rq       <- value-head record [VR_PH, VR_GAM)
 //                     kq                    <- key-head record [KR_KQ, KREC_BYTES)
 constexpr int SNTH = 512;                              // threads of the state kernel
-constexpr int G1_BYTES = VR_PH;                        // 27904
+constexpr int G1_BYTES = VR_PH;                        // 25856
 constexpr int G2_BYTES = KR_KTH;                       // 17408
 constexpr int G4K_BYTES = KR_RQ - KR_KTH;              // 37376
 constexpr int G4V_BYTES = VR_WDR + CH * 4 - VR_GAM;    // 512
 constexpr int G3V_BYTES = VR_GAM - VR_PH;              // 18688
 constexpr int G3K_BYTES = KREC_BYTES - KR_KQ;          // 256
 constexpr int XCH_BYTES = 4 * 4 * 64 * 16;             // one 16-byte vector per (chain wave, tile, lane)
-constexpr int S_LDS = G1_BYTES + G2_BYTES + G4K_BYTES + G4V_BYTES + G3V_BYTES + G3K_BYTES + 2 * BVC * L80 * 2 +
+constexpr int S_LDS = G1_BYTES + G2_BYTES + G4K_BYTES + G4V_BYTES + G3V_BYTES + G3K_BYTES + 2 * BVC * CH * 2 +
                       2 * XCH_BYTES + BVC * 4 * 4;
 static_assert(S_LDS <= 160 * 1024, "state kernel LDS");
 // The v taps of channel c sit at 16-byte slot 16 (c & 3) + c / 4, so the
@@ -690,8 +716,8 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     __shared__ __attribute__((aligned(16))) unsigned char g2s[G2_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char g4s[G4K_BYTES + G4V_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char g3s[G3V_BYTES + G3K_BYTES];
-    __shared__ __attribute__((aligned(16))) __bf16 VTh[BVC * L80];  // v^T hi, sw80
-    __shared__ __attribute__((aligned(16))) __bf16 VTl[BVC * L80];  // v^T lo, sw80
+    __shared__ __attribute__((aligned(16))) __bf16 VTh[BVC * CH];  // v^T hi, sw64
+    __shared__ __attribute__((aligned(16))) __bf16 VTl[BVC * CH];  // v^T lo, sw64
     __shared__ __attribute__((aligned(16))) f32x4 Dx[4 * 4 * 64];   // D: (chain wave, row tile, lane)
     __shared__ __attribute__((aligned(16))) bf16x8 Sx[4 * 4 * 64];  // hi(S) operand: (chain wave, k step, lane)
     __shared__ __attribute__((aligned(16))) float wv4[BVC * 4];
@@ -813,9 +839,10 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     };
     bf16x8 sb[4];
 
-    // ---- output side: v rows and taps; thread t4 takes channels 4 vc4 .. +3
-    // (vc4 = t4 & 15) and tokens 4 tq4 .. +3 (tq4 = t4 >> 4) of a chunk
-    const int vc4 = t4 & 15, tq4 = t4 >> 4;
+    // ---- output side: v rows and taps; lane l of wave w takes channels
+    // 4 vc4 .. +3 (vc4 = l >> 2) and tokens 4 tq4 .. +3 (tq4 = (l & 3) + 4 w)
+    // of a chunk
+    const int vc4 = lane >> 2, tq4 = (lane & 3) + 4 * w4;
     const int64_t gv = 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + t4;  // channel t4 (< 64)
     RowVec<ActT, 4> nvv[7];
     auto load_v = [&](int cs) {
@@ -858,7 +885,7 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int at = sw80(4 * vc4 + e, 4 * tq4);
+            const int at = sw64(4 * vc4 + e, 4 * tq4);
             *reinterpret_cast<u32x2*>(VTh + at) = th[e];
             *reinterpret_cast<u32x2*>(VTl + at) = tl[e];
         }
@@ -959,7 +986,7 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
             f32x4 D[4];
             bf16x8 vb[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) vb[ks] = *reinterpret_cast<const bf16x8*>(VTh + sw80(colv, 32 * ks + 8 * lg));
+            for (int ks = 0; ks < 2; ++ks) vb[ks] = *reinterpret_cast<const bf16x8*>(VTh + sw64(colv, 32 * ks + 8 * lg));
             // two row tiles at a time: their operands are read before their products
 #pragma unroll
             for (int mp = 0; mp < 4; mp += 2) {
@@ -969,12 +996,12 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2) {
                     const int mt = mp + m2, t0 = 16 * mt + 4 * lg;
-                    vh[m2] = *reinterpret_cast<const bf16x4*>(VTh + sw80(colv, t0));
-                    vl[m2] = *reinterpret_cast<const bf16x4*>(VTl + sw80(colv, t0));
+                    vh[m2] = *reinterpret_cast<const bf16x4*>(VTh + sw64(colv, t0));
+                    vl[m2] = *reinterpret_cast<const bf16x4*>(VTl + sw64(colv, t0));
                     bt[m2] = *reinterpret_cast<const f32x4*>(sbeta + t0);
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
-                        la[m2][ks] = *reinterpret_cast<const bf16x8*>(LTb + sw80(16 * mt + lr, 32 * ks + 8 * lg));
+                        la[m2][ks] = *reinterpret_cast<const bf16x8*>(LTb + sw64(16 * mt + lr, 32 * ks + 8 * lg));
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
                         wa[m2][kk] = cat8(ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 4 * lg),
