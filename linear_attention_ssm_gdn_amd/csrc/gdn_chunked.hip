@@ -240,6 +240,15 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 // A wave-uniform pointer moved to scalar registers (the builtin returns a
 // signed 32-bit value: each half is taken back as unsigned before widening).
+// A wave-uniform element offset moved to scalar registers; added to a
+// kernel-argument pointer it keeps that pointer's global address space (a
+// pointer rebuilt from an integer would be addressed as flat memory, whose
+// operations also count against the LDS wait counter).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)((hi << 32) | lo);
+}
 template <typename T> __device__ __forceinline__ T* uniform_ptr(T* p) {
     const uint64_t v = (uint64_t)(uintptr_t)p;
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -850,8 +859,8 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         // rows cs - 3 .. cs + 63 (clamped to the sequence) as 32-bit offsets
         // from a wave-uniform base row
         const int tb = cs >= 3 ? cs - 3 : 0;
-        const ActT* xb = uniform_ptr(X + (int64_t)(r0 + tb) * A.x_stride + 2 * (int64_t)A.h_k * DK +
-                                     (int64_t)h * A.d_v + colbase);
+        const ActT* xb = X + uniform64((int64_t)(r0 + tb) * A.x_stride + 2 * (int64_t)A.h_k * DK +
+                                       (int64_t)h * A.d_v + colbase);
 #pragma unroll
         for (int j = 0; j < 7; ++j) {
             const int t = cs + 4 * tq4 - 3 + j;
@@ -953,7 +962,7 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         }
         settle4_v(o_tile);  // tiles 1 and 3 end with a 16x16x32 product
         // rows of this chunk as 32-bit offsets from a wave-uniform base
-        float* ob = uniform_ptr(Og0 + (int64_t)pc * CH * o_stride);
+        float* ob = Og0 + uniform64((int64_t)pc * CH * o_stride);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1138,12 +1147,10 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) qs[mt] = qn[mt];
             lds_barrier();
-            // ================================ step B: the next chunk's v tile; refills
-            if (ci + 1 < nch) {
-                conv_v();
-                fill_g2(ci + 1);
-            }
+            // ================================ step B: refills (under the conv); the next chunk's v tile
+            if (ci + 1 < nch) fill_g2(ci + 1);
             fill_g3(ci);
+            if (ci + 1 < nch) conv_v();
             GDN_WAIT_VM(0);  // G2 of the next chunk, G3 of this one
             lds_barrier();
         }
