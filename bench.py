@@ -258,6 +258,18 @@ class MixedWorkload:
         self.seq = SeqWorkload(g, torch, seq_wl)
         self.ver = VerifyWorkload(g, torch, ver_wl, wk.F32)
         self.fused = True
+        self.launches = g.GDN_MIXED_AUTO  # gdn_mixed_step's launch choice when fused
+
+    def chosen_launches(self) -> int:
+        sw, vw = self.seq, self.ver
+        x, a, b, conv, state, o = sw.sets[0]
+        pages, vconv, vo, _ = vw.sets[0]
+        return self.g.gdn_mixed_launches(vw.dims, seq=dict(x=x, a=a, b=b, batch=sw.batch, conv=conv, state=state,
+                                                           o=o),
+                                         verify=dict(pages=pages, x=vw.x[0], a=vw.a[0], b=vw.b[0],
+                                                     n_req=vw.wl.n_req, n_cand=vw.wl.n_cand, req_page=vw.rp,
+                                                     num_accepted=vw.acc[0], step_parity=vw.par[0], conv=vconv,
+                                                     o=vo))
 
     def launch(self):
         g, sw, vw = self.g, self.seq, self.ver
@@ -273,7 +285,7 @@ class MixedWorkload:
             g.gdn_mixed_step(vw.dims, vw.params, seq=dict(x=x, a=a, b=b, batch=sw.batch, conv=conv, state=state, o=o),
                              verify=dict(pages=pages, x=vw.x[s], a=vw.a[s], b=vw.b[s], n_req=vw.wl.n_req,
                                          n_cand=vw.wl.n_cand, req_page=vw.rp, num_accepted=acc, step_parity=par,
-                                         conv=vconv, o=vo))
+                                         conv=vconv, o=vo), launches=self.launches)
         else:
             g.gdn_recurrent_seq(vw.dims, vw.params, x, a, b, sw.batch, conv, state, o=o)
             g.gdn_spec_verify(vw.dims, vw.params, pages, vw.x[s], vw.a[s], vw.b[s], vw.wl.n_req, vw.wl.n_cand,
@@ -504,10 +516,14 @@ def sweep_dispatch(g, torch, steps):
                 continue
             ub = UniformBatch(g, torch, base, n, T)
             ub.params = params
-            ub.chunk = 0
-            seq_ms, _ = measure(torch, ub, steps, 3)
-            ub.chunk = wl.chunk
-            chk_ms, _ = measure(torch, ub, steps, 3)
+            # the two paths in turn, twice; the faster round of each (the first
+            # path timed on fresh pools ran several percent slow)
+            t = {0: [], wl.chunk: []}
+            for _ in range(2):
+                for ch in t:
+                    ub.chunk = ch
+                    t[ch].append(measure(torch, ub, steps, 3)[0])
+            seq_ms, chk_ms = min(t[0]), min(t[wl.chunk])
             line = {"n_seqs": n, "seqlen": T, "tokens": n * T, "us_token_by_token": round(seq_ms * 1e3, 2),
                     "us_chunked": round(chk_ms * 1e3, 2), "faster": "chunked" if chk_ms < seq_ms else "token_by_token"}
             print(json.dumps(line), flush=True)
@@ -696,20 +712,30 @@ def main():
             res = {}
             small_seq = wk.SHORT_PREFILL.replace(name="small_prefill", seqlens=(45, 17, 9, 3))
             small_ver = wk.SPEC_VERIFY.replace(name="small_verify", n_req=8)
+            dec_seq = wk.SHORT_PREFILL.replace(name="decode_rows", seqlens=(1,) * 32)
             for name, sw, vw in (("short_prefill_plus_verify", wk.SHORT_PREFILL, wk.SPEC_VERIFY),
-                                 ("small_prefill_plus_verify", small_seq, small_ver)):
+                                 ("small_prefill_plus_verify", small_seq, small_ver),
+                                 ("decode_rows_plus_verify", dec_seq, wk.SPEC_VERIFY)):
                 log(f"mixed_step {name}")
                 w = MixedWorkload(g, torch, sw, vw)
-                n = max(args.steps // 4, 10)
-                w.fused = True
-                f_ms, _ = measure(torch, w, n, 5)
-                w.fused = False
-                s_ms, _ = measure(torch, w, n, 5)
-                res[name] = {"value": round(f_ms * 1e3, 1), "unit": "us/step", "us_separate_launches": round(s_ms * 1e3, 1),
+                n = max(args.steps // 8, 10)
+                # the three forms in turn, three rounds, median of each form's
+                # rounds (the first form timed on fresh pools ran 6-9% slow)
+                forms = ((True, g.GDN_MIXED_AUTO), (True, g.GDN_MIXED_ONE_LAUNCH), (False, g.GDN_MIXED_AUTO))
+                runs = {f: [] for f in forms}
+                for _ in range(3):
+                    for f in forms:
+                        w.fused, w.launches = f
+                        runs[f].append(measure(torch, w, n, 5)[0])
+                f_ms, one_ms, s_ms = (float(np.median(runs[f])) for f in forms)
+                res[name] = {"value": round(f_ms * 1e3, 1), "unit": "us/step",
+                             "launches": w.chosen_launches(), "us_one_launch": round(one_ms * 1e3, 1),
+                             "us_separate_launches": round(s_ms * 1e3, 1),
                              "speedup_vs_separate": round(s_ms / f_ms, 3),
                              "config": {"prefill_seqlens": list(sw.seqlens), "verify_n_req": vw.n_req,
                                         "verify_n_cand": vw.n_cand, "state_dtype": "f32"}}
-                log(f"mixed_step {name}: {f_ms * 1e3:.1f} us fused, {s_ms * 1e3:.1f} us as two launches")
+                log(f"mixed_step {name}: {f_ms * 1e3:.1f} us (gdn_mixed_step), {one_ms * 1e3:.1f} us one launch, "
+                    f"{s_ms * 1e3:.1f} us as two separate calls")
                 del w
                 torch.cuda.empty_cache()
             other["mixed_step"] = res

@@ -421,19 +421,49 @@ typedef struct gdn_verify_part {
 } gdn_verify_part;
 
 /* One serving step that mixes token-by-token sequences (prefill or decode
- * rows of a ragged batch) with speculative verify requests, in ONE launch
+ * rows of a ragged batch) with speculative verify requests
  * ("r9700-stack v0.2.3", section "1. Time to first token": the prefill
  * and verify kernels read their rows where the batch holds them, so such a
  * step gathers nothing first).  The result is that of
  * gdn_recurrent_seq on `seq` followed by gdn_spec_verify on `verify`, bit
- * for bit; the sequence workgroups come first in the grid (longest sequence
- * first), and the verify workgroups fill the slots shorter sequences free.
+ * for bit.  It runs as one launch -- the sequence workgroups first in the
+ * grid (longest sequence first), the verify workgroups filling the slots
+ * shorter sequences free -- or, for the shapes gdn_mixed_launches names, as
+ * those two calls' kernels in stream order.
  * seq and verify are host pointers; either may be NULL or empty (n_seqs or
  * n_req 0).  The two parts must touch distinct pages; their conv pools may
  * be one pool.  Each part is validated as its stand-alone entry point is;
  * err collects the device-side errors of both. */
 int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,
                        const gdn_verify_part* verify, int32_t* err, void* stream);
+
+#define GDN_MIXED_AUTO 0           /* what gdn_mixed_launches picks */
+#define GDN_MIXED_ONE_LAUNCH 1     /* one grid: sequence workgroups, then verify workgroups */
+#define GDN_MIXED_TWO_LAUNCHES 2   /* gdn_recurrent_seq's kernel, then gdn_spec_verify's, in stream order */
+
+/* The launch count gdn_mixed_step uses for these parts (host-only, nothing
+ * is launched).  *launches (host) receives GDN_MIXED_TWO_LAUNCHES when both
+ * parts are non-empty, every sequence has at most 4 rows
+ * (1 <= batch->max_seqlen <= 4), no spec_pages are set and d_v is a multiple
+ * of 64: gdn_recurrent_seq then runs the sequences on its short-sequence
+ * (decode) kernel, whose streaming workgroups beat the one grid's 32-column
+ * sequence workgroups by 5-48% on MI355X (uniform batches of 4-32
+ * sequences beside 8 or 32 verify requests).  Otherwise
+ * GDN_MIXED_ONE_LAUNCH: for longer sequences the one grid measured as fast
+ * as two launches or faster (up to 28% with one long sequence among short
+ * ones).  seq and verify may be NULL. */
+int32_t gdn_mixed_launches(const gdn_dims* dims, const gdn_seq_part* seq, const gdn_verify_part* verify,
+                           int32_t* launches);
+
+/* gdn_mixed_step with the launch count given: GDN_MIXED_AUTO,
+ * GDN_MIXED_ONE_LAUNCH or GDN_MIXED_TWO_LAUNCHES (anything else is
+ * GDN_ERR_ARG).  Every choice gives the same results bit for bit; with two
+ * launches the sequences take gdn_recurrent_seq's kernel for their shape
+ * (its 32-column kernel when spec_pages are set, which the short-sequence
+ * kernel does not write), so the first such call on a device makes the
+ * host queries described for gdn_recurrent_seq. */
+int32_t gdn_mixed_step_launches(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,
+                                const gdn_verify_part* verify, int32_t launches, int32_t* err, void* stream);
 
 #ifdef __cplusplus
 }

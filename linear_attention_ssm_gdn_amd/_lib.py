@@ -20,11 +20,13 @@ GDN_SPEC_ONEPAGE, GDN_SPEC_SLOTS = 0, 1
 GDN_DEVERR_PAGE, GDN_DEVERR_BATCH, GDN_DEVERR_ACCEPTED, GDN_DEVERR_PARITY, GDN_DEVERR_CACHE = 1, 2, 4, 8, 16
 GDN_PATH_TOKEN, GDN_PATH_CHUNKED = 0, 1
 GDN_PREFILL_MAX_DEFAULT = -1
+GDN_MIXED_AUTO, GDN_MIXED_ONE_LAUNCH, GDN_MIXED_TWO_LAUNCHES = 0, 1, 2
 GDN_NOALLOC_SYNC_WORDS = 65536
 
 SYMBOLS = ("gdn_abi_version", "gdn_status_str", "gdn_spec_page_layout", "gdn_chunked_workspace_bytes",
            "gdn_conv_update", "gdn_recurrent_seq", "gdn_recurrent_seq_noalloc", "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill",
-           "gdn_spec_verify", "gdn_spec_verify_cached", "gdn_prefix_restore", "gdn_mixed_step")
+           "gdn_spec_verify", "gdn_spec_verify_cached", "gdn_prefix_restore", "gdn_mixed_step",
+           "gdn_mixed_launches", "gdn_mixed_step_launches")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -136,5 +138,11 @@ def load() -> ctypes.CDLL:
     L.gdn_mixed_step.restype = _i32
     L.gdn_mixed_step.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams), ctypes.POINTER(GdnSeqPart),
                                  ctypes.POINTER(GdnVerifyPart), _vp, _vp]
+    L.gdn_mixed_launches.restype = _i32
+    L.gdn_mixed_launches.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnSeqPart),
+                                     ctypes.POINTER(GdnVerifyPart), ctypes.POINTER(_i32)]
+    L.gdn_mixed_step_launches.restype = _i32
+    L.gdn_mixed_step_launches.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(GdnParams),
+                                          ctypes.POINTER(GdnSeqPart), ctypes.POINTER(GdnVerifyPart), _i32, _vp, _vp]
     _lib = L
     return L

@@ -379,11 +379,31 @@ GDN_EXPORT int32_t gdn_prefix_restore(const gdn_dims* dims, int32_t layout, int3
     return from_hip(gdn::launch_restore(A, dims->act_dtype, dims->state_dtype, (hipStream_t)stream));
 }
 
-GDN_EXPORT int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,
-                                  const gdn_verify_part* verify, int32_t* err, void* stream) {
+namespace {
+bool mixed_two_launches(const gdn_dims* dims, const gdn_seq_part* seq, const gdn_verify_part* verify) {
+    return seq && verify && seq->batch && seq->batch->n_seqs > 0 && verify->n_req > 0 && !seq->spec_pages &&
+           seq->batch->max_seqlen >= 1 && seq->batch->max_seqlen <= 4 && dims->d_v % 64 == 0;
+}
+}  // namespace
+
+GDN_EXPORT int32_t gdn_mixed_launches(const gdn_dims* dims, const gdn_seq_part* seq, const gdn_verify_part* verify,
+                                      int32_t* launches) {
+    int32_t st;
+    if ((st = check_dims(dims)) != GDN_OK) return st;
+    if (!launches) return GDN_ERR_ARG;
+    if (seq && (st = check_batch(seq->batch)) != GDN_OK) return st;
+    *launches = mixed_two_launches(dims, seq, verify) ? GDN_MIXED_TWO_LAUNCHES : GDN_MIXED_ONE_LAUNCH;
+    return GDN_OK;
+}
+
+GDN_EXPORT int32_t gdn_mixed_step_launches(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,
+                                           const gdn_verify_part* verify, int32_t launches, int32_t* err,
+                                           void* stream) {
     int32_t st;
     if ((st = check_dims(dims)) != GDN_OK) return st;
     if ((st = check_params(params)) != GDN_OK) return st;
+    if (launches != GDN_MIXED_AUTO && launches != GDN_MIXED_ONE_LAUNCH && launches != GDN_MIXED_TWO_LAUNCHES)
+        return GDN_ERR_ARG;
     gdn::SeqArgs S{};
     gdn::VerifyArgs V{};
     int32_t layout = GDN_SPEC_ONEPAGE;
@@ -415,6 +435,28 @@ GDN_EXPORT int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params
                             v.num_accepted, v.step_parity, v.pages, v.page_bytes, v.n_pages, v.conv, v.o, err);
     }
     if (S.n_seqs == 0 && V.n_req == 0) return GDN_OK;
+    const bool two = launches == GDN_MIXED_TWO_LAUNCHES ||
+                     (launches == GDN_MIXED_AUTO && mixed_two_launches(dims, seq, verify));
+    if (two) {
+        // the sequences first, on gdn_recurrent_seq's kernel for their shape (its
+        // 32-column kernel when they also write speculative-page headers, which
+        // the short-sequence kernel does not do), then the verify requests
+        if (S.n_seqs > 0) {
+            const int max_len = S.spec_pages ? 0 : seq->batch->max_seqlen;
+            if ((st = from_hip(gdn::launch_seq(S, dims->d_k, dims->act_dtype, dims->state_dtype, max_len,
+                                               (hipStream_t)stream))) != GDN_OK)
+                return st;
+        }
+        if (V.n_req > 0)
+            return from_hip(gdn::launch_verify(V, dims->d_k, dims->act_dtype, dims->state_dtype, layout,
+                                               (hipStream_t)stream));
+        return GDN_OK;
+    }
     return from_hip(gdn::launch_mixed(S, V, dims->d_k, dims->act_dtype, dims->state_dtype, layout,
                                       (hipStream_t)stream));
+}
+
+GDN_EXPORT int32_t gdn_mixed_step(const gdn_dims* dims, const gdn_params* params, const gdn_seq_part* seq,
+                                  const gdn_verify_part* verify, int32_t* err, void* stream) {
+    return gdn_mixed_step_launches(dims, params, seq, verify, GDN_MIXED_AUTO, err, stream);
 }

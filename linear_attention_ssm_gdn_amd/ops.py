@@ -344,16 +344,9 @@ def gdn_prefix_restore(dims: Dims, pages: SpecPages, entry: torch.Tensor, req_pa
     _check("gdn_prefix_restore", st)
 
 
-def gdn_mixed_step(dims: Dims, params: Params, seq: Optional[dict] = None, verify: Optional[dict] = None,
-                   err: Optional[torch.Tensor] = None) -> None:
-    """One launch for a step mixing token-by-token sequences and verify requests.
-
-    seq:    dict(x, a, b, batch, conv, state, o) -- the arguments of gdn_recurrent_seq, and
-            optionally spec_pages (SpecPages) whose headers the sequences leave fresh
-    verify: dict(pages, x, a, b, n_req, n_cand, req_page, num_accepted, step_parity, conv, o)
-            -- the arguments of gdn_spec_verify (pages: SpecPages)
-    Outputs are written into the o tensors given."""
-    d, p = dims.c(), params.c()
+def _mixed_parts(seq: Optional[dict], verify: Optional[dict]):
+    """ctypes structs of a mixed step's parts (None where a part is absent),
+    the objects they point into, and the tensor whose stream is used."""
     sp = vp = None
     keep = []
     stream_of = None
@@ -378,9 +371,39 @@ def gdn_mixed_step(dims: Dims, params: Params, seq: Optional[dict] = None, verif
                              pages.buf.data_ptr(), pages.buf.stride(0), pages.buf.shape[0], v["conv"].c(),
                              _ptr(v.get("o")))
         stream_of = stream_of if stream_of is not None else v["req_page"]
+    return sp, vp, keep, stream_of
+
+
+def gdn_mixed_launches(dims: Dims, seq: Optional[dict] = None, verify: Optional[dict] = None) -> int:
+    """The launch count gdn_mixed_step uses for these parts (host only):
+    GDN_MIXED_ONE_LAUNCH or GDN_MIXED_TWO_LAUNCHES."""
+    d = dims.c()
+    sp, vp, keep, _ = _mixed_parts(seq, verify)
+    out = ctypes.c_int32(0)
+    st = L.load().gdn_mixed_launches(ctypes.byref(d), ctypes.byref(sp) if sp is not None else None,
+                                     ctypes.byref(vp) if vp is not None else None, ctypes.byref(out))
+    _check("gdn_mixed_launches", st)
+    return int(out.value)
+
+
+def gdn_mixed_step(dims: Dims, params: Params, seq: Optional[dict] = None, verify: Optional[dict] = None,
+                   err: Optional[torch.Tensor] = None, launches: int = L.GDN_MIXED_AUTO) -> None:
+    """A step mixing token-by-token sequences and verify requests: one
+    launch, or two where gdn_mixed_launches picks them (launches overrides:
+    GDN_MIXED_ONE_LAUNCH / GDN_MIXED_TWO_LAUNCHES; the results are the same
+    bit for bit).
+
+    seq:    dict(x, a, b, batch, conv, state, o) -- the arguments of gdn_recurrent_seq, and
+            optionally spec_pages (SpecPages) whose headers the sequences leave fresh
+    verify: dict(pages, x, a, b, n_req, n_cand, req_page, num_accepted, step_parity, conv, o)
+            -- the arguments of gdn_spec_verify (pages: SpecPages)
+    Outputs are written into the o tensors given."""
+    d, p = dims.c(), params.c()
+    sp, vp, keep, stream_of = _mixed_parts(seq, verify)
     if stream_of is None:
         return
-    st = L.load().gdn_mixed_step(ctypes.byref(d), ctypes.byref(p), ctypes.byref(sp) if sp is not None else None,
-                                 ctypes.byref(vp) if vp is not None else None, _ptr(err),
-                                 torch.cuda.current_stream(stream_of.device).cuda_stream)
+    st = L.load().gdn_mixed_step_launches(ctypes.byref(d), ctypes.byref(p),
+                                          ctypes.byref(sp) if sp is not None else None,
+                                          ctypes.byref(vp) if vp is not None else None, int(launches), _ptr(err),
+                                          torch.cuda.current_stream(stream_of.device).cuda_stream)
     _check("gdn_mixed_step", st)

@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported(so):
                           "gdn_chunked_workspace_bytes", "gdn_conv_update", "gdn_recurrent_seq",
                           "gdn_chunked_prefill", "gdn_prefill_path", "gdn_prefill", "gdn_spec_verify",
                           "gdn_spec_verify_cached", "gdn_prefix_restore", "gdn_mixed_step",
-                          "gdn_recurrent_seq_noalloc"}
+                          "gdn_recurrent_seq_noalloc", "gdn_mixed_launches", "gdn_mixed_step_launches"}
     for n in names:
         assert hasattr(so, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "linear_attention_ssm_gdn_amd",
@@ -346,6 +346,56 @@ def test_mixed_step_validation(so, L):
         assert call(seq=sp) == 1, (pages, nbytes)
     sp.spec_pages, sp.spec_page_bytes = FAKE, lay.page_bytes
     assert call(seq=sp) == 0                                     # empty batch: validated, nothing launched
+
+
+def test_mixed_step_launch_count(so, L):
+    """gdn_mixed_launches: two launches exactly when both parts are non-empty,
+    every sequence has 1-4 rows, no speculative pages are written and d_v is
+    a multiple of 64 (the short-sequence kernel's shapes); gdn_mixed_step_launches
+    takes AUTO, ONE or TWO and rejects anything else before launching."""
+    C = 2 * 16 * 128 + 32 * 128
+    lay = L.GdnSpecLayout()
+    d = _dims(L)
+    assert so.gdn_spec_page_layout(ctypes.byref(d), 0, ctypes.byref(lay)) == 0
+    sa = _seq_args(L, d)
+
+    def seq_part(max_seqlen, n_seqs=2, spec=False):
+        b = L.GdnBatch(FAKE, FAKE, None, n_seqs, max_seqlen, 4 * max(n_seqs, 1))
+        sp = L.GdnSeqPart(FAKE, C, FAKE, FAKE, 32, ctypes.pointer(b), L.GdnConvPool(FAKE, 10 * C, 10, 4, FAKE),
+                          sa["state"], FAKE)
+        sp._batch = b
+        if spec:
+            sp.spec_pages, sp.spec_page_bytes, sp.spec_n_pages = FAKE, lay.page_bytes, 4
+        return sp
+
+    def ver_part(n_req=2):
+        return L.GdnVerifyPart(0, FAKE, C, FAKE, FAKE, 32, n_req, 8, FAKE, FAKE, FAKE, FAKE, lay.page_bytes, 4,
+                               L.GdnConvPool(FAKE, 10 * C, 10, 4, FAKE), FAKE)
+
+    def launches(seq=None, ver=None, dims=d):
+        out = ctypes.c_int32(-1)
+        st = so.gdn_mixed_launches(ctypes.byref(dims), ctypes.byref(seq) if seq is not None else None,
+                                   ctypes.byref(ver) if ver is not None else None, ctypes.byref(out))
+        assert st == 0
+        return out.value
+    ONE, TWO = L.GDN_MIXED_ONE_LAUNCH, L.GDN_MIXED_TWO_LAUNCHES
+    for m in (1, 2, 3, 4):
+        assert launches(seq_part(m), ver_part()) == TWO, m
+    assert launches(seq_part(5), ver_part()) == ONE
+    assert launches(seq_part(0), ver_part()) == ONE                # longest length not given
+    assert launches(seq_part(1, spec=True), ver_part()) == ONE     # the prefill writes page headers
+    assert launches(seq_part(1), ver_part(n_req=0)) == ONE
+    assert launches(seq_part(1, n_seqs=0), ver_part()) == ONE
+    assert launches(seq_part(1)) == ONE
+    assert launches(None, ver_part()) == ONE
+    assert launches(seq_part(1), ver_part(), dims=_dims(L, d_v=96)) == ONE
+    d96 = _dims(L)
+    assert so.gdn_mixed_launches(ctypes.byref(d96), None, None, None) == 1
+    params = L.GdnParams(FAKE, FAKE, FAKE)
+    for bad in (-1, 3):
+        assert so.gdn_mixed_step_launches(ctypes.byref(d), ctypes.byref(params), None, None, bad, None, None) == 1
+    for ok in (0, 1, 2):
+        assert so.gdn_mixed_step_launches(ctypes.byref(d), ctypes.byref(params), None, None, ok, None, None) == 0
 
 
 def test_conv_update_validation(so, L):

@@ -77,7 +77,7 @@ def _step_args(w, ws, wv, si, vi, step, seq_rows, seq_cu, pages, vstep):
     return seq, ver
 
 
-def _run(layout, state_dtype, fused, d_k=128, d_v=128):
+def _run(layout, state_dtype, fused, d_k=128, d_v=128, launches=0):
     ws, wv = _workloads(state_dtype, seed=71, d_k=d_k, d_v=d_v)
     si = wk.make_sequence_inputs(ws)
     vi = wk.make_verify_inputs(wv)
@@ -99,7 +99,7 @@ def _run(layout, state_dtype, fused, d_k=128, d_v=128):
         seq, ver = _step_args(w, ws, wv, sinp if sinp is not None else si, vi, step if vstep is None else vstep[0],
                               rows, scu, list(range(N_SEQ_PAGES)), vstep)
         if fused:
-            g.gdn_mixed_step(w.dims, w.params, seq=seq, verify=ver, err=w.err)
+            g.gdn_mixed_step(w.dims, w.params, seq=seq, verify=ver, err=w.err, launches=launches)
         else:
             if seq is not None:
                 g.gdn_recurrent_seq(w.dims, w.params, seq["x"], seq["a"], seq["b"], seq["batch"], w.conv, w.state,
@@ -114,9 +114,13 @@ def _run(layout, state_dtype, fused, d_k=128, d_v=128):
     return outs
 
 
+@pytest.mark.parametrize("launches", [0, 1, 2])
 @pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
-def test_mixed_step_equals_separate_launches(state_dtype):
-    fused = _run(0, state_dtype, fused=True)
+def test_mixed_step_equals_separate_launches(state_dtype, launches):
+    """Every launch choice (the library's, one grid, two launches) gives the
+    separate launches' results bit for bit; the step with decode rows is the
+    one the library runs as two launches."""
+    fused = _run(0, state_dtype, fused=True, launches=launches)
     sep = _run(0, state_dtype, fused=False)
     for step, ((so_f, vo_f, snap_f), (so_s, vo_s, snap_s)) in enumerate(zip(fused, sep)):
         for got, ref in ((so_f, so_s), (vo_f, vo_s)):
@@ -141,7 +145,7 @@ def test_mixed_step_slots_layout():
             assert torch.equal(got, ref)
 
 
-def _prefill_then_verify(state_dtype, via_spec_pages):
+def _prefill_then_verify(state_dtype, via_spec_pages, launches=0):
     """Prefill four sequences, then run verify steps on their pages.  Either
     the prefill writes straight into the speculative pages (state pool
     aliased onto the checkpoints, spec_pages set, headers left fresh), or it
@@ -168,7 +172,7 @@ def _prefill_then_verify(state_dtype, via_spec_pages):
         state = pages.checkpoint_pool()
         state.buf.copy_(dev(si["S0"], dims.state_torch))
         g.gdn_mixed_step(dims, params, seq=dict(x=x, a=a, b=b, batch=batch, conv=conv, state=state, o=o_pref,
-                                                spec_pages=pages), err=err)
+                                                spec_pages=pages), err=err, launches=launches)
     else:
         state = g.StatePool(dev(si["S0"], dims.state_torch))
         g.gdn_recurrent_seq(dims, params, x, a, b, batch, conv, state, o=o_pref, err=err)
@@ -193,9 +197,12 @@ def _prefill_then_verify(state_dtype, via_spec_pages):
     return outs, pages, conv, (ws, wv, si, vi)
 
 
+@pytest.mark.parametrize("launches", [0, 2])
 @pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
-def test_prefill_into_spec_pages_equals_copy_and_zero(state_dtype):
-    got, pages_a, conv_a, _ = _prefill_then_verify(state_dtype, True)
+def test_prefill_into_spec_pages_equals_copy_and_zero(state_dtype, launches):
+    """Also with two launches forced: the sequences then take the 32-column
+    kernel, which leaves the page headers fresh as the one grid does."""
+    got, pages_a, conv_a, _ = _prefill_then_verify(state_dtype, True, launches=launches)
     ref, pages_b, conv_b, _ = _prefill_then_verify(state_dtype, False)
     for g_, r_ in zip(got, ref):
         assert not torch.isnan(g_).any()
@@ -357,3 +364,19 @@ def test_mixed_step_at_the_benchmark_shape(ora):
                 ref = vo[step, r, :, h]
                 worst = max(worst, np.abs(outs[step][1][r, :, h] - ref).max() / np.abs(ref).max())
     assert worst <= 1e-4, worst
+
+
+def test_mixed_step_launch_choice_at_decode_and_prefill_shapes():
+    """The library picks two launches for a step whose sequences have at
+    most four rows each beside verify requests, one launch otherwise."""
+    g = gdn()
+    ws, wv = _workloads(wk.F32, seed=75)
+    si = wk.make_sequence_inputs(ws.replace(seqlens=(1, 5, 2, 3)))
+    vi = wk.make_verify_inputs(wv)
+    w = World(ws, wv, wk.make_sequence_inputs(ws), vi, 0)
+    for lens, want in (((1, 4, 2, 3), g.GDN_MIXED_TWO_LAUNCHES), ((1, 5, 2, 3), g.GDN_MIXED_ONE_LAUNCH)):
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        seq, ver = _step_args(w, ws, wv, si, vi, 0, (0, int(cu[-1])), cu, list(range(N_SEQ_PAGES)),
+                              (0, np.zeros(N_REQ, np.int32)))
+        assert g.gdn_mixed_launches(w.dims, seq=seq, verify=ver) == want, lens
+        assert g.gdn_mixed_launches(w.dims, seq=seq) == g.GDN_MIXED_ONE_LAUNCH
