@@ -170,8 +170,9 @@ const char* gdn_status_str(int32_t status);
 int32_t gdn_spec_page_layout(const gdn_dims* dims, int32_t layout, gdn_spec_layout* out);
 
 /* Workspace bytes gdn_chunked_prefill needs for this batch shape (host-only):
- * (n_seqs + ceil(n_rows / chunk)) chunk slots of h_k key-head and h_v
- * value-head records (about 145 KB per slot at h_k = 16, h_v = 32, d = 128). */
+ * (n_seqs + ceil(n_rows / chunk)) chunk slots of h_k key-head records
+ * (71 KB each at d = 128) and h_v value-head records (27.25 KB each): about
+ * 1.96 MiB per slot at h_k = 16, h_v = 32. */
 int32_t gdn_chunked_workspace_bytes(const gdn_dims* dims, int32_t n_seqs, int64_t n_rows,
                                     int32_t chunk, size_t* out_bytes);
 
@@ -233,8 +234,8 @@ int32_t gdn_recurrent_seq_noalloc(const gdn_dims* dims, const gdn_params* params
  * W = T diag(beta e^G) K, U = T diag(beta) V and the chunk-state update,
  * with bf16 matrix-core products accumulated in fp32.  chunk == 64 is
  * compiled.  Two launches on `stream`: the first writes every chunk's
- * state-independent operands (normalised q/k, T-derived W and (T - I)
- * diag(beta), the masked decayed Q K^T, gates) into the workspace, the
+ * state-independent operands (q and k rows and k^T, (T - I) diag(beta),
+ * the masked decayed Q K^T, gates and norm factors) into the workspace, the
  * second runs each sequence's chunk-to-chunk state chain from them.
  * workspace: caller-owned device memory of at least
  * gdn_chunked_workspace_bytes bytes, 256-byte aligned, else GDN_ERR_ARG; its

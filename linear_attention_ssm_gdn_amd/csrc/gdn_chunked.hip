@@ -16,22 +16,25 @@
 //       (k_t.k_s) e^{G_t-G_s} for s < t, masked before the exponential; the
 //       UT transform T = (I + A)^{-1} (16x16 diagonal blocks by the doubling
 //       identity (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8), then the three block
-//       sub-diagonals); W = T diag(beta e^G rk) K (exact diagonal + MFMA for
-//       T - I).  All of it goes to the chunk's workspace records.
-// k_chunk_state: one workgroup of 4 waves per (sequence, value head, 64 value
-// columns); wave w owns columns 16w .. 16w+15 and its share of the fp32 state
-// S (128 x 16) in MFMA accumulator registers for the whole sequence.  Chunks
-// run in order, their records streamed into LDS one step ahead:
+//       sub-diagonals) and (T - I) diag(beta).  All of it goes to the chunk's
+//       workspace records.
+// k_chunk_state: one workgroup of 8 waves per (sequence, value head, 64 value
+// columns): four waves hold the fp32 state S (128 x 16 columns each) and run
+// the chain, four run the v conv and the outputs (details at the kernel).
+// Chunks run in order, their records streamed into LDS one step ahead:
 //   v conv + SiLU (4 channels x 4 tokens per thread) into a transposed hi/lo tile;
-//   D = U - W S = diag(beta) V + (T - I) diag(beta) V - W S;
+//   D = U - W S with the WY matrices U = T diag(beta) V and W = T diag(beta
+//       e^G rk) K, computed as D = T diag(beta) E, E = V - diag(e^G rk) K S:
+//       one product K S, then D = beta E + (T - I) diag(beta) E, so W is
+//       never formed;
 //   O = diag(e^G rq) Q S + diag(k.q) D + P D;
 //   S <- e^{G_last} S + K^T diag(rk e^{G_last-G}) D, the chunk's last row as
 //   an exact fp32 outer product.
 // Rounding points were chosen by emulating the error against the fp64
 // recurrence: single bf16 roundings that multiply a weight-one term (the
-// diagonal of T and of Q K^T, the last row of the state update) would cost up
-// to 2^-8 each, so those terms stay fp32, and P, D and K take hi/lo splits in
-// the products where they dominate.
+// diagonal of T and of Q K^T, the last row of the state update, beta E) would
+// cost up to 2^-8 each, so those terms stay fp32, and P, D, E and K take
+// hi/lo splits in the products where they dominate.
 #include "gdn_block.hpp"
 #include "gdn_kernels.h"
 #include "../../include/gdn.h"
@@ -53,19 +56,18 @@ constexpr int LT = 72;         // bf16 row stride of [..][64] arrays
 constexpr int LAF = 68;        // fp32 row stride of A [64][64]
 
 // LDS of the prep kernel (bytes): token-major q and k hi/lo; after the
-// products the k regions hold T and LTbg, the q-lo region A and then -W.
+// products the k hi region holds T, the q-lo region A.
 constexpr int SZ_TOK = CH * LQK * 2;          // 17408
 constexpr int SZ_REG = 18432;                  // regions that later hold two [64][72] bf16 arrays
 constexpr int OFF_QH = 0;
-constexpr int OFF_KH = OFF_QH + SZ_TOK;        // then T (first half) + LTbg (second half)
-constexpr int OFF_QL = OFF_KH + SZ_REG;        // then A (fp32), then -W
+constexpr int OFF_KH = OFF_QH + SZ_TOK;        // then T
+constexpr int OFF_QL = OFF_KH + SZ_REG;        // then A (fp32)
 constexpr int OFF_KL = OFF_QL + SZ_REG;
 constexpr int PREP_LDS = OFF_KL + SZ_REG;
 static_assert(CH * LAF * 4 <= SZ_REG && CH * LQK * 2 <= SZ_REG && 2 * CH * LT * 2 <= SZ_REG, "region sizes");
-static_assert(DK * CH * 2 <= SZ_TOK && DK * CH * 2 <= SZ_REG, "k^T hi/lo fit the q hi and k lo regions");
 
 // scalar rows in the SC block
-enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
+enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_WDR, SC_G };
 
 // A vector instruction that reads a matrix-core result must not issue
 // within the product's write-back.  The compiler schedules such reads (or the
@@ -85,10 +87,6 @@ enum { SC_RQ = 0, SC_RK, SC_KQ, SC_BETA, SC_GAM, SC_BGR, SC_WDR, SC_G };
 // states, which depend on every UT solve, never differed.
 #define GDN_SETTLE_NOPS "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
 __device__ __forceinline__ void settle(f32x4& a, f32x4& b) { asm volatile(GDN_SETTLE_NOPS : "+a"(a), "+a"(b)); }
-__device__ __forceinline__ void settle8(f32x4 (&a)[8]) {
-    asm volatile(GDN_SETTLE_NOPS : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]),
-                 "+a"(a[6]), "+a"(a[7]));
-}
 // The same wait on accumulators held in architectural registers (kernels
 // whose register budget is shared by two waves per SIMD keep MFMA results
 // there rather than split the budget with accumulator registers).
@@ -185,21 +183,22 @@ template <int N> struct RowVec<float, N> {
 // holds h_k key-head records, then h_v value-head records, in the LDS
 // layouts the state kernel reads.
 constexpr int KR_QH = 0;                         // bf16 [64][LQK]: q hi
-constexpr int KR_KTH = KR_QH + CH * LQK * 2;     // bf16 [128][LT]: k^T hi
+constexpr int KR_KH = KR_QH + CH * LQK * 2;      // bf16 [64][LQK]: k hi
+constexpr int KR_KTH = KR_KH + CH * LQK * 2;     // bf16 [128][LT]: k^T hi
 constexpr int KR_KTL = KR_KTH + DK * LT * 2;     // bf16 [128][LT]: k^T lo
 constexpr int KR_KLAST = KR_KTL + DK * LT * 2;   // fp32 [128]: rk k of the chunk's last row
 constexpr int KR_RQ = KR_KLAST + DK * 4;         // fp32 [64]: rq (with the output scale)
 constexpr int KR_KQ = KR_RQ + CH * 4;            // fp32 [64]: rq rk (q.k) of each row
-constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 55296
-constexpr int VR_WM = 0;                         // bf16 [64][LQK]: -W
-constexpr int VR_LTB = VR_WM + CH * LQK * 2;     // bf16 [64][64] (sw64): (T - I) diag(beta)
+constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 72704
+constexpr int VR_LTB = 0;                        // bf16 [64][64] (sw64): (T - I) diag(beta)
 constexpr int VR_BETA = VR_LTB + CH * CH * 2;    // fp32 [64]
-constexpr int VR_PH = VR_BETA + CH * 4;          // bf16 [64][LT]: P hi (tiles on or below the diagonal)
+constexpr int VR_GRK = VR_BETA + CH * 4;         // fp32 [64]: e^G rk
+constexpr int VR_PH = VR_GRK + CH * 4;           // bf16 [64][LT]: P hi (tiles on or below the diagonal)
 constexpr int VR_PL = VR_PH + CH * LT * 2;       // bf16 [64][LT]: P lo
 constexpr int VR_GRQ = VR_PL + CH * LT * 2;      // fp32 [64]: e^G rq
 constexpr int VR_GAM = VR_GRQ + CH * 4;          // fp32 [64]: e^G
 constexpr int VR_WDR = VR_GAM + CH * 4;          // fp32 [64]: rk e^{G_last - G}, 0 for the last row
-constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 45056, a multiple of 256
+constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 27904, a multiple of 256
 static_assert(VREC_BYTES % 256 == 0 && KREC_BYTES % 256 == 0, "records keep 256-byte alignment");
 static_assert(VR_WDR + CH * 4 <= VREC_BYTES && KREC_BYTES % 256 == 0 && VREC_BYTES % 256 == 0, "records");
 
@@ -210,7 +209,7 @@ __device__ __forceinline__ int64_t chunk_slot(int seq, int r0, int c) { return (
 // read the lanes {0-7, 24-31} and {8-15, 16-23} of each half wave (measured
 // with the bank-conflict counter).  An MFMA operand read takes row lr = lane
 // & 15 and column group lg = lane >> 4.
-//  - [rows][LT] (k^T, P) and [rows][LQK] (q, -W): 8-byte reads of rows 36
+//  - [rows][LT] (k^T, P) and [rows][LQK] (q, k): 8-byte reads of rows 36
 //    (68) words apart fill all 64 banks for every 32 lanes.
 //  - sw64 ([rows][64], LTb and the v tile, read both 8 and 16 bytes wide):
 //    rows 128 bytes apart, the 16-byte column group XORed with (row >> 1) & 7;
@@ -286,10 +285,8 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
     __bf16* Kh = reinterpret_cast<__bf16*>(lds + OFF_KH);
     __bf16* Ql = reinterpret_cast<__bf16*>(lds + OFF_QL);
     __bf16* Kl = reinterpret_cast<__bf16*>(lds + OFF_KL);
-    float* Af = reinterpret_cast<float*>(lds + OFF_QL);                    // after Q K^T
-    __bf16* Tm = reinterpret_cast<__bf16*>(lds + OFF_KH);                  // after Q K^T
-    __bf16* LTbg = reinterpret_cast<__bf16*>(lds + OFF_KH + CH * LT * 2);  // after the UT solve
-    __bf16* Wm = reinterpret_cast<__bf16*>(lds + OFF_QL);                  // -W, once A is dead
+    float* Af = reinterpret_cast<float*>(lds + OFF_QL);    // after Q K^T
+    __bf16* Tm = reinterpret_cast<__bf16*>(lds + OFF_KH);  // after Q K^T
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // Chunks are handed out last-first, so the records the state kernel reads
@@ -414,9 +411,10 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
         }
     }
     lds_barrier();
-    // ---- the key head's record: q hi, the last row of rk k (the same bits
-    // as k^T holds), rq; k^T went there from the conv
+    // ---- the key head's record: q hi, k hi, the last row of rk k (the same
+    // bits as k^T holds), rq; k^T went there from the conv
     copy_from_lds(lds + OFF_QH, krec + KR_QH, CH * LQK * 2, tid);
+    copy_from_lds(lds + OFF_KH, krec + KR_KH, CH * LQK * 2, tid);
     if (tid < DK) {
         const int d = tid, tl = n - 1;
         reinterpret_cast<float*>(krec + KR_KLAST)[d] =
@@ -469,38 +467,6 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
     }
     lds_barrier();  // every product read of Q, K (token-major) is done; KQ is published
     if (tid < CH) reinterpret_cast<float*>(krec + KR_KQ)[tid] = sc[SC_KQ * CH + tid];
-    // ---- k^T hi/lo into LDS for the W phases ([128][64], sw64), transposed
-    // from the token-major k rows: hi into q hi's region (q hi is in the
-    // record), lo over k lo's own region once every lane has read it.  Item
-    // i = tid + 256 p: channel i & 127, tokens 8 (i >> 7) .. +7.
-    __bf16* KTsh = reinterpret_cast<__bf16*>(lds + OFF_QH);
-    __bf16* KTsl = reinterpret_cast<__bf16*>(lds + OFF_KL);
-    {
-        u32x4 lo_items[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int i = tid + NTH * p, d = i & (DK - 1), t0 = 8 * (i >> 7);
-            u32x4 hv, lv;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const __bf16* h0 = Kh + (t0 + 2 * m) * LQK + d;
-                const __bf16* l0 = Kl + (t0 + 2 * m) * LQK + d;
-                hv[m] = (uint32_t)__builtin_bit_cast(uint16_t, h0[0]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, h0[LQK]) << 16);
-                lv[m] = (uint32_t)__builtin_bit_cast(uint16_t, l0[0]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, l0[LQK]) << 16);
-            }
-            *reinterpret_cast<u32x4*>(KTsh + sw64(d, t0)) = hv;
-            lo_items[p] = lv;
-        }
-        lds_barrier();  // every read of k lo is done
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int i = tid + NTH * p, d = i & (DK - 1), t0 = 8 * (i >> 7);
-            *reinterpret_cast<u32x4*>(KTsl + sw64(d, t0)) = lo_items[p];
-        }
-    }
-
     for (int jv = 0; jv < rr; ++jv) {
         const int h = ki * rr + jv;
         unsigned char* vrec = slot + (int64_t)A.h_k * KREC_BYTES + (int64_t)h * VREC_BYTES;
@@ -526,12 +492,12 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             sc[SC_G * CH + t] = G * LOG2E;
             sc[SC_BETA * CH + t] = beta;
             sc[SC_GAM * CH + t] = gam;
-            sc[SC_BGR * CH + t] = beta * gam * rk;
             // the last row of the chunk enters the state update exactly, not through the MFMA
             const float wdr = (t == n - 1) ? 0.0f : expf(Glast - G) * rk;
             sc[SC_WDR * CH + t] = wdr;
             float* vs = reinterpret_cast<float*>(vrec);
             vs[VR_BETA / 4 + t] = beta;
+            vs[VR_GRK / 4 + t] = gam * rk;
             vs[VR_GRQ / 4 + t] = gam * sc[SC_RQ * CH + t];
             vs[VR_GAM / 4 + t] = gam;
             vs[VR_WDR / 4 + t] = wdr;
@@ -611,7 +577,7 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             }
             lds_barrier();
         }
-        // LT = T - I (strictly lower), column-scaled by beta and by beta e^G rk
+        // LT = T - I (strictly lower), column-scaled by beta
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             const int e = tid + NTH * pass;
@@ -619,63 +585,14 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             const bf16x8 tv = *reinterpret_cast<const bf16x8*>(Tm + t * LT + s0);
             const f32x4 b0 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0);
             const f32x4 b1 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0 + 4);
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + s0);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + s0 + 4);
             float lt[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) lt[k] = s0 + k < t ? (float)tv[k] : 0.0f;
             const u32x4 ob = {pack_bf2(lt[0] * b0[0], lt[1] * b0[1]), pack_bf2(lt[2] * b0[2], lt[3] * b0[3]),
                               pack_bf2(lt[4] * b1[0], lt[5] * b1[1]), pack_bf2(lt[6] * b1[2], lt[7] * b1[3])};
-            const u32x4 og = {pack_bf2(lt[0] * g0[0], lt[1] * g0[1]), pack_bf2(lt[2] * g0[2], lt[3] * g0[3]),
-                              pack_bf2(lt[4] * g1[0], lt[5] * g1[1]), pack_bf2(lt[6] * g1[2], lt[7] * g1[3])};
-            *reinterpret_cast<u32x4*>(LTbg + t * LT + s0) = og;
             *reinterpret_cast<u32x4*>(vrec + VR_LTB + sw64(t, s0) * 2) = ob;
         }
-        lds_barrier();  // LTbg, and (first value head) k^T in LDS
-        // ---- W[t][d] = bgr_t K[t][d] + (LTbg K)[t][d]; 32 tiles, 8 per wave
-        {
-            f32x4 wacc[8];
-            // four tiles at a time: their k^T reads are issued together, ahead
-            // of the products
-#pragma unroll
-            for (int kb = 0; kb < 8; kb += 4) {
-                bf16x4 kh[4], kl[4];
-                bf16x8 bop[4][2];
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
-                    const int idx = wvs + 4 * (kb + k4), mt = idx >> 3, dt = idx & 7;
-                    const int d = 16 * dt + lr;
-                    const int ko = sw64(d, 16 * mt + 4 * lg);
-                    kh[k4] = *reinterpret_cast<const bf16x4*>(KTsh + ko);
-                    kl[k4] = *reinterpret_cast<const bf16x4*>(KTsl + ko);
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        bop[k4][ks] = *reinterpret_cast<const bf16x8*>(KTsh + sw64(d, 32 * ks + 8 * lg));
-                }
-                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
-                    const int k = kb + k4, idx = wvs + 4 * k, mt = idx >> 3;
-                    const f32x4 bg = *reinterpret_cast<const f32x4*>(sc + SC_BGR * CH + 16 * mt + 4 * lg);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) wacc[k][j] = bg[j] * ((float)kh[k4][j] + (float)kl[k4][j]);
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        wacc[k] = mma32(ld8(LTbg, LT, 16 * mt + lr, 32 * ks + 8 * lg), bop[k4][ks], wacc[k]);
-                }
-            }
-            settle8(wacc);
-            // A (same region) is dead since the LT pass
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int idx = wvs + 4 * k, mt = idx >> 3, dt = idx & 7;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Wm[(16 * mt + 4 * lg + j) * LQK + 16 * dt + lr] = (__bf16)(-wacc[k][j]);
-            }
-        }
-        lds_barrier();
-        copy_from_lds(reinterpret_cast<const unsigned char*>(Wm), vrec + VR_WM, CH * LQK * 2, tid);
-        lds_barrier();  // Wm (A's region) and the scalars are rewritten by the next value head
+        lds_barrier();  // T, A and the scalars are rewritten by the next value head
     }
 }
 
@@ -686,7 +603,7 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
 // state and D that the chain hands over in LDS, so the two interleave on
 // every SIMD.  Wave w of either side owns value columns 16 (w & 3) .. +15 of
 // the block.  A chunk takes two steps, each closed by a barrier:
-//   step A(c)  chain:  refill G4 <- chunk c;  D(c) = U - W S(c)
+//   step A(c)  chain:  refill G4 <- chunk c;  D(c) = T diag(beta) (V - diag(e^G rk) K S(c))
 //              output: x rows of chunk c+1 -> registers;  Q S(c);  O(c-1)
 //   step B(c)  chain:  refill G1 <- chunk c+1;  D(c) -> LDS;  S(c+1);
 //                      hi(S(c+1)) -> LDS
@@ -695,15 +612,18 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
 // barrier that ends the last read of its buffer and is awaited (vector
 // memory count 0 in the waves that issued it) before the barrier that
 // precedes its first read.
-//   G1 (D = U - W S): -W, LTb, beta         <- value-head record [0, VR_PH)
+//   G1 (D):           LTb, beta, e^G rk     <- value-head record [0, VR_PH)
+//                     k hi                  <- key-head record [KR_KH, KR_KTH)
 //   G2 (Q S):         q hi                  <- key-head record [0, KR_KTH)
 //   G4 (S update):    k^T hi/lo, klast      <- key-head record [KR_KTH, KR_RQ)
 //                     gam, wdr              <- value-head record [VR_GAM, VR_WDR + 256)
 //   G3 (P D, output): P hi/lo, e^G rq       <- value-head record [VR_PH, VR_GAM)
 //                     kq                    <- key-head record [KR_KQ, KREC_BYTES)
 constexpr int SNTH = 512;                              // threads of the state kernel
-constexpr int G1_BYTES = VR_PH;                        // 25856
-constexpr int G2_BYTES = KR_KTH;                       // 17408
+constexpr int G1V_BYTES = VR_PH;                       // 8704
+constexpr int G1K_BYTES = KR_KTH - KR_KH;              // 17408
+constexpr int G1_BYTES = G1V_BYTES + G1K_BYTES;
+constexpr int G2_BYTES = KR_KH;                        // 17408
 constexpr int G4K_BYTES = KR_RQ - KR_KTH;              // 37376
 constexpr int G4V_BYTES = VR_WDR + CH * 4 - VR_GAM;    // 512
 constexpr int G3V_BYTES = VR_GAM - VR_PH;              // 18688
@@ -731,9 +651,10 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     __shared__ __attribute__((aligned(16))) bf16x8 Sx[4 * 4 * 64];  // hi(S) operand: (chain wave, k step, lane)
     __shared__ __attribute__((aligned(16))) float wv4[BVC * 4];
     __shared__ int sh_last;
-    const __bf16* Wm = reinterpret_cast<const __bf16*>(g1s + VR_WM);
     const __bf16* LTb = reinterpret_cast<const __bf16*>(g1s + VR_LTB);
     const float* sbeta = reinterpret_cast<const float*>(g1s + VR_BETA);
+    const float* sgrk = reinterpret_cast<const float*>(g1s + VR_GRK);
+    const __bf16* Kr = reinterpret_cast<const __bf16*>(g1s + G1V_BYTES);
     const __bf16* Qh = reinterpret_cast<const __bf16*>(g2s);
     const __bf16* KTh = reinterpret_cast<const __bf16*>(g4s);
     const __bf16* KTl = reinterpret_cast<const __bf16*>(g4s + DK * LT * 2);
@@ -819,7 +740,10 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         return ws + chunk_slot(seq, r0, c) * slot_bytes + (int64_t)A.h_k * KREC_BYTES + (int64_t)h * VREC_BYTES;
     };
     // refills, each split over the four waves of the side that reads it
-    auto fill_g1 = [&](int c) { copy_to_lds<G1_BYTES>(vrec(c), g1s, w4, lane); };
+    auto fill_g1 = [&](int c) {
+        copy_to_lds<G1V_BYTES>(vrec(c), g1s, w4, lane);
+        copy_to_lds<G1K_BYTES>(krec(c) + KR_KH, g1s + G1V_BYTES, w4, lane);
+    };
     auto fill_g4 = [&](int c) {
         copy_to_lds<G4K_BYTES>(krec(c) + KR_KTH, g4s, w4, lane);
         copy_to_lds<G4V_BYTES>(vrec(c) + VR_GAM, g4s + G4K_BYTES, w4, lane);
@@ -990,43 +914,68 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         const int colv = 16 * w4 + lr;
         for (int ci = 0; ci < nch; ++ci) {
             const int n = (T - ci * CH < CH) ? (T - ci * CH) : CH;
-            // ================================ step A: D = U - W S = beta V + LTb V + (-W) S
+            // ================================ step A: D = U - W S with W = T diag(beta e^G rk) K, computed
+            // as D = T diag(beta) E, E = V - diag(e^G rk) K S: Z = K S, then
+            // D = beta E + LTb E with E split hi/lo (LTb = (T - I) diag(beta))
             fill_g4(ci);
-            f32x4 D[4];
-            bf16x8 vb[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) vb[ks] = *reinterpret_cast<const bf16x8*>(VTh + sw64(colv, 32 * ks + 8 * lg));
-            // two row tiles at a time: their operands are read before their products
+            f32x4 Z[4], D[4];
+            const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+            // two row tiles at a time: their k reads are issued before their products
 #pragma unroll
             for (int mp = 0; mp < 4; mp += 2) {
-                bf16x4 vh[2], vl[2];
-                f32x4 bt[2];
-                bf16x8 la[2][2], wa[2][4];
+                bf16x8 ka[2][4];
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2) {
-                    const int mt = mp + m2, t0 = 16 * mt + 4 * lg;
-                    vh[m2] = *reinterpret_cast<const bf16x4*>(VTh + sw64(colv, t0));
-                    vl[m2] = *reinterpret_cast<const bf16x4*>(VTl + sw64(colv, t0));
-                    bt[m2] = *reinterpret_cast<const f32x4*>(sbeta + t0);
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        la[m2][ks] = *reinterpret_cast<const bf16x8*>(LTb + sw64(16 * mt + lr, 32 * ks + 8 * lg));
+                    const int mt = mp + m2;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        wa[m2][kk] = cat8(ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 4 * lg),
-                                          ld4s(Wm + (16 * mt + lr) * LQK + 32 * kk + 16 + 4 * lg));
+                        ka[m2][kk] = cat8(ld4s(Kr + (16 * mt + lr) * LQK + 32 * kk + 4 * lg),
+                                          ld4s(Kr + (16 * mt + lr) * LQK + 32 * kk + 16 + 4 * lg));
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2) {
-                    f32x4 u;
+                    f32x4 z = zero4;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) u[j] = bt[m2][j] * ((float)vh[m2][j] + (float)vl[m2][j]);
+                    for (int kk = 0; kk < 4; ++kk) z = mma32(ka[m2][kk], sb[kk], z);
+                    Z[mp + m2] = z;
+                }
+            }
+            // the LTb operands (K index permuted as E's: lane group lg supplies
+            // rows 32 ks + 4 lg + 0..3 and 32 ks + 16 + 4 lg + 0..3); LTb is
+            // strictly lower triangular, so row tiles 0 and 1 need ks = 0 only
+            bf16x8 la[4][2];
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) u = mma32(la[m2][ks], vb[ks], u);
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) u = mma32(wa[m2][kk], sb[kk], u);
-                    D[mp + m2] = u;
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks > 0 && mt < 2) continue;
+                    la[mt][ks] = cat8(ld4s(LTb + sw64(16 * mt + lr, 32 * ks + 4 * lg)),
+                                      ld4s(LTb + sw64(16 * mt + lr, 32 * ks + 16 + 4 * lg)));
+                }
+            settle4_v(Z);
+            bf16x4 eh[4], el[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int t0 = 16 * mt + 4 * lg;
+                const bf16x4 vh = *reinterpret_cast<const bf16x4*>(VTh + sw64(colv, t0));
+                const bf16x4 vl = *reinterpret_cast<const bf16x4*>(VTl + sw64(colv, t0));
+                const f32x4 grk = *reinterpret_cast<const f32x4*>(sgrk + t0);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(sbeta + t0);
+                f32x4 e;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) e[j] = ((float)vh[j] + (float)vl[j]) - grk[j] * Z[mt][j];
+                split4(e, eh[mt], el[mt]);
+                D[mt] = bt * e;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 ebh = cat8(eh[2 * ks], eh[2 * ks + 1]), ebl = cat8(el[2 * ks], el[2 * ks + 1]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    if (ks > 0 && mt < 2) continue;
+                    D[mt] = mma32(la[mt][ks], ebh, D[mt]);
+                    D[mt] = mma32(la[mt][ks], ebl, D[mt]);
                 }
             }
             settle4_v(D);
