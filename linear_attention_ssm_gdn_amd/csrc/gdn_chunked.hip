@@ -339,6 +339,18 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
                 nqk[j].zero();
         }
     }
+    // the gate inputs of the key head's first two value heads (wave 0, lane =
+    // token), issued with the x rows so that their latency hides under the conv
+    float ga0 = 0.0f, gb0 = 0.0f, ga1 = 0.0f, gb1 = 0.0f;
+    if (wv == 0) {
+        const int64_t row = (int64_t)(r0 + c0 + (lane < n ? lane : n - 1)) * A.ab_stride + (int64_t)ki * rr;
+        ga0 = to_f32(static_cast<const ActT*>(A.a)[row]);
+        gb0 = to_f32(static_cast<const ActT*>(A.b)[row]);
+        if (rr > 1) {
+            ga1 = to_f32(static_cast<const ActT*>(A.a)[row + 1]);
+            gb1 = to_f32(static_cast<const ActT*>(A.b)[row + 1]);
+        }
+    }
     __syncthreads();
     // ---- conv + SiLU of q and k (log2(e)-scaled), hi/lo rows, k^T, norms
     {
@@ -475,8 +487,8 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             const int t = lane;
             const int tt = c0 + (t < n ? t : n - 1);
             const int64_t row = (int64_t)(r0 + tt) * A.ab_stride + h;
-            const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
-            const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
+            const float av = jv == 0 ? ga0 : jv == 1 ? ga1 : to_f32(static_cast<const ActT*>(A.a)[row]);
+            const float bv = jv == 0 ? gb0 : jv == 1 ? gb1 : to_f32(static_cast<const ActT*>(A.b)[row]);
             const float exp_alog = expf(A.a_log[h]);
             const float g = t < n ? -exp_alog * softplus(av + A.dt_bias[h]) : 0.0f;
             const float beta = t < n ? sigmoid(bv) : 0.0f;
