@@ -224,6 +224,22 @@ __device__ __forceinline__ void sload_u32_n<6>(const void* const (&p)[6], uint32
         : "s"(p[0]), "s"(p[1]), "s"(p[2]), "s"(p[3]), "s"(p[4]), "s"(p[5])
         : "memory");
 }
+template <>
+__device__ __forceinline__ void sload_u32_n<8>(const void* const (&p)[8], uint32_t (&a)[8]) {
+    asm volatile(
+        "s_load_dword %0, %8, 0x0\n\t"
+        "s_load_dword %1, %9, 0x0\n\t"
+        "s_load_dword %2, %10, 0x0\n\t"
+        "s_load_dword %3, %11, 0x0\n\t"
+        "s_load_dword %4, %12, 0x0\n\t"
+        "s_load_dword %5, %13, 0x0\n\t"
+        "s_load_dword %6, %14, 0x0\n\t"
+        "s_load_dword %7, %15, 0x0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(a[0]), "=&s"(a[1]), "=&s"(a[2]), "=&s"(a[3]), "=&s"(a[4]), "=&s"(a[5]), "=&s"(a[6]), "=&s"(a[7])
+        : "s"(p[0]), "s"(p[1]), "s"(p[2]), "s"(p[3]), "s"(p[4]), "s"(p[5]), "s"(p[6]), "s"(p[7])
+        : "memory");
+}
 __device__ __forceinline__ int32_t sload_i32(const int32_t* p) { return (int32_t)sload_u32(p); }
 __device__ __forceinline__ float sload_f32(const float* p) { return __uint_as_float(sload_u32(p)); }
 // One byte: the aligned dword that holds it (same page, so always mapped).

@@ -67,18 +67,32 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
     }
     uint8_t* pg = A.pages + (int64_t)page * A.page_bytes;
     gdn_spec_header* hdr = reinterpret_cast<gdn_spec_header*>(pg + A.header_off);
-    const uint32_t flag = hdr->flag;
+    // The header words, the step parity, the acceptance and the head's decay
+    // parameters in one batch of scalar loads (uniform addresses; one wait
+    // instead of a dependent vector load and wait each).  The live slot and
+    // parity bits change only when the request's last workgroup flips the
+    // flag, after every workgroup of the request has read it, and a launch
+    // starts with the scalar cache clean.
+    uint32_t hw[8];
+    const uintptr_t par_addr = reinterpret_cast<uintptr_t>(A.step_parity + req);
+    {
+        const void* const ptrs[8] = {&hdr->flag, &hdr->n_rows[0], &hdr->n_rows[1], A.num_accepted + req,
+                                     reinterpret_cast<const void*>(par_addr & ~(uintptr_t)3), A.a_log + h,
+                                     A.dt_bias + h, A.req_page + req};
+        sload_u32_n<8>(ptrs, hw);
+    }
+    const uint32_t flag = hw[0];
     const int L = (int)(flag & 1u);
     const int P = (int)((flag >> 1) & 1u);
-    const int nr = (int)hdr->n_rows[L];
-    const int par = A.step_parity[req] & 1;
+    const int nr = (int)(L ? hw[2] : hw[1]);
+    const int par = (int)((hw[4] >> ((par_addr & 3u) * 8u)) & 1u);
     if (par == P) {
         if (reporter) set_err(A.err, GDN_DEVERR_PARITY);
         return;
     }
     int acc = 0;
     if (nr > 0) {
-        acc = A.num_accepted[req];
+        acc = (int32_t)hw[3];
         if (acc < 0 || acc >= nr || nr > A.n_spec + 1) {
             if (reporter) set_err(A.err, GDN_DEVERR_ACCEPTED);
             return;
@@ -117,33 +131,39 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
 
     // ---- this thread's conv channel: weights, window rows acc..acc+2 of the conv buffer
     ActT* __restrict__ cbuf = static_cast<ActT*>(A.conv_base) + (int64_t)page * A.conv_page_stride;
+    // Every small input is loaded raw first and converted only once all of
+    // them are in flight, so they share one wait.
     const int lc = tid;
     int64_t gc = -1;
     float w[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xw0 = 0.0f, xw1 = 0.0f, xw2 = 0.0f;
-    if (lc < NLC) {
+    if (lc < NLC)
         gc = lc < DK ? (int64_t)ki * DK + lc
            : lc < 2 * DK ? (int64_t)A.h_k * DK + (int64_t)ki * DK + (lc - DK)
            : 2 * (int64_t)A.h_k * DK + (int64_t)h * A.d_v + colbase + (lc - 2 * DK);
-        const ActT* Wc = static_cast<const ActT*>(A.conv_w) + gc * 4;
+    // unconditional (threads without a channel read channel 0 and drop it):
+    // a load inside a branch would take its conversion, and its wait, with it
+    const int64_t gc0 = gc >= 0 ? gc : 0;
+    ActT wr[4], xr0, xr1, xr2;
+    {
+        const ActT* Wc = static_cast<const ActT*>(A.conv_w) + gc0 * 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = to_f32(Wc[e]);
-        xw0 = to_f32(cbuf[(int64_t)(acc + 0) * C + gc]);
-        xw1 = to_f32(cbuf[(int64_t)(acc + 1) * C + gc]);
-        xw2 = to_f32(cbuf[(int64_t)(acc + 2) * C + gc]);
+        for (int e = 0; e < 4; ++e) wr[e] = Wc[e];
+        xr0 = cbuf[(int64_t)(acc + 0) * C + gc0];
+        xr1 = cbuf[(int64_t)(acc + 1) * C + gc0];
+        xr2 = cbuf[(int64_t)(acc + 2) * C + gc0];
     }
     // the cached prefix's window: buffer rows cache_j .. cache_j+2
     float cw0 = 0.0f, cw1 = 0.0f, cw2 = 0.0f;
+    ActT cr0 = {}, cr1 = {}, cr2 = {};
     if constexpr (CACHE) {
-        if (cache_e >= 0 && lc < NLC) {
-            cw0 = to_f32(cbuf[(int64_t)(cache_j + 0) * C + gc]);
-            cw1 = to_f32(cbuf[(int64_t)(cache_j + 1) * C + gc]);
-            cw2 = to_f32(cbuf[(int64_t)(cache_j + 2) * C + gc]);
-        }
+        cr0 = cbuf[(int64_t)(cache_j + 0) * C + gc0];
+        cr1 = cbuf[(int64_t)(cache_j + 1) * C + gc0];
+        cr2 = cbuf[(int64_t)(cache_j + 2) * C + gc0];
     }
     float* ydst = lc < DK ? sq + qk_pos<DK>(lc) : lc < 2 * DK ? sk + qk_pos<DK>(lc - DK) : sv + (lc - 2 * DK);
     const int yld = lc < 2 * DK ? DK : BV;
-    float exp_alog_v = expf(A.a_log[h]);
-    float dtb = A.dt_bias[h];
+    float exp_alog_v = expf(__uint_as_float(hw[5]));
+    float dtb = __uint_as_float(hw[6]);
     asm volatile("" : "+v"(dtb));
     const float& exp_alog = exp_alog_v;
 
@@ -160,7 +180,10 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
     // ---- small inputs first, then the state: loads complete in order, so
     // everything above the state is usable while the state is in flight
     float xp[TT];
+    ActT xr[TT];
     float pa = 0.0f, pb = 0.0f;   // gate inputs of candidate cidx
+    ActT par_raw = {}, pbr_raw = {};
+    const bool cand_ok = cidx >= 0 && cidx < nc;
     const int64_t row_bytes = A.record_row_bytes;
     const int64_t rows_per_slot = A.n_spec + 1;
     float ra = 0.0f, rb = 0.0f;   // gate inputs of replayed row gtok
@@ -169,31 +192,6 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         const float* rrow = reinterpret_cast<const float*>(rec + (gtok < n_replay ? gtok : 0) * row_bytes);
         ra = rrow[C + h];
         rb = rrow[C + A.h_v + h];
-    }
-    {
-        // unconditional loads (row and channel clamped into range) stay in flight
-        // together; values past the candidates are zeroed
-        const ActT* X = static_cast<const ActT*>(A.x);
-        const int64_t gcl = gc >= 0 ? gc : 0;
-        if (nc > 0) {
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                const int t = tt < nc ? tt : nc - 1;
-                const float xv = to_f32(X[((int64_t)req * nc + t) * A.x_stride + gcl]);
-                xp[tt] = (gc >= 0 && tt < nc) ? xv : 0.0f;
-            }
-            {
-                const bool ok = cidx >= 0 && cidx < nc;
-                const int64_t row = ((int64_t)req * nc + (ok ? cidx : nc - 1)) * A.ab_stride + h;
-                const float av = to_f32(static_cast<const ActT*>(A.a)[row]);
-                const float bv = to_f32(static_cast<const ActT*>(A.b)[row]);
-                pa = ok ? av : 0.0f;
-                pb = ok ? bv : 0.0f;
-            }
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) xp[tt] = 0.0f;
-        }
     }
     // One-page: the replayed rows go straight into the LDS rows 0 .. n_replay-1,
     // all in flight at once: lane l of a wave lands at base + 4 l, and each
@@ -225,10 +223,46 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
                     ydst[i * yld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc];
         }
     }
+    {
+        // unconditional loads (row and channel clamped into range) stay in flight
+        // together; values past the candidates are zeroed
+        const ActT* X = static_cast<const ActT*>(A.x);
+        const int64_t gcl = gc >= 0 ? gc : 0;
+        if (nc > 0) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const int t = tt < nc ? tt : nc - 1;
+                xr[tt] = X[((int64_t)req * nc + t) * A.x_stride + gcl];
+            }
+            {
+                const int64_t row = ((int64_t)req * nc + (cand_ok ? cidx : nc - 1)) * A.ab_stride + h;
+                par_raw = static_cast<const ActT*>(A.a)[row];
+                pbr_raw = static_cast<const ActT*>(A.b)[row];
+            }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) xr[tt] = ActT{};
+        }
+    }
     // Every small input is taken (waited for) here, before the state's loads
     // are issued: a use after them would make the compiler wait for the
     // whole state, since it cannot count through the replay loop above.
     {
+        const bool has_ch = gc >= 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = has_ch ? to_f32(wr[e]) : 0.0f;
+        xw0 = has_ch ? to_f32(xr0) : 0.0f;
+        xw1 = has_ch ? to_f32(xr1) : 0.0f;
+        xw2 = has_ch ? to_f32(xr2) : 0.0f;
+        if constexpr (CACHE) {
+            cw0 = (has_ch && cache_e >= 0) ? to_f32(cr0) : 0.0f;
+            cw1 = (has_ch && cache_e >= 0) ? to_f32(cr1) : 0.0f;
+            cw2 = (has_ch && cache_e >= 0) ? to_f32(cr2) : 0.0f;
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) xp[tt] = (gc >= 0 && tt < nc) ? to_f32(xr[tt]) : 0.0f;
+        pa = cand_ok ? to_f32(par_raw) : 0.0f;
+        pb = cand_ok ? to_f32(pbr_raw) : 0.0f;
         float exp_pin = exp_alog;
         asm volatile("" : "+v"(exp_pin), "+v"(pa), "+v"(pb), "+v"(ra), "+v"(rb), "+v"(xw0), "+v"(xw1), "+v"(xw2));
         asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
