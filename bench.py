@@ -42,6 +42,7 @@ FP32_VALU_REACHABLE_TFLOPS = 78.6
 ROTATION_BYTES = 512 << 20       # bytes touched between two uses of one buffer copy
 MIN_POOLS = 2
 POOLS = 4                        # the dispatch sweep's state copies (its inputs are shared)
+WARM_S = 0.3                     # least untimed launch time before each secondary workload is timed
 LAST_PERCENTILES = {}  # per-launch kernel time percentiles (us) of the last measure()
 
 
@@ -293,9 +294,18 @@ class MixedWorkload:
         st[3] = n + 1
 
 
-def measure(torch, wload, steps, warmup):
-    for _ in range(warmup):
+def measure(torch, wload, steps, warmup, min_warm_s=0.0):
+    """Time `steps` launches after `warmup` untimed ones; with min_warm_s the
+    untimed launches go on until that much wall time has passed too (the
+    VALU-bound kernels run several percent slow for their first hundred or so
+    launches after the GPU has been idle)."""
+    t_w = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t_w < min_warm_s:
         wload.launch()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     timer = Timer(torch)
     t0 = time.perf_counter()
@@ -541,6 +551,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warm-s", type=float, default=WARM_S,
+                    help="least untimed launch time before each secondary workload is timed (0 for profiler runs)")
     ap.add_argument("--only", default="decode,short_prefill,long_prefill,spec_verify,mixed_step")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep-dispatch", action="store_true",
@@ -612,7 +624,7 @@ def main():
             wl = wk.SHORT_PREFILL
             log("short_prefill")
             w = SeqWorkload(g, torch, wl)
-            k_ms, wall_ms = measure(torch, w, max(args.steps // 4, 10), 5)
+            k_ms, wall_ms = measure(torch, w, max(args.steps // 4, 10), 5, args.warm_s)
             fl = recurrence_flops(wl)
             tf = fl / (k_ms * 1e-3) / 1e12
             other["short_prefill"] = {
@@ -634,7 +646,7 @@ def main():
             torch.cuda.empty_cache()
             try:
                 w = SeqWorkload(g, torch, wl, chunk=64)
-                c_ms, _ = measure(torch, w, max(args.steps // 4, 10), 5)
+                c_ms, _ = measure(torch, w, max(args.steps // 4, 10), 5, args.warm_s)
                 other["short_prefill"]["chunked_path"] = {
                     "value": round(wl.n_tokens / (c_ms * 1e-3)), "unit": "tokens/s/layer",
                     "us_per_call": round(c_ms * 1e3, 2), "us_per_call_percentiles": dict(LAST_PERCENTILES),
@@ -657,7 +669,7 @@ def main():
                                               wl.chunk)
                 log("long_prefill")
                 w = SeqWorkload(g, torch, wl, chunk=wl.chunk)
-                k_ms, wall_ms = measure(torch, w, max(args.steps // 20, 5), 2)
+                k_ms, wall_ms = measure(torch, w, max(args.steps // 20, 5), 2, args.warm_s)
                 fl = chunked_flops(wl)
                 tf = fl / (k_ms * 1e-3) / 1e12
                 other["long_prefill"] = {
@@ -688,7 +700,7 @@ def main():
             for sd in (wk.F32, wk.BF16):
                 log(f"spec_verify {sd}")
                 w = VerifyWorkload(g, torch, wl, sd)
-                k_ms, wall_ms = measure(torch, w, max(args.steps // 2, 10), 10)
+                k_ms, wall_ms = measure(torch, w, max(args.steps // 2, 10), 10, args.warm_s)
                 nb = verify_bytes(wl, sd, w.mean_replay)
                 gbs = nb / (k_ms * 1e-3) / 1e9
                 res[sd] = {"value": round(k_ms * 1e3, 2), "unit": "us/step", "us_per_step_percentiles": dict(LAST_PERCENTILES),
@@ -726,7 +738,7 @@ def main():
                 for _ in range(3):
                     for f in forms:
                         w.fused, w.launches = f
-                        runs[f].append(measure(torch, w, n, 5)[0])
+                        runs[f].append(measure(torch, w, n, 5, args.warm_s)[0])
                 f_ms, one_ms, s_ms = (float(np.median(runs[f])) for f in forms)
                 res[name] = {"value": round(f_ms * 1e3, 1), "unit": "us/step",
                              "launches": w.chosen_launches(), "us_one_launch": round(one_ms * 1e3, 1),

@@ -266,8 +266,8 @@ int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* params,
  * launched).  Token by token while the longest sequence has at most
  * `token_max` rows, chunked above.  token_max < 0 takes the library's
  * default, the kernel-time break-even measured on MI355X over uniform
- * batches at d_k = d_v = 128: 32 rows for batches of 1-4 sequences, 16 rows
- * for 5-8, 8 rows for more (past that the chunked form is faster at every
+ * batches at d_k = d_v = 128: 32 rows for batches of 1-2 sequences, 16 rows
+ * for 3-8, 8 rows for more (past that the chunked form is faster at every
  * length and batch size measured, 16 to 8192 rows and 1 to 32 sequences).  A large
  * token_max keeps every batch on the token-by-token path (relative error
  * 1e-4 against the exact recurrence, against 3e-3 for the bf16 matrix-core

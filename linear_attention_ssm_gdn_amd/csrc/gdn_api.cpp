@@ -264,11 +264,12 @@ GDN_EXPORT int32_t gdn_chunked_prefill(const gdn_dims* dims, const gdn_params* p
 namespace {
 // Kernel-time break-even of the two sequence paths on MI355X (uniform
 // batches, d_k = d_v = 128, bf16 activations, fp32 state; the chunked form
-// pays about 33 us for its two launches at any size): token by token is
-// faster up to 32 rows per sequence for 1-4 sequences, up to 16 rows for 5-8,
-// and below 16 rows for more; the chunked form is faster everywhere past that.
-constexpr int32_t kTokenMaxFew = 32;   // batches of 1-4 sequences
-constexpr int32_t kTokenMaxMid = 16;   // 5-8 sequences
+// pays about 28 us for its two launches at any size): token by token is
+// faster up to 32 rows per sequence for 1-2 sequences, up to 16 rows for 3-8
+// (at 4 sequences and 32 rows the two are within 3%), and below 16 rows for
+// more; the chunked form is faster everywhere past that.
+constexpr int32_t kTokenMaxFew = 32;   // batches of 1-2 sequences
+constexpr int32_t kTokenMaxMid = 16;   // 3-8 sequences
 constexpr int32_t kTokenMaxMany = 8;   // larger batches
 constexpr int32_t kPrefillChunk = 64;
 }  // namespace
@@ -281,7 +282,7 @@ GDN_EXPORT int32_t gdn_prefill_path(const gdn_dims* dims, const gdn_batch* batch
     if (!path) return GDN_ERR_ARG;
     const int64_t longest = batch->max_seqlen > 0 ? batch->max_seqlen : batch->n_rows;
     const int64_t limit = token_max >= 0     ? token_max
-                          : batch->n_seqs <= 4 ? kTokenMaxFew
+                          : batch->n_seqs <= 2 ? kTokenMaxFew
                           : batch->n_seqs <= 8 ? kTokenMaxMid
                                                : kTokenMaxMany;
     const bool chunked_ok = gdn::chunked_supported(dims->d_k, dims->d_v, kPrefillChunk);

@@ -231,7 +231,7 @@ def test_chunked_validation(so, L):
 
 def test_prefill_path_selection(so, L):
     """Host-side choice between the token-by-token and chunked paths: the
-    measured default break-even (32 rows for 1-4 sequences, 16 for 5-8, 8 for
+    measured default break-even (32 rows for 1-2 sequences, 16 for 3-8, 8 for
     more), an explicit token_max, max_seqlen unknown (n_rows stands in), and
     head dims the chunked kernel is not compiled for."""
     def path(dims, n_seqs, max_seqlen, token_max=-1, n_rows=None):
@@ -241,9 +241,9 @@ def test_prefill_path_selection(so, L):
         return out.value
     d = _dims(L)
     T, K = L.GDN_PATH_TOKEN, L.GDN_PATH_CHUNKED
-    for n in (1, 2, 4):
+    for n in (1, 2):
         assert path(d, n, 1) == T and path(d, n, 32) == T and path(d, n, 33) == K
-    for n in (5, 8):
+    for n in (3, 4, 5, 8):
         assert path(d, n, 16) == T and path(d, n, 17) == K and path(d, n, 8192) == K
     for n in (9, 16, 64):
         assert path(d, n, 8) == T and path(d, n, 9) == K and path(d, n, 8192) == K

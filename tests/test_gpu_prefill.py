@@ -70,7 +70,7 @@ def test_short_batches_run_token_by_token(ora, lens):
     _same(got, run_seq(wl, inp))
 
 
-@pytest.mark.parametrize("lens", [(333, 64, 129), (33,), (17, 3, 2, 9, 5)])
+@pytest.mark.parametrize("lens", [(333, 64, 129), (33,), (17, 3, 2, 9, 5), (30, 5, 3, 20)])
 def test_longer_batches_run_chunked(ora, lens):
     wl = _wl(lens, seed=62)
     inp = wk.make_sequence_inputs(wl)
