@@ -380,3 +380,62 @@ def test_decode_stream_many_claims(ora):
     lens = tuple(int(x) for x in rng.integers(1, 5, size=200))
     wl = wk.DECODE.replace(seqlens=lens, seed=29)
     _check(ora, wl, wk.make_sequence_inputs(wl))
+
+
+def _stream_shapes():
+    d64v64 = wk.Workload("d64v64", h_k=4, h_v=8, d_k=64, d_v=64, conv_w=4, act_dtype=wk.BF16,
+                         state_dtype=wk.F32, seqlens=(1,), seed=31, scale=64 ** -0.5)
+    d32v128 = wk.Workload("d32v128", h_k=4, h_v=8, d_k=32, d_v=128, conv_w=4, act_dtype=wk.BF16,
+                          state_dtype=wk.F32, seqlens=(1,), seed=32)
+    return {"decode": wk.DECODE.replace(seed=30), "d64v64": d64v64, "d32v128": d32v128}
+
+
+@pytest.mark.parametrize("state_dtype", [wk.F32, wk.BF16])
+@pytest.mark.parametrize("shape", ["decode", "d64v64", "d32v128"])
+def test_decode_stream_grid_shapes_agree(ora, shape, state_dtype):
+    """Above four items per compute unit the decode kernel runs one
+    workgroup per CU, each walking many items (most of them claimed from the
+    work counter); at four or fewer it fills every resident slot.  The same
+    sequences -- 1 to 4 tokens, fresh and continuing states -- run once as
+    one batch and once as consecutive calls of at most four items per CU on
+    fresh pools: outputs, states and windows agree bit for bit (128- and
+    64-column items, d_k = 32 and 128, fp32 and bf16 state), and the batch
+    run matches the oracle."""
+    base = _stream_shapes()[shape]
+    ncu = torch.cuda.get_device_properties(DEV).multi_processor_count
+    per_seq = base.h_v * (base.d_v // (128 if base.d_v % 128 == 0 else 64))
+    small = max(1, 4 * ncu // per_seq)          # sequences per call at four items per CU or fewer
+    n = 3 * small + 5                           # more than four items per CU in one call
+    rng = np.random.default_rng(33)
+    lens = tuple(int(v) for v in rng.integers(1, 5, size=n))
+    wl = base.replace(seqlens=lens, state_dtype=state_dtype)
+    inp = wk.make_sequence_inputs(wl)
+    has = (rng.random(n) < 0.8).astype(np.uint8)
+    pages = list(range(n))
+    o1, c1, s1 = run_seq(wl, inp, pages=pages, n_pages=n, has_init=has)
+
+    g = gdn()
+    dims, conv, state = seq_pools(wl, inp, pages, n)
+    params = params_of(inp, wl)
+    x, a, b = (dev(inp[k], dims.act_torch) for k in ("x", "a", "b"))
+    o2 = torch.full((x.shape[0], wl.h_v, wl.d_v), float("nan"), device=DEV)
+    cu = inp["cu_seqlens"]
+    for lo in range(0, n, small):
+        hi = min(n, lo + small)
+        r0, r1 = int(cu[lo]), int(cu[hi])
+        batch = make_batch(cu[lo:hi + 1] - r0, pages[lo:hi], r1 - r0, has[lo:hi])
+        g.gdn_recurrent_seq(dims, params, x[r0:r1], a[r0:r1], b[r0:r1], batch, conv, state, o=o2[r0:r1])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(s1.buf, state.buf)
+    assert torch.equal(c1.buf, conv.buf)
+    assert int(c1.sync.abs().sum()) == 0 and int(conv.sync.abs().sum()) == 0
+
+    # Outputs normwise per head over the batch, as in the repeated-steps
+    # test: a one-token slice can be orders of magnitude below the head's
+    # typical output, and its own relative error then measures fp32 rounding.
+    o_ref, win_ref, S_ref = oracle_seq(ora, wl, inp, has_init=has)
+    oh = host(o1)
+    assert max(rel(oh[:, h], o_ref[:, h]) for h in range(wl.h_v)) <= TOL
+    assert max_slice_rel_S(host(s1.buf), S_ref) <= (TOL if state_dtype == wk.F32 else 2.0 ** -8)
+    np.testing.assert_array_equal(host(c1.buf), win_ref)
