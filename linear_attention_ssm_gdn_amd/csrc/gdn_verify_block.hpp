@@ -193,35 +193,25 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         ra = rrow[C + h];
         rb = rrow[C + A.h_v + h];
     }
-    // One-page: the replayed rows go straight into the LDS rows 0 .. n_replay-1,
-    // all in flight at once: lane l of a wave lands at base + 4 l, and each
-    // region's base is chosen so that lane lc writes its own channel's slot.
-    // That placement was checked for loads whose lanes start at lane 0 of
-    // their wave.  With d_k not a multiple of 64 the k channels start inside
-    // a wave (lane d_k), and there the replayed rows came out wrong (at
-    // d_k = 32 the one-page states left those of the slot design from the
-    // first replay on, consistent with the k row landing 32 floats early), so
-    // for such d_k the rows go through registers.
-    if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
-        if constexpr (DK % 64 == 0) {
-            // the lane landing at q/k position p fetches the element qk_elem(p)
-            const int wbase = tid & ~63;
-            const int64_t gq = lc < DK ? gc - lc + qk_elem<DK>(lc)
-                             : lc < 2 * DK ? gc - (lc - DK) + qk_elem<DK>(lc - DK) : gc;
-            for (int i = 0; i < n_replay; ++i) {
-                const float* row = reinterpret_cast<const float*>(rec + i * row_bytes);
-                if (lc < DK)
-                    load_lds_elem(row + gq, reinterpret_cast<unsigned char*>(sq + i * DK + wbase));
-                else if (lc < 2 * DK)
-                    load_lds_elem(row + gq, reinterpret_cast<unsigned char*>(sk + i * DK + wbase - DK));
-                else if (lc < NLC)
-                    load_lds_elem(row + gc, reinterpret_cast<unsigned char*>(sv + i * BV + wbase - 2 * DK));
-            }
-        } else {
-            if (lc < NLC)
-                for (int i = 0; i < n_replay; ++i)
-                    ydst[i * yld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc];
-        }
+    // One-page: this lane's channel of the replayed rows.  With the split
+    // layout (at most TT/2 rows) they come into registers, in flight with the
+    // other small inputs and the state, and go to their LDS rows once the
+    // state's loads are issued; otherwise row by row, here.  No direct
+    // global->LDS loads: with one of those in flight the compiler waits for
+    // every vector load before using any loaded register, which would put the
+    // state's latency after the small inputs' instead of beside it.
+    constexpr int RP = TT / 2;
+    float rv[RP];
+    const bool replay_regs = LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0 && split;
+    if (replay_regs) {
+        const int64_t gcl = gc >= 0 ? gc : 0;
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            rv[i] = reinterpret_cast<const float*>(rec + (int64_t)(i < n_replay ? i : 0) * row_bytes)[gcl];
+    } else if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
+        if (lc < NLC)
+            for (int i = 0; i < n_replay; ++i)
+                ydst[i * yld] = reinterpret_cast<const float*>(rec + i * row_bytes)[gc];
     }
     {
         // unconditional loads (row and channel clamped into range) stay in flight
@@ -244,9 +234,28 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
             for (int tt = 0; tt < TT; ++tt) xr[tt] = ActT{};
         }
     }
-    // Every small input is taken (waited for) here, before the state's loads
-    // are issued: a use after them would make the compiler wait for the
-    // whole state, since it cannot count through the replay loop above.
+    // The state's loads are issued before any small input is used, so the two
+    // latencies overlap: loads complete in order, and the waits for the small
+    // inputs below leave the state's loads in flight.
+    float s[CPL][R];
+    load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
+    asm volatile("" ::: "memory");
+    // Every raw small input passes through an empty asm statement here, after
+    // the state's loads: volatile asm keeps its place, so the compiler waits
+    // for these values here (the state still in flight) rather than hoisting
+    // their conversions, and its waits, above the state's loads.
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(wr[e]));
+        asm volatile("" : "+v"(xr0), "+v"(xr1), "+v"(xr2), "+v"(par_raw), "+v"(pbr_raw), "+v"(ra), "+v"(rb));
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) asm volatile("" : "+v"(xr[tt]));
+        if constexpr (CACHE) asm volatile("" : "+v"(cr0), "+v"(cr1), "+v"(cr2));
+        if (replay_regs) {
+#pragma unroll
+            for (int i = 0; i < RP; ++i) asm volatile("" : "+v"(rv[i]));
+        }
+    }
     {
         const bool has_ch = gc >= 0;
 #pragma unroll
@@ -271,10 +280,11 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         for (int tt = 0; tt < TT; ++tt) asm volatile("" : "+v"(xp[tt]));
         exp_alog_v = exp_pin;
     }
-    asm volatile("" ::: "memory");  // the state's loads are issued after all of the above
-
-    float s[CPL][R];
-    load_state<StT, DK, CPL>(Sload, A.d_v, s, tid);
+    if (replay_regs && gc >= 0) {
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            if (i < n_replay) ydst[i * yld] = rv[i];
+    }
 
     StT* __restrict__ cst = nullptr;  // this workgroup's block of the cache entry's state
     if constexpr (CACHE) {
@@ -347,16 +357,11 @@ __device__ __forceinline__ void verify_block(const VerifyArgs& A, const int bloc
         }
     };
     if (split) {
-        // Everything but the state has arrived once at most the state's R
-        // loads (one per row, issued last) are outstanding; the candidates'
-        // record stores come after this wait.
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(R) : "memory");
         cand_conv();
         lds_barrier();
         gates(true, nc > 0);
         lds_barrier();
     } else if (LAYOUT == GDN_SPEC_ONEPAGE && n_replay > 0) {
-        wait_vmem();
         lds_barrier();
         gates(true, false);
         lds_barrier();
