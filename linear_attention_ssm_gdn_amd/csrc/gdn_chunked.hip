@@ -193,12 +193,23 @@ constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 72704
 constexpr int VR_LTB = 0;                        // bf16 [64][64] (sw64): (T - I) diag(beta)
 constexpr int VR_BETA = VR_LTB + CH * CH * 2;    // fp32 [64]
 constexpr int VR_GRK = VR_BETA + CH * 4;         // fp32 [64]: e^G rk
-constexpr int VR_PH = VR_GRK + CH * 4;           // bf16 [64][LT]: P hi (tiles on or below the diagonal)
-constexpr int VR_PL = VR_PH + CH * LT * 2;       // bf16 [64][LT]: P lo
-constexpr int VR_GRQ = VR_PL + CH * LT * 2;      // fp32 [64]: e^G rq
+// P holds only its tiles on or below the diagonal: the 16 rows of tile row
+// tb keep their first 16 (tb + 1) columns, at a row pitch of 24 + 16 tb
+// elements (p_row); the pitches are 12, 20, 28 and 36 words, four times an
+// odd number, so the 16 rows of an 8-byte operand read start in 16 distinct
+// groups of four banks.
+__host__ __device__ constexpr int p_pitch(int tb) { return 24 + 16 * tb; }
+__host__ __device__ constexpr int p_row(int t) {
+    return 16 * (24 * (t >> 4) + 8 * (t >> 4) * ((t >> 4) - 1)) + (t & 15) * p_pitch(t >> 4);
+}
+constexpr int P_ELEMS = p_row(CH);               // 3072
+static_assert(P_ELEMS == 3072 && p_row(63) + 64 <= P_ELEMS, "P tiles on and below the diagonal");
+constexpr int VR_PH = VR_GRK + CH * 4;           // bf16, p_row layout: P hi
+constexpr int VR_PL = VR_PH + P_ELEMS * 2;       // bf16, p_row layout: P lo
+constexpr int VR_GRQ = VR_PL + P_ELEMS * 2;      // fp32 [64]: e^G rq
 constexpr int VR_GAM = VR_GRQ + CH * 4;          // fp32 [64]: e^G
 constexpr int VR_WDR = VR_GAM + CH * 4;          // fp32 [64]: rk e^{G_last - G}, 0 for the last row
-constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 27904, a multiple of 256
+constexpr int VREC_BYTES = VR_WDR + CH * 4;      // 21760, a multiple of 256
 static_assert(VREC_BYTES % 256 == 0 && KREC_BYTES % 256 == 0, "records keep 256-byte alignment");
 static_assert(VR_WDR + CH * 4 <= VREC_BYTES && KREC_BYTES % 256 == 0 && VREC_BYTES % 256 == 0, "records");
 
@@ -209,8 +220,9 @@ __device__ __forceinline__ int64_t chunk_slot(int seq, int r0, int c) { return (
 // read the lanes {0-7, 24-31} and {8-15, 16-23} of each half wave (measured
 // with the bank-conflict counter).  An MFMA operand read takes row lr = lane
 // & 15 and column group lg = lane >> 4.
-//  - [rows][LT] (k^T, P) and [rows][LQK] (q, k): 8-byte reads of rows 36
-//    (68) words apart fill all 64 banks for every 32 lanes.
+//  - [rows][LT] (k^T), [rows][LQK] (q, k) and P's rows (p_row): 8-byte
+//    reads of rows 36 (68; 12, 20, 28 or 36 for a tile row of P) words apart
+//    fill all 64 banks for every 32 lanes.
 //  - sw64 ([rows][64], LTb and the v tile, read both 8 and 16 bytes wide):
 //    rows 128 bytes apart, the 16-byte column group XORed with (row >> 1) & 7;
 //    conflict free for both read widths, and for the v conv's 8-byte writes
@@ -537,8 +549,8 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             uint32_t h0, l0, h1, l1;
             split_pk(p[0], p[1], h0, l0);
             split_pk(p[2], p[3], h1, l1);
-            *reinterpret_cast<u32x2*>(vrec + VR_PH + (t * LT + s0) * 2) = u32x2{h0, h1};
-            *reinterpret_cast<u32x2*>(vrec + VR_PL + (t * LT + s0) * 2) = u32x2{l0, l1};
+            *reinterpret_cast<u32x2*>(vrec + VR_PH + (p_row(t) + s0) * 2) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(vrec + VR_PL + (p_row(t) + s0) * 2) = u32x2{l0, l1};
             *reinterpret_cast<f32x4*>(Af + t * LAF + s0) = a;
         }
         lds_barrier();
@@ -858,19 +870,19 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         f32x4 grq[4], kq[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int row = 16 * mt + lr;
+            const int prow = p_row(16 * mt) + lr * p_pitch(mt);  // row 16 mt + lr
             const int t0 = 16 * mt + 4 * lg;
             grq[mt] = *reinterpret_cast<const f32x4*>(sgrq + t0);
             kq[mt] = *reinterpret_cast<const f32x4*>(skq + t0);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 if (2 * kk + 1 > mt) continue;
-                pa[mt][kk][0] = cat8(ld4s(Ph + row * LT + 32 * kk + 4 * lg), ld4s(Ph + row * LT + 32 * kk + 16 + 4 * lg));
-                pa[mt][kk][1] = cat8(ld4s(Pl + row * LT + 32 * kk + 4 * lg), ld4s(Pl + row * LT + 32 * kk + 16 + 4 * lg));
+                pa[mt][kk][0] = cat8(ld4s(Ph + prow + 32 * kk + 4 * lg), ld4s(Ph + prow + 32 * kk + 16 + 4 * lg));
+                pa[mt][kk][1] = cat8(ld4s(Pl + prow + 32 * kk + 4 * lg), ld4s(Pl + prow + 32 * kk + 16 + 4 * lg));
             }
             if ((mt & 1) == 0) {
-                pd[mt >> 1][0] = ld4s(Ph + row * LT + 16 * mt + 4 * lg);
-                pd[mt >> 1][1] = ld4s(Pl + row * LT + 16 * mt + 4 * lg);
+                pd[mt >> 1][0] = ld4s(Ph + prow + 16 * mt + 4 * lg);
+                pd[mt >> 1][1] = ld4s(Pl + prow + 16 * mt + 4 * lg);
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
