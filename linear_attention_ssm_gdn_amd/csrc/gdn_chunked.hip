@@ -182,6 +182,7 @@ template <int N> struct RowVec<float, N> {
 // for packed sequences, fewer than n_seqs + ceil(n_rows / 64) in all); a slot
 // holds h_k key-head records, then h_v value-head records, in the LDS
 // layouts the state kernel reads.
+constexpr int LTB_ELEMS = 32 * 32 + 32 * CH;      // 3072 (ltb_at)
 constexpr int KR_QH = 0;                         // bf16 [64][LQK]: q hi
 constexpr int KR_KH = KR_QH + CH * LQK * 2;      // bf16 [64][LQK]: k hi
 constexpr int KR_KTH = KR_KH + CH * LQK * 2;     // bf16 [128][LT]: k^T hi
@@ -190,8 +191,8 @@ constexpr int KR_KLAST = KR_KTL + DK * LT * 2;   // fp32 [128]: rk k of the chun
 constexpr int KR_RQ = KR_KLAST + DK * 4;         // fp32 [64]: rq (with the output scale)
 constexpr int KR_KQ = KR_RQ + CH * 4;            // fp32 [64]: rq rk (q.k) of each row
 constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 72704
-constexpr int VR_LTB = 0;                        // bf16 [64][64] (sw64): (T - I) diag(beta)
-constexpr int VR_BETA = VR_LTB + CH * CH * 2;    // fp32 [64]
+constexpr int VR_LTB = 0;                        // bf16, ltb_at layout: (T - I) diag(beta)
+constexpr int VR_BETA = VR_LTB + LTB_ELEMS * 2;  // fp32 [64]
 constexpr int VR_GRK = VR_BETA + CH * 4;         // fp32 [64]: e^G rk
 // P holds only its tiles on or below the diagonal: the 16 rows of tile row
 // tb keep their first 16 (tb + 1) columns, at a row pitch of 24 + 16 tb
@@ -223,12 +224,21 @@ __device__ __forceinline__ int64_t chunk_slot(int seq, int r0, int c) { return (
 //  - [rows][LT] (k^T), [rows][LQK] (q, k) and P's rows (p_row): 8-byte
 //    reads of rows 36 (68; 12, 20, 28 or 36 for a tile row of P) words apart
 //    fill all 64 banks for every 32 lanes.
-//  - sw64 ([rows][64], LTb and the v tile, read both 8 and 16 bytes wide):
+//  - sw64 ([rows][64], the v tile and rows 32-63 of LTb, read both 8 and 16 bytes wide):
 //    rows 128 bytes apart, the 16-byte column group XORed with (row >> 1) & 7;
 //    conflict free for both read widths, and for the v conv's 8-byte writes
 //    when four consecutive lanes share a channel group (all measured).
 __device__ __forceinline__ int ktr_at(int row, int col) { return row * LT + col; }
 __device__ __forceinline__ int sw64(int row, int col) { return row * CH + (col ^ (((row >> 1) & 7) << 3)); }
+// (T - I) diag(beta) is strictly lower triangular, and its row tiles 0 and 1
+// are read in columns 0-31 only: rows 0-31 keep 32 columns (64-byte rows,
+// the 8-byte piece XORed with 2 ((row >> 2) & 3): rows 16 words apart then
+// cover all 64 banks in an 8-byte read of 32 lanes), rows 32-63 all 64
+// (sw64 rows, whose banks do not change by starting 2 KiB later).
+__host__ __device__ constexpr int ltb_at(int row, int col) {
+    return row < 32 ? row * 32 + (((col >> 2) ^ (((row >> 2) & 3) << 1)) << 2) + (col & 3)
+                    : 32 * 32 + (row - 32) * CH + (col ^ ((((row - 32) >> 1) & 7) << 3));
+}
 
 // Copy BYTES (a multiple of 64) from global memory into LDS with direct
 // global->LDS loads, 16 bytes per lane: wave w copies the w-th quarter in
@@ -606,6 +616,7 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
         for (int pass = 0; pass < 2; ++pass) {
             const int e = tid + NTH * pass;
             const int t = e >> 3, s0 = 8 * (e & 7);
+            if (t < 32 && s0 >= 32) continue;  // not stored (ltb_at)
             const bf16x8 tv = *reinterpret_cast<const bf16x8*>(Tm + t * LT + s0);
             const f32x4 b0 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0);
             const f32x4 b1 = *reinterpret_cast<const f32x4*>(sc + SC_BETA * CH + s0 + 4);
@@ -614,7 +625,7 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
             for (int k = 0; k < 8; ++k) lt[k] = s0 + k < t ? (float)tv[k] : 0.0f;
             const u32x4 ob = {pack_bf2(lt[0] * b0[0], lt[1] * b0[1]), pack_bf2(lt[2] * b0[2], lt[3] * b0[3]),
                               pack_bf2(lt[4] * b1[0], lt[5] * b1[1]), pack_bf2(lt[6] * b1[2], lt[7] * b1[3])};
-            *reinterpret_cast<u32x4*>(vrec + VR_LTB + sw64(t, s0) * 2) = ob;
+            *reinterpret_cast<u32x4*>(vrec + VR_LTB + ltb_at(t, s0) * 2) = ob;
         }
         lds_barrier();  // T, A and the scalars are rewritten by the next value head
     }
@@ -974,8 +985,8 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     if (ks > 0 && mt < 2) continue;
-                    la[mt][ks] = cat8(ld4s(LTb + sw64(16 * mt + lr, 32 * ks + 4 * lg)),
-                                      ld4s(LTb + sw64(16 * mt + lr, 32 * ks + 16 + 4 * lg)));
+                    la[mt][ks] = cat8(ld4s(LTb + ltb_at(16 * mt + lr, 32 * ks + 4 * lg)),
+                                      ld4s(LTb + ltb_at(16 * mt + lr, 32 * ks + 16 + 4 * lg)));
                 }
             settle4_v(Z);
             bf16x4 eh[4], el[4];
