@@ -183,14 +183,14 @@ template <int N> struct RowVec<float, N> {
 // holds h_k key-head records, then h_v value-head records, in the LDS
 // layouts the state kernel reads.
 constexpr int LTB_ELEMS = 32 * 32 + 32 * CH;      // 3072 (ltb_at)
-constexpr int KR_QH = 0;                         // bf16 [64][LQK]: q hi
-constexpr int KR_KH = KR_QH + CH * LQK * 2;      // bf16 [64][LQK]: k hi
-constexpr int KR_KTH = KR_KH + CH * LQK * 2;     // bf16 [128][LT]: k^T hi
-constexpr int KR_KTL = KR_KTH + DK * LT * 2;     // bf16 [128][LT]: k^T lo
-constexpr int KR_KLAST = KR_KTL + DK * LT * 2;   // fp32 [128]: rk k of the chunk's last row
+constexpr int KR_QH = 0;                         // bf16 [64][128] (qk_at): q hi
+constexpr int KR_KH = KR_QH + CH * DK * 2;       // bf16 [64][128] (qk_at): k hi
+constexpr int KR_KTH = KR_KH + CH * DK * 2;      // bf16 [128][64] (sw64): k^T hi
+constexpr int KR_KTL = KR_KTH + DK * CH * 2;     // bf16 [128][64] (sw64): k^T lo
+constexpr int KR_KLAST = KR_KTL + DK * CH * 2;   // fp32 [128]: rk k of the chunk's last row
 constexpr int KR_RQ = KR_KLAST + DK * 4;         // fp32 [64]: rq (with the output scale)
 constexpr int KR_KQ = KR_RQ + CH * 4;            // fp32 [64]: rq rk (q.k) of each row
-constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 72704
+constexpr int KREC_BYTES = KR_KQ + CH * 4;       // 66560
 constexpr int VR_LTB = 0;                        // bf16, ltb_at layout: (T - I) diag(beta)
 constexpr int VR_BETA = VR_LTB + LTB_ELEMS * 2;  // fp32 [64]
 constexpr int VR_GRK = VR_BETA + CH * 4;         // fp32 [64]: e^G rk
@@ -221,15 +221,20 @@ __device__ __forceinline__ int64_t chunk_slot(int seq, int r0, int c) { return (
 // read the lanes {0-7, 24-31} and {8-15, 16-23} of each half wave (measured
 // with the bank-conflict counter).  An MFMA operand read takes row lr = lane
 // & 15 and column group lg = lane >> 4.
-//  - [rows][LT] (k^T), [rows][LQK] (q, k) and P's rows (p_row): 8-byte
-//    reads of rows 36 (68; 12, 20, 28 or 36 for a tile row of P) words apart
+//  - P's rows (p_row): 8-byte reads of rows 12, 20, 28 or 36 words apart
 //    fill all 64 banks for every 32 lanes.
-//  - sw64 ([rows][64], the v tile and rows 32-63 of LTb, read both 8 and 16 bytes wide):
+//  - qk_at ([64][128], q and k rows): rows 256 bytes apart, the 8-byte piece
+//    XORed with 2 (row & 15); an 8-byte read of 16 rows and two adjacent
+//    pieces by 32 lanes covers all 64 banks.
+//  - sw64 ([rows][64], k^T, the v tile and rows 32-63 of LTb, read both 8 and 16 bytes wide):
 //    rows 128 bytes apart, the 16-byte column group XORed with (row >> 1) & 7;
 //    conflict free for both read widths, and for the v conv's 8-byte writes
 //    when four consecutive lanes share a channel group (all measured).
-__device__ __forceinline__ int ktr_at(int row, int col) { return row * LT + col; }
 __device__ __forceinline__ int sw64(int row, int col) { return row * CH + (col ^ (((row >> 1) & 7) << 3)); }
+__device__ __forceinline__ int ktr_at(int row, int col) { return sw64(row, col); }  // k^T [128][64]
+__device__ __forceinline__ int qk_at(int row, int col) {
+    return row * DK + (((col >> 2) ^ ((row & 15) << 1)) << 2) + (col & 3);
+}
 // (T - I) diag(beta) is strictly lower triangular, and its row tiles 0 and 1
 // are read in columns 0-31 only: rows 0-31 keep 32 columns (64-byte rows,
 // the 8-byte piece XORed with 2 ((row >> 2) & 3): rows 16 words apart then
@@ -289,10 +294,13 @@ __device__ __forceinline__ void copy_to_lds(const unsigned char* src, unsigned c
             dma16(uniform_ptr(sw + 1024 * j), 16u * (uint32_t)lane, __builtin_amdgcn_readfirstlane(base + 1024u * j));
     }
 }
-// The same copy through registers, LDS to global (16 bytes per thread and pass).
-__device__ __forceinline__ void copy_from_lds(const unsigned char* src, unsigned char* dst, int bytes, int tid) {
-    for (int p = tid; p < (bytes >> 4); p += NTH)
-        *reinterpret_cast<u32x4*>(dst + (int64_t)p * 16) = *reinterpret_cast<const u32x4*>(src + p * 16);
+// q or k rows from a [64][LQK] LDS array into the record's qk_at layout,
+// through registers, 16 bytes per thread and pass.
+__device__ __forceinline__ void store_qk_rows(const __bf16* src, __bf16* dst, int tid) {
+    for (int p = tid; p < CH * (DK / 8); p += NTH) {
+        const int r = p / (DK / 8), c = 8 * (p % (DK / 8));
+        *reinterpret_cast<u32x4*>(dst + qk_at(r, c)) = *reinterpret_cast<const u32x4*>(src + r * LQK + c);
+    }
 }
 
 // ---------------------------------------------------------------- prep
@@ -447,8 +455,8 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
     lds_barrier();
     // ---- the key head's record: q hi, k hi, the last row of rk k (the same
     // bits as k^T holds), rq; k^T went there from the conv
-    copy_from_lds(lds + OFF_QH, krec + KR_QH, CH * LQK * 2, tid);
-    copy_from_lds(lds + OFF_KH, krec + KR_KH, CH * LQK * 2, tid);
+    store_qk_rows(reinterpret_cast<const __bf16*>(lds + OFF_QH), reinterpret_cast<__bf16*>(krec + KR_QH), tid);
+    store_qk_rows(reinterpret_cast<const __bf16*>(lds + OFF_KH), reinterpret_cast<__bf16*>(krec + KR_KH), tid);
     if (tid < DK) {
         const int d = tid, tl = n - 1;
         reinterpret_cast<float*>(krec + KR_KLAST)[d] =
@@ -655,15 +663,17 @@ __global__ __launch_bounds__(NTH, 2) void k_chunk_prep(const ChunkArgs A, const 
 //   G3 (P D, output): P hi/lo, e^G rq       <- value-head record [VR_PH, VR_GAM)
 //                     kq                    <- key-head record [KR_KQ, KREC_BYTES)
 constexpr int SNTH = 512;                              // threads of the state kernel
-constexpr int G1V_BYTES = VR_PH;                       // 8704
-constexpr int G1K_BYTES = KR_KTH - KR_KH;              // 17408
+constexpr int G1V_BYTES = VR_PH;                       // 6656
+constexpr int G1K_BYTES = KR_KTH - KR_KH;              // 16384
 constexpr int G1_BYTES = G1V_BYTES + G1K_BYTES;
-constexpr int G2_BYTES = KR_KH;                        // 17408
-constexpr int G4K_BYTES = KR_RQ - KR_KTH;              // 37376
+constexpr int G2_BYTES = KR_KH;                        // 16384
+constexpr int G4K_BYTES = KR_RQ - KR_KTH;              // 33280
 constexpr int G4V_BYTES = VR_WDR + CH * 4 - VR_GAM;    // 512
-constexpr int G3V_BYTES = VR_GAM - VR_PH;              // 18688
+constexpr int G3V_BYTES = VR_GAM - VR_PH;              // 12544
 constexpr int G3K_BYTES = KREC_BYTES - KR_KQ;          // 256
 constexpr int XCH_BYTES = 4 * 4 * 64 * 16;             // one 16-byte vector per (chain wave, tile, lane)
+static_assert(G1V_BYTES == 6656 && G1K_BYTES == 16384 && G4K_BYTES == 33280 && G3V_BYTES == 12544,
+              "refill group sizes");
 constexpr int S_LDS = G1_BYTES + G2_BYTES + G4K_BYTES + G4V_BYTES + G3V_BYTES + G3K_BYTES + 2 * BVC * CH * 2 +
                       2 * XCH_BYTES + BVC * 4 * 4;
 static_assert(S_LDS <= 160 * 1024, "state kernel LDS");
@@ -692,8 +702,8 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const __bf16* Kr = reinterpret_cast<const __bf16*>(g1s + G1V_BYTES);
     const __bf16* Qh = reinterpret_cast<const __bf16*>(g2s);
     const __bf16* KTh = reinterpret_cast<const __bf16*>(g4s);
-    const __bf16* KTl = reinterpret_cast<const __bf16*>(g4s + DK * LT * 2);
-    const float* klast = reinterpret_cast<const float*>(g4s + 2 * DK * LT * 2);
+    const __bf16* KTl = reinterpret_cast<const __bf16*>(g4s + DK * CH * 2);
+    const float* klast = reinterpret_cast<const float*>(g4s + 2 * DK * CH * 2);
     const float* sgam4 = reinterpret_cast<const float*>(g4s + G4K_BYTES);
     const float* swdr = reinterpret_cast<const float*>(g4s + G4K_BYTES + CH * 4);
     const __bf16* Ph = reinterpret_cast<const __bf16*>(g3s);
@@ -964,8 +974,8 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
                     const int mt = mp + m2;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        ka[m2][kk] = cat8(ld4s(Kr + (16 * mt + lr) * LQK + 32 * kk + 4 * lg),
-                                          ld4s(Kr + (16 * mt + lr) * LQK + 32 * kk + 16 + 4 * lg));
+                        ka[m2][kk] = cat8(ld4s(Kr + qk_at(16 * mt + lr, 32 * kk + 4 * lg)),
+                                          ld4s(Kr + qk_at(16 * mt + lr, 32 * kk + 16 + 4 * lg)));
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
@@ -1112,7 +1122,7 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
                     const int row = 16 * (mp + m2) + lr;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        qa[m2][kk] = cat8(ld4s(Qh + row * LQK + 32 * kk + 4 * lg), ld4s(Qh + row * LQK + 32 * kk + 16 + 4 * lg));
+                        qa[m2][kk] = cat8(ld4s(Qh + qk_at(row, 32 * kk + 4 * lg)), ld4s(Qh + qk_at(row, 32 * kk + 16 + 4 * lg)));
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
