@@ -674,7 +674,7 @@ constexpr int G3K_BYTES = KREC_BYTES - KR_KQ;          // 256
 constexpr int XCH_BYTES = 4 * 4 * 64 * 16;             // one 16-byte vector per (chain wave, tile, lane)
 static_assert(G1V_BYTES == 6656 && G1K_BYTES == 16384 && G4K_BYTES == 33280 && G3V_BYTES == 12544,
               "refill group sizes");
-constexpr int S_LDS = G1_BYTES + G2_BYTES + G4K_BYTES + G4V_BYTES + G3V_BYTES + G3K_BYTES + 2 * BVC * CH * 2 +
+constexpr int S_LDS = G1_BYTES + 2 * G2_BYTES + G4K_BYTES + G4V_BYTES + G3V_BYTES + G3K_BYTES + 2 * BVC * CH * 2 +
                       2 * XCH_BYTES + BVC * 4 * 4;
 static_assert(S_LDS <= 160 * 1024, "state kernel LDS");
 // The v taps of channel c sit at 16-byte slot 16 (c & 3) + c / 4, so the
@@ -687,7 +687,7 @@ template <typename ActT, typename StT>
 __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_chunk_state(const ChunkArgs A, const int nck) {
     // One LDS object per operand group and hand-over buffer.
     __shared__ __attribute__((aligned(16))) unsigned char g1s[G1_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char g2s[G2_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char g2s[2 * G2_BYTES];  // q rows of chunks c (even, odd)
     __shared__ __attribute__((aligned(16))) unsigned char g4s[G4K_BYTES + G4V_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char g3s[G3V_BYTES + G3K_BYTES];
     __shared__ __attribute__((aligned(16))) __bf16 VTh[BVC * CH];  // v^T hi, sw64
@@ -793,7 +793,7 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         copy_to_lds<G4K_BYTES>(krec(c) + KR_KTH, g4s, w4, lane);
         copy_to_lds<G4V_BYTES>(vrec(c) + VR_GAM, g4s + G4K_BYTES, w4, lane);
     };
-    auto fill_g2 = [&](int c) { copy_to_lds<G2_BYTES>(krec(c), g2s, w4, lane); };
+    auto fill_g2 = [&](int c) { copy_to_lds<G2_BYTES>(krec(c), g2s + (c & 1) * G2_BYTES, w4, lane); };
     auto fill_g3 = [&](int c) {
         copy_to_lds<G3V_BYTES>(vrec(c) + VR_PH, g3s, w4, lane);
         copy_to_lds<G3K_BYTES>(krec(c) + KR_KQ, g3s + G3V_BYTES, w4, lane);
@@ -1110,6 +1110,11 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         for (int ci = 0; ci < nch; ++ci) {
             // ================================ step A: Q S of this chunk, O of the previous one
             if (ci + 1 < nch) load_v((ci + 1) * CH);
+            // the next chunk's q rows into the other buffer (last read in the
+            // previous step A), after the x rows: loads complete in order, and
+            // the v conv waits for the x rows only
+            if (ci + 1 < nch) fill_g2(ci + 1);
+            const __bf16* Qc = Qh + (ci & 1) * (G2_BYTES / 2);
             f32x4 qn[4];
             bf16x8 sbo[4];
 #pragma unroll
@@ -1122,7 +1127,7 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
                     const int row = 16 * (mp + m2) + lr;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        qa[m2][kk] = cat8(ld4s(Qh + qk_at(row, 32 * kk + 4 * lg)), ld4s(Qh + qk_at(row, 32 * kk + 16 + 4 * lg)));
+                        qa[m2][kk] = cat8(ld4s(Qc + qk_at(row, 32 * kk + 4 * lg)), ld4s(Qc + qk_at(row, 32 * kk + 16 + 4 * lg)));
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
@@ -1142,10 +1147,9 @@ __global__ __launch_bounds__(SNTH) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
             for (int mt = 0; mt < 4; ++mt) qs[mt] = qn[mt];
             lds_barrier();
             // ================================ step B: refills (under the conv); the next chunk's v tile
-            if (ci + 1 < nch) fill_g2(ci + 1);
             fill_g3(ci);
             if (ci + 1 < nch) conv_v();
-            GDN_WAIT_VM(0);  // G2 of the next chunk, G3 of this one
+            GDN_WAIT_VM(0);  // G2 of the next chunk (issued in step A), G3 of this one
             lds_barrier();
         }
         // ---- the last chunk's outputs (its D and G3 arrived in the last step)
